@@ -1,0 +1,37 @@
+/*
+ * moe_mxfp4_profiling.h -- instrumented variant of moe_grouped_ffn_mxfp4 for
+ * measurement tools.
+ *
+ * For callers that time the grouped FFN's kernels one by one (benchmarks, the
+ * roofline report): it does exactly what moe_grouped_ffn_mxfp4 does (same
+ * arguments, checks, kernels and stream; see moe_mxfp4.h) and additionally
+ * records three caller-owned events on `stream`:
+ *   events[0]  after the row-tile plan, just before the W1 (gate|up + SwiGLU) kernel
+ *   events[1]  after the W1 kernel, just before the W2 kernel
+ *   events[2]  after the W2 kernel
+ * Each entry is a hipEvent_t created by the caller (passed as void*); all three
+ * must be non-NULL when T > 0.  Elapsed time between consecutive events is the
+ * duration of one kernel.  T = 0 records nothing.
+ */
+#ifndef MOE_MXFP4_PROFILING_H
+#define MOE_MXFP4_PROFILING_H
+
+#include "moe_mxfp4.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+moe_status moe_grouped_ffn_mxfp4_timed(const uint16_t* x, int64_t T, int32_t H, int32_t I,
+                                       int32_t E, int32_t k, const uint8_t* w1,
+                                       const uint8_t* w1_scale, const uint8_t* w2,
+                                       const uint8_t* w2_scale, const int32_t* counts,
+                                       const int32_t* offsets, const int32_t* gather,
+                                       float swiglu_limit, uint16_t* y_sorted, void* ws,
+                                       size_t ws_bytes, void* const* events, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MXFP4_PROFILING_H */

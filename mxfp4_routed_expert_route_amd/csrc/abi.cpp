@@ -1,0 +1,108 @@
+// extern "C" entry points of libmoe_mxfp4.so: host-side checks, then launches.
+#include <hip/hip_runtime.h>
+
+#include "../../include/moe_mxfp4.h"
+#include "../../include/moe_mxfp4_profiling.h"
+#include "launch.h"
+#include "validate.h"
+
+namespace {
+
+moe_status from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* topk_ids,
+                     float* topk_weights, void* stream) {
+  moe_status s = moe::check_route(logits, T, E, k, topk_ids, topk_weights);
+  if (s != MOE_OK || T == 0) return s;
+  return from_hip(moe::launch_route(logits, T, E, k, topk_ids, topk_weights, as_stream(stream)));
+}
+
+moe_status moe_build_bitmatrix(const int32_t* topk_ids, int64_t T, int32_t E, int32_t k,
+                               uint32_t* bitmatrix, void* stream) {
+  moe_status s = moe::check_bitmatrix(topk_ids, T, E, k, bitmatrix);
+  if (s != MOE_OK || T == 0) return s;
+  return from_hip(moe::launch_bitmatrix(topk_ids, T, E, k, bitmatrix, as_stream(stream)));
+}
+
+moe_status moe_expert_offsets(const uint32_t* bitmatrix, const int32_t* topk_ids, int64_t T,
+                              int32_t E, int32_t k, int32_t* counts, int32_t* offsets,
+                              int32_t* gather, int32_t* scatter, void* ws, size_t ws_bytes,
+                              void* stream) {
+  moe_status s = moe::check_offsets(bitmatrix, topk_ids, T, E, k, counts, offsets, gather,
+                                    scatter, ws, ws_bytes);
+  if (s != MOE_OK) return s;
+  return from_hip(moe::launch_offsets(bitmatrix, topk_ids, T, E, k, counts, offsets, gather,
+                                      scatter, ws, as_stream(stream)));
+}
+
+moe_status moe_grouped_ffn_mxfp4(const uint16_t* x, int64_t T, int32_t H, int32_t I, int32_t E,
+                                 int32_t k, const uint8_t* w1, const uint8_t* w1_scale,
+                                 const uint8_t* w2, const uint8_t* w2_scale,
+                                 const int32_t* counts, const int32_t* offsets,
+                                 const int32_t* gather, float swiglu_limit, uint16_t* y_sorted,
+                                 void* ws, size_t ws_bytes, void* stream) {
+  moe_status s = moe::check_ffn(x, T, H, I, E, k, w1, w1_scale, w2, w2_scale, counts, offsets,
+                                gather, y_sorted, ws, ws_bytes);
+  if (s != MOE_OK || T == 0) return s;
+  moe::WsLayout L;
+  s = moe::workspace_layout(T, E, k, H, I, &L);
+  if (s != MOE_OK) return s;
+  return from_hip(moe::launch_ffn(x, T, H, I, E, k, w1, w1_scale, w2, w2_scale, counts, offsets,
+                                  gather, swiglu_limit, y_sorted, ws, L.ffn_h_offset,
+                                  L.ffn_plan_offset, L.tile_bound, as_stream(stream)));
+}
+
+moe_status moe_grouped_ffn_mxfp4_timed(const uint16_t* x, int64_t T, int32_t H, int32_t I,
+                                       int32_t E, int32_t k, const uint8_t* w1,
+                                       const uint8_t* w1_scale, const uint8_t* w2,
+                                       const uint8_t* w2_scale, const int32_t* counts,
+                                       const int32_t* offsets, const int32_t* gather,
+                                       float swiglu_limit, uint16_t* y_sorted, void* ws,
+                                       size_t ws_bytes, void* const* events, void* stream) {
+  moe_status s = moe::check_ffn(x, T, H, I, E, k, w1, w1_scale, w2, w2_scale, counts, offsets,
+                                gather, y_sorted, ws, ws_bytes);
+  if (s != MOE_OK || T == 0) return s;
+  if (!events || !events[0] || !events[1] || !events[2]) return MOE_ERR_INVALID_ARGUMENT;
+  moe::WsLayout L;
+  s = moe::workspace_layout(T, E, k, H, I, &L);
+  if (s != MOE_OK) return s;
+  hipEvent_t ev[3] = {static_cast<hipEvent_t>(events[0]), static_cast<hipEvent_t>(events[1]),
+                      static_cast<hipEvent_t>(events[2])};
+  return from_hip(moe::launch_ffn(x, T, H, I, E, k, w1, w1_scale, w2, w2_scale, counts, offsets,
+                                  gather, swiglu_limit, y_sorted, ws, L.ffn_h_offset,
+                                  L.ffn_plan_offset, L.tile_bound, as_stream(stream), ev));
+}
+
+moe_status moe_combine(const uint16_t* y_sorted, const float* topk_weights,
+                       const int32_t* scatter, int64_t T, int32_t H, int32_t k, uint16_t* y,
+                       void* stream) {
+  moe_status s = moe::check_combine(y_sorted, topk_weights, scatter, T, H, k, y);
+  if (s != MOE_OK || T == 0) return s;
+  return from_hip(moe::launch_combine(y_sorted, topk_weights, scatter, T, H, k, y,
+                                      as_stream(stream)));
+}
+
+size_t moe_workspace_bytes(int64_t T, int32_t E, int32_t k, int32_t H, int32_t I) {
+  moe::WsLayout L;
+  if (moe::workspace_layout(T, E, k, H, I, &L) != MOE_OK) return 0;
+  return L.total;
+}
+
+const char* moe_status_string(moe_status status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARGUMENT: return "MOE_ERR_INVALID_ARGUMENT";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_MISALIGNED: return "MOE_ERR_MISALIGNED";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+}  // extern "C"

@@ -1,0 +1,30 @@
+// Internal launchers: each enqueues its kernels on `stream` and returns the
+// launch status.  Arguments are already checked by validate.cpp.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <cstddef>
+#include <cstdint>
+
+namespace moe {
+
+hipError_t launch_route(const float* logits, int64_t T, int E, int k, int32_t* ids,
+                        float* weights, hipStream_t stream);
+
+hipError_t launch_bitmatrix(const int32_t* ids, int64_t T, int E, int k, uint32_t* bm,
+                            hipStream_t stream);
+
+hipError_t launch_offsets(const uint32_t* bm, const int32_t* ids, int64_t T, int E, int k,
+                          int32_t* counts, int32_t* offsets, int32_t* gather, int32_t* scatter,
+                          void* ws, hipStream_t stream);
+
+hipError_t launch_ffn(const uint16_t* x, int64_t T, int H, int I, int E, int k,
+                      const uint8_t* w1, const uint8_t* w1s, const uint8_t* w2,
+                      const uint8_t* w2s, const int32_t* counts, const int32_t* offsets,
+                      const int32_t* gather, float limit, uint16_t* y_sorted, void* ws,
+                      size_t h_offset, size_t plan_offset, int64_t tile_bound,
+                      hipStream_t stream, hipEvent_t const* events = nullptr);
+
+hipError_t launch_combine(const uint16_t* ys, const float* w, const int32_t* scatter, int64_t T,
+                          int H, int k, uint16_t* y, hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,77 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host before touching a GPU (CPU only: no compute calls)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from mxfp4_routed_expert_route_amd import build as build_mod
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_mxfp4.h")
+
+OK, INVALID, UNSUPPORTED, MISALIGNED, WS_SMALL = 0, 1, 2, 3, 4
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(build_mod.LIB):
+        build_mod.build_library()
+    return ctypes.CDLL(build_mod.LIB)
+
+
+def test_header_declares_the_five_calls():
+    names = declared_functions()
+    for n in ("moe_route", "moe_build_bitmatrix", "moe_expert_offsets", "moe_grouped_ffn_mxfp4",
+              "moe_combine", "moe_workspace_bytes", "moe_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", build_mod.LIB], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s+(\S+)", out))
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, missing
+    for n in declared_functions():
+        getattr(lib, n)
+
+
+def test_host_validation_driver():
+    exe = build_mod.build_validate_check()
+    r = subprocess.run([exe], capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "validate_check ok" in r.stdout
+
+
+def test_error_codes_through_the_abi(lib):
+    P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    lib.moe_route.argtypes = [P, I64, I32, I32, P, P, P]
+    lib.moe_build_bitmatrix.argtypes = [P, I64, I32, I32, P, P]
+    lib.moe_combine.argtypes = [P, P, P, I64, I32, I32, P, P]
+    lib.moe_workspace_bytes.argtypes = [I64, I32, I32, I32, I32]
+    lib.moe_workspace_bytes.restype = ctypes.c_size_t
+    lib.moe_status_string.argtypes = [ctypes.c_int]
+    lib.moe_status_string.restype = ctypes.c_char_p
+    assert lib.moe_route(None, 16, 256, 6, None, None, None) == INVALID
+    assert lib.moe_route(None, 0, 256, 6, None, None, None) == OK          # T = 0: nothing enqueued
+    assert lib.moe_route(None, 16, 256, 9, None, None, None) == UNSUPPORTED
+    assert lib.moe_route(None, 16, 2000, 6, None, None, None) == UNSUPPORTED
+    assert lib.moe_route(None, -1, 256, 6, None, None, None) == INVALID
+    assert lib.moe_route(1, 16, 256, 6, 8, 8, None) == MISALIGNED
+    assert lib.moe_build_bitmatrix(None, 16, 256, 7, None, None) == INVALID
+    assert lib.moe_combine(None, None, None, 0, 4096, 6, None, None) == OK
+    assert lib.moe_combine(None, None, None, 4, 4100, 6, None, None) == UNSUPPORTED
+    assert lib.moe_workspace_bytes(8191, 256, 6, 4096, 2048) >= 49146 * 2048 * 2
+    assert lib.moe_workspace_bytes(-1, 256, 6, 4096, 2048) == 0
+    assert lib.moe_status_string(WS_SMALL) == b"MOE_ERR_WORKSPACE_TOO_SMALL"

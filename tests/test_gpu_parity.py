@@ -1,0 +1,244 @@
+"""GPU parity: the HIP library, called through the C ABI, against the CPU oracle.
+
+Routing outputs (ids, bit matrix, counts, offsets, gather, scatter) must match
+bit for bit.  Routing weights: |gpu - oracle| <= 1e-6 * oracle (fp32 exponentials
+against a float64 softmax).  FFN and combined outputs:
+max|gpu - oracle| <= 2e-2 * max|oracle| + 1e-3, the oracle accumulating in fp32
+over the dequantised weights.  Full-size workloads are checked on all routing
+outputs and on a sample of tokens the oracle recomputes one by one.
+"""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle
+from mxfp4_routed_expert_route_amd import inputs
+from tests import invariants
+
+pytestmark = pytest.mark.gpu
+
+REL_TOL, ABS_TOL = 2e-2, 1e-3
+
+
+def _say(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from mxfp4_routed_expert_route_amd import binding
+    binding.load()          # fails loudly if the library is missing
+
+
+def _layer():
+    from mxfp4_routed_expert_route_amd import layer
+    return layer
+
+
+def run_gpu(inp, limit=10.0):
+    layer = _layer()
+    T = inp["logits"].shape[0]
+    wl = inp["workload"]
+    dev = layer.to_device(inp)
+    b = layer.LayerBuffers.allocate(T, wl.E, wl.k, wl.H, wl.I)
+    layer.run_layer(dev, b, limit)
+    torch.cuda.synchronize()
+    return b
+
+
+def ffn_close(gpu, ref):
+    gpu = np.asarray(gpu, np.float64)
+    ref = np.asarray(ref, np.float64)
+    nan_g, nan_r = np.isnan(gpu), np.isnan(ref)
+    assert (nan_g == nan_r).all(), f"NaN positions differ ({nan_g.sum()} vs {nan_r.sum()})"
+    ok = ~nan_r
+    if not ok.any():
+        return 0.0
+    err = float(np.abs(gpu[ok] - ref[ok]).max())
+    bound = REL_TOL * float(np.abs(ref[ok]).max()) + ABS_TOL
+    assert err <= bound, f"max err {err:.4g} > bound {bound:.4g}"
+    return err / max(float(np.abs(ref[ok]).max()), 1e-30)
+
+
+def check_routing(b, ref, E, k):
+    ids = b.topk_ids.cpu().numpy()
+    assert np.array_equal(ids, ref["ids"]), "topk ids differ"
+    w = b.topk_weights.cpu().numpy()
+    assert (np.abs(w.astype(np.float64) - ref["weights"]) <= 1e-6 * ref["weights"]).all(), \
+        "routing weights differ"
+    bm = b.bitmatrix.cpu().numpy().view(np.uint32)
+    assert np.array_equal(bm, ref["bitmatrix"]), "bitmatrix differs"
+    invariants.check_bitmatrix(bm, ids, E)
+    for name in ("counts", "offsets", "gather", "scatter"):
+        got = getattr(b, name).cpu().numpy()
+        assert np.array_equal(got, ref[name]), f"{name} differs"
+    invariants.check_offsets(b.counts.cpu().numpy(), b.offsets.cpu().numpy(),
+                             b.gather.cpu().numpy(), b.scatter.cpu().numpy(), ids, E, bm=bm)
+
+
+def oracle_routing(logits, E, k):
+    ids, w = oracle.route(logits, k)
+    counts, offsets, gather, scatter = oracle.expert_offsets(ids, E)
+    return dict(ids=ids, weights=w, bitmatrix=oracle.bitmatrix(ids, E), counts=counts,
+                offsets=offsets, gather=gather, scatter=scatter)
+
+
+# ------------------------------------------------------------ small, whole-layer parity
+
+def tiny(T, E, k, H, I, seed, skew=False):
+    rng = np.random.default_rng(seed)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    if skew:
+        logits += (2.0 * np.log(1.0 / (rng.permutation(E) + 1))).astype(np.float32)
+    return dict(
+        workload=inputs.Workload(0, "t", T, E, k, H, I), logits=logits,
+        x=inputs.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32)),
+        w1=rng.integers(0, 256, (E, 2 * I, H // 2), dtype=np.uint8),
+        w1_s=rng.integers(120, 127, (E, 2 * I, H // 32), dtype=np.uint8),
+        w2=rng.integers(0, 256, (E, H, I // 2), dtype=np.uint8),
+        w2_s=rng.integers(120, 127, (E, H, I // 32), dtype=np.uint8))
+
+
+def whole_layer_parity(inp, limit):
+    wl = inp["workload"]
+    T = inp["logits"].shape[0]
+    _say(f"[parity] T={T} E={wl.E} k={wl.k} H={wl.H} I={wl.I} limit={limit}")
+    b = run_gpu(inp, limit)
+    ref = oracle.moe_layer(inp, limit)
+    check_routing(b, ref, wl.E, wl.k)
+    r1 = ffn_close(b.y_sorted.float().cpu().numpy(), ref["y_sorted"])
+    r2 = ffn_close(b.y.float().cpu().numpy(), ref["y"])
+    return r1, r2
+
+
+@pytest.mark.parametrize("limit", [10.0, 0.0])
+def test_workload0_whole_layer(limit):
+    whole_layer_parity(inputs.make_inputs(0), limit)
+
+
+@pytest.mark.parametrize("T,E,k,H,I,seed", [
+    (1, 256, 6, 256, 128, 1),        # one token
+    (7, 256, 6, 256, 128, 2),
+    (11, 64, 6, 128, 256, 3),        # rows span two bitmatrix wavefronts
+    (70, 32, 6, 384, 128, 4),        # ragged row tiles (>64 rows for some experts)
+    (300, 16, 2, 256, 384, 5),       # many rows per expert: several 64-row tiles + tail
+    (1030, 48, 8, 128, 128, 6),      # crosses a 1024-token offsets block
+    (33, 1024, 8, 128, 128, 7),      # maximum E and k
+    (40, 8, 1, 128, 128, 8),         # k = 1
+])
+def test_ragged_shapes_whole_layer(T, E, k, H, I, seed):
+    whole_layer_parity(tiny(T, E, k, H, I, seed), 10.0)
+
+
+def test_skewed_small_whole_layer():
+    whole_layer_parity(tiny(500, 64, 6, 256, 128, 9, skew=True), 10.0)
+
+
+def test_all_tied_logits_route_to_lowest_ids():
+    inp = tiny(130, 40, 6, 128, 128, 10)
+    inp["logits"][:] = 0.0
+    inp["logits"][::3, 7] = -0.0
+    whole_layer_parity(inp, 10.0)
+
+
+def test_one_expert_takes_every_token():
+    inp = tiny(200, 32, 4, 128, 128, 11)
+    inp["logits"][:, 5] += 100.0
+    whole_layer_parity(inp, None)
+
+
+def test_nan_and_extreme_scales():
+    inp = tiny(24, 16, 3, 128, 128, 12)
+    w1_s = inp["w1_s"].copy()
+    w2_s = inp["w2_s"].copy()
+    w1_s[3, 5, 1] = 255       # NaN block in gate row 5 of expert 3
+    w1_s[4, :, 0] = 0         # 2^-127 blocks: contribute ~0, must not misbehave
+    w2_s[6, 9, 2] = 255       # NaN block in output row 9 of expert 6
+    inp = dict(inp, w1_s=w1_s, w2_s=w2_s)
+    whole_layer_parity(inp, 10.0)
+
+
+def test_repeat_runs_are_bit_identical():
+    inp = inputs.make_inputs(0)
+    b1 = run_gpu(inp)
+    y1 = b1.y.view(torch.int16).cpu().numpy().copy()
+    ys1 = b1.y_sorted.view(torch.int16).cpu().numpy().copy()
+    b2 = run_gpu(inp)
+    assert np.array_equal(y1, b2.y.view(torch.int16).cpu().numpy())
+    assert np.array_equal(ys1, b2.y_sorted.view(torch.int16).cpu().numpy())
+
+
+def test_outputs_leave_guard_bytes_untouched():
+    from mxfp4_routed_expert_route_amd import binding
+    inp = tiny(37, 64, 6, 256, 128, 13)
+    layer = _layer()
+    dev = layer.to_device(inp)
+    T, E, k, H, I = 37, 64, 6, 256, 128
+    pad = 4096
+    def guarded(n, dtype):
+        t = torch.full((n + pad,), 0x5A, dtype=torch.uint8, device="cuda")
+        return t, t[: n * torch.tensor([], dtype=dtype).element_size()].view(dtype)
+    bufs = {}
+    shapes = dict(ids=(T * k, torch.int32), w=(T * k, torch.float32), bm=(T * 2, torch.int32),
+                  counts=(E, torch.int32), offsets=(E + 1, torch.int32), gather=(T * k, torch.int32),
+                  scatter=(T * k, torch.int32), ys=(T * k * H, torch.bfloat16), y=(T * H, torch.bfloat16))
+    for name, (n, dt) in shapes.items():
+        bufs[name] = guarded(n, dt)
+    ws_n = binding.moe_workspace_bytes(T, E, k, H, I)
+    ws_raw, ws = guarded(ws_n, torch.uint8)
+    v = {n: t[1] for n, t in bufs.items()}
+    binding.moe_route(dev["logits"], k, v["ids"].view(T, k), v["w"].view(T, k))
+    binding.moe_build_bitmatrix(v["ids"].view(T, k), E, v["bm"].view(T, 2))
+    binding.moe_expert_offsets(v["bm"].view(T, 2), v["ids"].view(T, k), E, v["counts"], v["offsets"],
+                               v["gather"], v["scatter"], ws)
+    binding.moe_grouped_ffn_mxfp4(dev["x"], k, dev["w1"], dev["w1_s"], dev["w2"], dev["w2_s"],
+                                  v["counts"], v["offsets"], v["gather"], 10.0,
+                                  v["ys"].view(T * k, H), ws)
+    binding.moe_combine(v["ys"].view(T * k, H), v["w"].view(T, k), v["scatter"], v["y"].view(T, H))
+    torch.cuda.synchronize()
+    for name, (raw, view) in list(bufs.items()) + [("ws", (ws_raw, ws))]:
+        tail = raw[view.numel() * view.element_size():].cpu().numpy()
+        assert (tail == 0x5A).all(), f"{name}: bytes past the end were written"
+
+
+# ------------------------------------------------------------ full-size workloads
+
+def _sample_tokens(T, n=6):
+    picks = {0, T - 1, T // 2}
+    rng = np.random.default_rng(T)
+    while len(picks) < min(n, T):
+        picks.add(int(rng.integers(0, T)))
+    return sorted(picks)
+
+
+@pytest.mark.parametrize("index", [1, 2, 3, 4])
+def test_full_size_workload(index):
+    wl = inputs.workload(index)
+    _say(f"[full] workload {index} ({wl.name}) T={wl.T}: generating inputs")
+    inp = inputs.make_inputs(index)
+    b = run_gpu(inp, 10.0)
+    _say(f"[full] workload {index}: routing parity")
+    ref = oracle_routing(inp["logits"], wl.E, wl.k)
+    check_routing(b, ref, wl.E, wl.k)
+    # sampled tokens: the oracle recomputes the layer for those tokens alone (a
+    # token's output depends only on its own logits row and activations)
+    S = _sample_tokens(wl.T)
+    sub = dict(inp, logits=inp["logits"][S], x=inp["x"][S])
+    _say(f"[full] workload {index}: oracle on tokens {S}")
+    ref_s = oracle.moe_layer(sub, 10.0)
+    ffn_close(b.y.float().cpu().numpy()[S], ref_s["y"])
+    # and the sorted rows of those tokens
+    scatter = b.scatter.cpu().numpy().reshape(wl.T, wl.k)
+    ys = b.y_sorted.float().cpu().numpy()
+    ref_scatter = ref_s["scatter"].reshape(len(S), wl.k)
+    ffn_close(ys[scatter[S].ravel()], ref_s["y_sorted"][ref_scatter.ravel()])
+    del inp, b
+    torch.cuda.empty_cache()
