@@ -29,8 +29,9 @@
  *   - The library holds no state; calls are reentrant.  Two calls that share
  *     an output or workspace buffer must not run concurrently.
  *   - Sizes: T >= 0 tokens, E experts (1..1024), k experts per token (1..8,
- *     k <= E), hidden size H and expert intermediate size I (positive multiples
- *     of 128).  T*k must fit in int32.
+ *     k <= E), hidden size H and expert intermediate size I (multiples of 128,
+ *     at most 65536).  T*k must fit in int32, and for the FFN each of T*H,
+ *     T*k*I and T*k*H bf16 values must fit in 3.5 GiB.
  *   - Row-major layouts throughout; "bf16" buffers hold bfloat16 bit patterns.
  */
 #ifndef MOE_MXFP4_H
@@ -46,7 +47,8 @@ extern "C" {
 typedef enum moe_status {
   MOE_OK = 0,
   MOE_ERR_INVALID_ARGUMENT = 1,   /* negative T, k < 1, k > E, null pointer, ... */
-  MOE_ERR_UNSUPPORTED = 2,        /* E > 1024, k > 8, H or I not a multiple of 128, T*k > INT32_MAX */
+  MOE_ERR_UNSUPPORTED = 2,        /* E > 1024, k > 8, H or I not a multiple of 128 or above
+                                     65536, T*k > INT32_MAX, activations above 3.5 GiB */
   MOE_ERR_MISALIGNED = 3,         /* a buffer is not aligned as its call requires */
   MOE_ERR_WORKSPACE_TOO_SMALL = 4,
   MOE_ERR_HIP = 5                 /* the HIP runtime rejected a launch */

@@ -1,5 +1,6 @@
 // Tiling constants shared by the host launch code and the kernels.
 #pragma once
+#include <cstddef>
 #include <cstdint>
 
 namespace moe {
@@ -7,15 +8,28 @@ namespace moe {
 constexpr int kMaxE = 1024;           // experts per layer
 constexpr int kMaxK = 8;              // experts per token
 constexpr int kWave = 64;             // CDNA wavefront width
+constexpr int kMaxDim = 65536;        // largest H or I
+constexpr int64_t kMaxActivationBytes = 3758096384LL;   // 3.5 GiB: 32-bit buffer offsets
 
-// moe_expert_offsets: tokens per workgroup (16 wavefronts of 64 tokens)
-constexpr int kOffsBlockTokens = 1024;
+// moe_expert_offsets: tokens per workgroup (8 wavefronts of 64 tokens)
+constexpr int kOffsBlockTokens = 512;
 
-// grouped FFN: rows per row tile (4 MFMA subtiles of 16 rows), K chunk per step
+// grouped FFN: rows per row tile of the 64-row path (4 MFMA subtiles of 16 rows),
+// the smallest row tile of any path, and the K chunk per step
 constexpr int kFfnTileRows = 64;
+constexpr int kFfnMinTileRows = 16;
 constexpr int kFfnKChunk = 128;
 constexpr int kFfnW1ColsPerBlock = 64;   // gate columns per workgroup (plus the matching up columns)
 constexpr int kFfnW2ColsPerBlock = 128;  // output columns per workgroup
+// streaming path: LDS for the staged E8M0 scales of a workgroup (4 wavefronts x
+// 64 rows x K/32 bytes); above this the scales are read from memory
+constexpr size_t kStreamMaxScaleLds = 64 * 1024;
+
+// Upper bound on the row tiles of n_slots rows over E experts cut into tiles of
+// tile_rows rows: at most one partial tile per non-empty expert.
+inline int64_t ffn_tile_bound(int64_t n_slots, int E, int tile_rows) {
+  return (n_slots < E ? n_slots : E) + n_slots / tile_rows;
+}
 
 struct RowTile {
   int32_t expert;

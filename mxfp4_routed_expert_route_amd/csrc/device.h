@@ -9,6 +9,16 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
+// Buffer resource over [base, base + bytes): loads at offsets past `bytes` return
+// zero instead of touching memory.  The third dword is the CDNA raw-buffer format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
+}
+// A byte offset that no buffer here reaches (sizes are checked on the host to stay
+// below it, with room for any in-row offset added to it).
+constexpr uint32_t kRsrcOutOfRange = 0xFFF00000u;
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
 // fp32 -> bf16 bit pattern, round to nearest even (NaN stays NaN).

@@ -33,7 +33,7 @@ namespace {
 
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ counts,
                                                     const int32_t* __restrict__ offsets, int E,
-                                                    int64_t n_slots, int64_t tile_bound,
+                                                    int tile_rows, int64_t n_slots, int64_t tile_bound,
                                                     int32_t* __restrict__ n_tiles,
                                                     RowTile* __restrict__ tiles) {
   __shared__ int wave_tot[16];
@@ -45,7 +45,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
     if (c < 0 || begin < 0 || begin > n_slots) c = 0;
     if (static_cast<int64_t>(begin) + c > n_slots) c = static_cast<int>(n_slots - begin);
   }
-  const int nt = (c + kFfnTileRows - 1) / kFfnTileRows;
+  const int nt = (c + tile_rows - 1) / tile_rows;
   int incl = nt;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
@@ -62,8 +62,8 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
     if (slot >= tile_bound) break;
     RowTile rt;
     rt.expert = e;
-    rt.p_begin = begin + i * kFfnTileRows;
-    rt.p_end = (i + 1) * kFfnTileRows < c ? begin + (i + 1) * kFfnTileRows : begin + c;
+    rt.p_begin = begin + i * tile_rows;
+    rt.p_end = (i + 1) * tile_rows < c ? begin + (i + 1) * tile_rows : begin + c;
     rt.pad = 0;
     tiles[slot] = rt;
   }
@@ -203,41 +203,321 @@ __global__ __launch_bounds__(256) void gemm_kernel(
   }
 }
 
+// ---------------------------------------------------------------- streaming GEMM (few rows)
+//
+// For row tiles of at most 16*MSUB rows (decode-shaped batches, where each
+// expert has a handful of rows and the weights are read once): one wavefront
+// owns a row tile and 64 weight rows (W1: 32 gate rows and the 32 matching up
+// rows; W2: 64 output rows) and needs no barrier, so many wavefronts stay
+// resident per CU.  Per K chunk of 128 each lane loads 16 bytes from each of its
+// four weight rows (one scale block per row).
+//
+// Memory pipeline.  Vector-memory loads retire in issue order, and a wait is a
+// count of loads still allowed in flight, so the order of issue decides what a
+// wait drains.  Per chunk c the loop issues the activations of chunk c+1, then
+// the weights of chunk c+3, then computes chunk c: the wait for c's activations
+// leaves the weights of c+2 and c+3 in flight.  Every load in the loop is
+// unconditional (rows past the tile read zeros through a bounded buffer
+// resource; prefetches past the end re-read the last chunk), which keeps those
+// wait counts exact.  The E8M0 scales of the wavefront's 64 rows are staged in
+// LDS once, transposed so that one 16-byte LDS read per chunk gives a lane the
+// scale of each of its four rows; they never enter the vector-memory queue.
+// kDeep selects that pipeline (K a multiple of 512); otherwise a one-chunk
+// prefetch with scales read from memory.
+template <bool kW1, int MSUB, bool kDeep>
+__global__ __launch_bounds__(256) void gemm_stream_kernel(
+    const uint16_t* __restrict__ act, uint32_t act_bytes, const int32_t* __restrict__ gather,
+    int k_top, int n_slots, const uint8_t* __restrict__ wq, const uint8_t* __restrict__ wsc,
+    const RowTile* __restrict__ tiles, const int32_t* __restrict__ n_tiles, int K, int n_rows,
+    int half, int waves_per_tile, float limit, int clamp, uint16_t* __restrict__ out,
+    int ld_out) {
+  extern __shared__ uint32_t scale_lds[];   // kDeep: per wavefront [K/128][16][4] dwords
+  const int lane = threadIdx.x & 63;
+  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int tile_id = gw / waves_per_tile;
+  const int cg = gw - tile_id * waves_per_tile;
+  if (tile_id >= *n_tiles) return;   // per wavefront: no workgroup barrier in this kernel
+  const RowTile rt = tiles[tile_id];
+  const int r16 = lane & 15, g = lane >> 4;
+  const int n_chunks = K / kFfnKChunk;
+
+  const __amdgpu_buffer_rsrc_t arsrc = make_rsrc(act, act_bytes);
+  uint32_t aoff[MSUB];   // byte offset of this lane's activation run in chunk 0
+#pragma unroll
+  for (int mi = 0; mi < MSUB; ++mi) {
+    const int p = rt.p_begin + mi * 16 + r16;
+    bool valid = p < rt.p_end;
+    uint32_t row = 0;
+    if (valid) {
+      if (kW1) {
+        const int slot = gather[p];   // a slot id outside [0, T*k) feeds zeros, never an address
+        valid = static_cast<unsigned>(slot) < static_cast<unsigned>(n_slots);
+        row = valid ? static_cast<uint32_t>(slot / k_top) : 0u;
+      } else {
+        row = static_cast<uint32_t>(p);
+      }
+    }
+    aoff[mi] = valid ? row * static_cast<uint32_t>(K) * 2u + 64u * g : kRsrcOutOfRange;
+  }
+
+  // weight row of fragment f for a lane whose MFMA column is c16
+  auto wrow = [&](int f, int c16) {
+    return kW1 ? (f >= 2 ? half : 0) + cg * 32 + (f & 1) * 16 + c16   // gate, gate, up, up
+               : cg * 64 + f * 16 + c16;
+  };
+  int nrow[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) nrow[f] = wrow(f, r16);
+  const size_t row_q = static_cast<size_t>(K / 2), row_s = static_cast<size_t>(K / 32);
+  const size_t e_rows = static_cast<size_t>(rt.expert) * n_rows;
+  const uint8_t* bq[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) bq[f] = wq + (e_rows + nrow[f]) * row_q + 16 * g;
+
+  uint32_t* my_scales = scale_lds + (threadIdx.x >> 6) * (n_chunks * 64);
+  if (kDeep) {
+    // lane L stages the scales of row (f = L/16, column L%16): the dword of chunk c
+    // (one byte per lane group) goes to my_scales[(c*16 + L%16)*4 + f]
+    const int f = lane >> 4;
+    const uint8_t* srow = wsc + (e_rows + wrow(f, r16)) * row_s;
+    for (int c = 0; c < n_chunks; c += 4) {
+      const uint4 d = *reinterpret_cast<const uint4*>(srow + c * 4);
+      my_scales[((c + 0) * 16 + r16) * 4 + f] = d.x;
+      my_scales[((c + 1) * 16 + r16) * 4 + f] = d.y;
+      my_scales[((c + 2) * 16 + r16) * 4 + f] = d.z;
+      my_scales[((c + 3) * 16 + r16) * 4 + f] = d.w;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+  const uint8_t* bs[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) bs[f] = wsc + (e_rows + nrow[f]) * row_s + g;
+
+  floatx4 acc[MSUB][4];
+#pragma unroll
+  for (int mi = 0; mi < MSUB; ++mi)
+#pragma unroll
+    for (int f = 0; f < 4; ++f) acc[mi][f] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  auto load_w = [&](uint4 (&q)[4], int kc) {
+#pragma unroll
+    for (int f = 0; f < 4; ++f) q[f] = *reinterpret_cast<const uint4*>(bq[f] + kc * 64);
+  };
+  auto load_s = [&](uint32_t (&sc)[4], int kc) {   // from memory (shallow pipeline)
+#pragma unroll
+    for (int f = 0; f < 4; ++f) sc[f] = bs[f][kc * 4];
+  };
+  auto lds_s = [&](uint32_t (&sc)[4], int kc) {    // from the staged copy
+    const uint4 d = *reinterpret_cast<const uint4*>(my_scales + (kc * 16 + r16) * 4);
+    const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+    for (int f = 0; f < 4; ++f) sc[f] = (dw[f] >> (8 * g)) & 0xFFu;
+  };
+  auto load_a = [&](bf16x8 (&a)[MSUB][4], int kc) {
+#pragma unroll
+    for (int mi = 0; mi < MSUB; ++mi)
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        a[mi][s] = __builtin_bit_cast(
+            bf16x8, __builtin_amdgcn_raw_buffer_load_b128(arsrc, aoff[mi] + kc * 256 + 16 * s, 0, 0));
+  };
+  auto compute = [&](const uint4 (&q)[4], const uint32_t (&sc)[4], const bf16x8 (&a)[MSUB][4]) {
+    const uint32_t w[4][4] = {{q[0].x, q[0].y, q[0].z, q[0].w},
+                              {q[1].x, q[1].y, q[1].z, q[1].w},
+                              {q[2].x, q[2].y, q[2].z, q[2].w},
+                              {q[3].x, q[3].y, q[3].z, q[3].w}};
+    float scl[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) scl[f] = e8m0_as_f32(sc[f]);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        const bf16x8 b = dequant8(w[f][s], scl[f]);
+#pragma unroll
+        for (int mi = 0; mi < MSUB; ++mi)
+          acc[mi][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mi][s], b, acc[mi][f], 0, 0, 0);
+      }
+    }
+  };
+
+  if constexpr (kDeep) {
+    // n_chunks is a multiple of 4 (>= 4).  Ring: weights q0..q3, activations a0/a1.
+    uint4 q0[4], q1[4], q2[4], q3[4];
+    bf16x8 a0[MSUB][4], a1[MSUB][4];
+    uint32_t sc[4];
+    const int last = n_chunks - 1;
+    // prologue in steady-state order (..., activations of c, weights of c+2), so the
+    // loop header sees the same outstanding-load count from entry and back edge
+    load_w(q0, 0);
+    load_w(q1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    load_a(a0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(q2, 2);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int kc = 0; kc < n_chunks; kc += 4) {
+#define MOE_STREAM_STEP(A_NEXT, KA, Q_NEXT, KQ, Q_CUR, A_CUR, KC) \
+  load_a(A_NEXT, KA);                                              \
+  __builtin_amdgcn_sched_barrier(0);                               \
+  load_w(Q_NEXT, KQ);                                              \
+  __builtin_amdgcn_sched_barrier(0);                               \
+  lds_s(sc, KC);                                                   \
+  compute(Q_CUR, sc, A_CUR);                                       \
+  __builtin_amdgcn_sched_barrier(0);
+      MOE_STREAM_STEP(a1, kc + 1, q3, kc + 3, q0, a0, kc)
+      MOE_STREAM_STEP(a0, kc + 2, q0, kc + 4 <= last ? kc + 4 : last, q1, a1, kc + 1)
+      MOE_STREAM_STEP(a1, kc + 3, q1, kc + 5 <= last ? kc + 5 : last, q2, a0, kc + 2)
+      MOE_STREAM_STEP(a0, kc + 4 <= last ? kc + 4 : last, q2, kc + 6 <= last ? kc + 6 : last, q3,
+                      a1, kc + 3)
+#undef MOE_STREAM_STEP
+    }
+  } else {
+    uint4 qa[4], qb[4];
+    uint32_t sa[4], sb[4];
+    load_w(qa, 0);
+    load_s(sa, 0);
+    int kc = 0;
+    for (; kc + 2 <= n_chunks; kc += 2) {
+      bf16x8 a0[MSUB][4];
+      load_a(a0, kc);
+      __builtin_amdgcn_sched_barrier(0);
+      load_w(qb, kc + 1);
+      load_s(sb, kc + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(qa, sa, a0);
+      __builtin_amdgcn_sched_barrier(0);
+      bf16x8 a1[MSUB][4];
+      load_a(a1, kc + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      const int kn = kc + 2 < n_chunks ? kc + 2 : kc + 1;   // last pass re-reads a valid chunk
+      load_w(qa, kn);
+      load_s(sa, kn);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(qb, sb, a1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (kc < n_chunks) {   // odd chunk count: the last chunk is in qa
+      bf16x8 a0[MSUB][4];
+      load_a(a0, kc);
+      compute(qa, sa, a0);
+    }
+  }
+
+  // D layout of a 16x16 MFMA tile: lane holds column (lane & 15), rows 4*(lane>>4) + i.
+  const bool do_clamp = clamp != 0;
+#pragma unroll
+  for (int mi = 0; mi < MSUB; ++mi) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int p = rt.p_begin + mi * 16 + 4 * g + i;
+      if (p >= rt.p_end) continue;
+      uint16_t* orow = out + static_cast<int64_t>(p) * ld_out;
+      if (kW1) {
+        orow[nrow[0]] = f32_to_bf16_bits(swiglu(acc[mi][0][i], acc[mi][2][i], limit, do_clamp));
+        orow[nrow[1]] = f32_to_bf16_bits(swiglu(acc[mi][1][i], acc[mi][3][i], limit, do_clamp));
+      } else {
+#pragma unroll
+        for (int f = 0; f < 4; ++f) orow[nrow[f]] = f32_to_bf16_bits(acc[mi][f][i]);
+      }
+    }
+  }
+}
+
+// Launch one streaming GEMM; picks the deep pipeline when K allows it.
+template <bool kW1, int MSUB>
+hipError_t launch_stream(unsigned grid, hipStream_t stream, const uint16_t* act, uint32_t act_bytes,
+                         const int32_t* gather, int k_top, int n_slots, const uint8_t* wq,
+                         const uint8_t* wsc, const RowTile* tiles, const int32_t* n_tiles, int K,
+                         int n_rows, int half, int wpt, float limit, int clamp, uint16_t* out,
+                         int ld_out) {
+  const int n_chunks = K / kFfnKChunk;
+  const size_t lds = static_cast<size_t>(4) * n_chunks * 64 * sizeof(uint32_t);
+  if (n_chunks % 4 == 0 && lds <= kStreamMaxScaleLds)
+    gemm_stream_kernel<kW1, MSUB, true><<<grid, 256, lds, stream>>>(
+        act, act_bytes, gather, k_top, n_slots, wq, wsc, tiles, n_tiles, K, n_rows, half, wpt,
+        limit, clamp, out, ld_out);
+  else
+    gemm_stream_kernel<kW1, MSUB, false><<<grid, 256, 0, stream>>>(
+        act, act_bytes, gather, k_top, n_slots, wq, wsc, tiles, n_tiles, K, n_rows, half, wpt,
+        limit, clamp, out, ld_out);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_ffn(const uint16_t* x, int64_t T, int H, int I, int E, int k,
                       const uint8_t* w1, const uint8_t* w1s, const uint8_t* w2,
                       const uint8_t* w2s, const int32_t* counts, const int32_t* offsets,
                       const int32_t* gather, float limit, uint16_t* y_sorted, void* ws,
-                      size_t h_offset, size_t plan_offset, int64_t tile_bound,
+                      size_t h_offset, size_t plan_offset, int64_t /*tile_bound_min_rows*/,
                       hipStream_t stream, hipEvent_t const* events) {
   const int64_t n_slots = T * k;
   uint16_t* h = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + h_offset);
   int32_t* n_tiles = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + plan_offset);
   RowTile* tiles = reinterpret_cast<RowTile*>(static_cast<char*>(ws) + plan_offset + 256);
   const bool clamp = limit > 0.f && limit <= 3.402823466e38f;   // finite and positive
+  const int clamp_i = clamp ? 1 : 0;
+  const int slots_i = static_cast<int>(n_slots);
+  const uint32_t x_bytes = static_cast<uint32_t>(T * H * 2);         // < 2^32 - 2^20 (host check)
+  const uint32_t h_bytes = static_cast<uint32_t>(n_slots * I * 2);
 
-  plan_kernel<<<1, 1024, 0, stream>>>(counts, offsets, E, n_slots, tile_bound, n_tiles, tiles);
+  // Path: a token picks an expert at most once, so no expert has more than T rows.
+  // Few rows per expert -> weight streaming with 16- or 32-row tiles; else 64-row tiles.
+  const int64_t avg_rows = n_slots / E;
+  int tile_rows;
+  if (T <= 16)
+    tile_rows = 16;
+  else if (avg_rows <= 24)
+    tile_rows = 32;
+  else
+    tile_rows = kFfnTileRows;
+  const int64_t tile_bound = ffn_tile_bound(n_slots, E, tile_rows);
+
+  plan_kernel<<<1, 1024, 0, stream>>>(counts, offsets, E, tile_rows, n_slots, tile_bound, n_tiles,
+                                      tiles);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-
   if (events) {
     err = hipEventRecord(events[0], stream);
     if (err != hipSuccess) return err;
   }
-  const int bpt1 = I / kFfnW1ColsPerBlock;
-  gemm_kernel<true><<<dim3(static_cast<unsigned>(tile_bound * bpt1)), dim3(256), 0, stream>>>(
-      x, gather, k, static_cast<int>(n_slots), w1, w1s, tiles, n_tiles, H, 2 * I, I, bpt1, limit, clamp ? 1 : 0, h, I);
-  err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  if (events) {
-    err = hipEventRecord(events[1], stream);
-    if (err != hipSuccess) return err;
-  }
 
-  const int bpt2 = H / kFfnW2ColsPerBlock;
-  gemm_kernel<false><<<dim3(static_cast<unsigned>(tile_bound * bpt2)), dim3(256), 0, stream>>>(
-      h, nullptr, k, static_cast<int>(n_slots), w2, w2s, tiles, n_tiles, I, H, 0, bpt2, limit, 0, y_sorted, H);
+  if (tile_rows <= 32) {
+    const int wpt1 = I / 32, wpt2 = H / 64;
+    const unsigned g1 = static_cast<unsigned>((tile_bound * wpt1 + 3) / 4);
+    const unsigned g2 = static_cast<unsigned>((tile_bound * wpt2 + 3) / 4);
+    err = tile_rows == 16
+              ? launch_stream<true, 1>(g1, stream, x, x_bytes, gather, k, slots_i, w1, w1s, tiles,
+                                       n_tiles, H, 2 * I, I, wpt1, limit, clamp_i, h, I)
+              : launch_stream<true, 2>(g1, stream, x, x_bytes, gather, k, slots_i, w1, w1s, tiles,
+                                       n_tiles, H, 2 * I, I, wpt1, limit, clamp_i, h, I);
+    if (err != hipSuccess) return err;
+    if (events) {
+      err = hipEventRecord(events[1], stream);
+      if (err != hipSuccess) return err;
+    }
+    err = tile_rows == 16
+              ? launch_stream<false, 1>(g2, stream, h, h_bytes, nullptr, k, slots_i, w2, w2s,
+                                        tiles, n_tiles, I, H, 0, wpt2, limit, 0, y_sorted, H)
+              : launch_stream<false, 2>(g2, stream, h, h_bytes, nullptr, k, slots_i, w2, w2s,
+                                        tiles, n_tiles, I, H, 0, wpt2, limit, 0, y_sorted, H);
+  } else {
+    const int bpt1 = I / kFfnW1ColsPerBlock;
+    gemm_kernel<true><<<dim3(static_cast<unsigned>(tile_bound * bpt1)), dim3(256), 0, stream>>>(
+        x, gather, k, slots_i, w1, w1s, tiles, n_tiles, H, 2 * I, I, bpt1, limit, clamp_i, h, I);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    if (events) {
+      err = hipEventRecord(events[1], stream);
+      if (err != hipSuccess) return err;
+    }
+    const int bpt2 = H / kFfnW2ColsPerBlock;
+    gemm_kernel<false><<<dim3(static_cast<unsigned>(tile_bound * bpt2)), dim3(256), 0, stream>>>(
+        h, nullptr, k, slots_i, w2, w2s, tiles, n_tiles, I, H, 0, bpt2, limit, 0, y_sorted, H);
+  }
   err = hipGetLastError();
   if (err != hipSuccess || !events) return err;
   return hipEventRecord(events[2], stream);

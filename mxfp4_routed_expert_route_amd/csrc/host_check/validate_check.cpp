@@ -46,8 +46,8 @@ int main() {
   // offsets
   WsLayout L;
   expect("layout", workspace_layout(8191, 256, 6, 4096, 2048, &L), MOE_OK);
-  if (L.n_blocks != 8 || L.offsets_bytes != 8 * 256 * 4) { std::printf("FAIL offsets layout\n"); ++failures; }
-  if (L.tile_bound != 256 + 49146 / kFfnTileRows) { std::printf("FAIL tile bound\n"); ++failures; }
+  if (L.n_blocks != 16 || L.offsets_bytes != 16 * 256 * 4) { std::printf("FAIL offsets layout\n"); ++failures; }
+  if (L.tile_bound != 256 + 49146 / kFfnMinTileRows) { std::printf("FAIL tile bound\n"); ++failures; }
   if (L.ffn_plan_offset < (size_t)49146 * 2048 * 2 || L.total < L.ffn_bytes || L.total < L.offsets_bytes) {
     std::printf("FAIL ffn layout\n"); ++failures;
   }

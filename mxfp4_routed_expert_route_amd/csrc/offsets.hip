@@ -2,19 +2,22 @@
 //
 // Expert-major grouping of the (token, slot) rows before the expert products (the
 // grouped-expert step of the deployment's README, mynewscn.com translation).
-// Three small kernels, all deterministic (integer work, no order-dependent atomics):
-//   1. block_counts: a workgroup owns 1024 consecutive tokens (16 wavefronts x 64
-//      tokens, one token per lane).  For each expert e a wavefront takes a ballot
-//      of "my token's bit e is set"; the popcount is that wavefront's count.  The
-//      workgroup's per-expert sum goes to the workspace.
-//   2. scan: one workgroup; thread e turns the per-block counts of expert e into
-//      exclusive per-block bases (in place) and the total counts[e]; a workgroup
-//      scan over e gives offsets.
-//   3. ranks: the same 1024-token workgroups recount per wavefront, prefix the
-//      wavefront counts per expert in LDS, then ballot again: a lane whose token
-//      chose e has rank popcount(ballot & lanes-below-me) among the wavefront's
-//      tokens, so its row is p = offsets[e] + block base + wavefront base + rank
-//      (tokens ascending within an expert).  The slot j comes from topk_ids.
+// Everything is integer work with no order-dependent atomics, so results are
+// deterministic.
+//
+// Core step, per wavefront of 64 consecutive tokens (one per lane): for every
+// expert e, a ballot of "my token's bit e is set" gives the 64-bit column mask of
+// e over those tokens.  Lane (e mod 64) collects that mask with writelane, so a
+// group of 64 experts costs about four instructions per expert and one 64-bit
+// LDS store per lane.  From the masks:
+//   count of e in the wavefront       = popcount(mask[e])
+//   rank of my token among e's tokens = popcount(mask[e] & lanes-below-me)
+// which orders the rows of an expert by token, as the definition asks.
+//
+// Workgroups own 512 consecutive tokens (8 wavefronts).  T <= 512: one fused
+// kernel does counts, offsets and permutations.  Larger T: block_counts writes
+// per-workgroup expert counts, scan turns them into per-workgroup bases and
+// offsets, and ranks writes the permutations.
 #include "config.h"
 #include "device.h"
 #include "launch.h"
@@ -22,48 +25,162 @@
 namespace moe {
 namespace {
 
-constexpr int kWaves = kOffsBlockTokens / 64;   // 16
+constexpr int kWaves = kOffsBlockTokens / 64;   // 8
 
-// Per-wavefront expert counts into cnt[wave][e]; returns nothing.
-__device__ __forceinline__ void wave_expert_counts(const uint32_t* __restrict__ bm, int64_t t,
-                                                   bool valid, int E, int words, int lane,
-                                                   int* __restrict__ cnt_row) {
-  int mine = 0;
-  for (int w = 0; w < words; ++w) {
-    const uint32_t word = valid ? bm[t * words + w] : 0u;
-    const int nbits = (E - w * 32) < 32 ? (E - w * 32) : 32;
-    for (int b = 0; b < nbits; ++b) {
-      const int e = w * 32 + b;
-      const unsigned long long m = __ballot((word >> b) & 1u);
-      if (lane == (e & 63)) mine = __popcll(m);
-      if ((e & 63) == 63 || e == E - 1) {
-        if (lane <= (e & 63)) cnt_row[(e & ~63) + lane] = mine;
-      }
-    }
+// The LLVM writelane intrinsic (v_writelane_b32), which this clang does not expose
+// as a builtin.  Going through the intrinsic, rather than inline assembly, lets
+// the compiler see the instruction and insert the wait state it needs after a
+// VALU write of the SGPR it reads (the ballot's compare).
+extern "C" __device__ int llvm_amdgcn_writelane(int src, int lane, int old)
+    __asm("llvm.amdgcn.writelane.i32");
+
+// v <- v with lane `kLane` replaced by the wave-uniform value s.
+template <int kLane>
+__device__ __forceinline__ uint32_t write_lane(uint32_t v, uint32_t s) {
+  return static_cast<uint32_t>(
+      llvm_amdgcn_writelane(static_cast<int>(s), kLane, static_cast<int>(v)));
+}
+
+template <int kBase, int kBit = 0>
+__device__ __forceinline__ void collect_word(uint32_t word, uint32_t& lo, uint32_t& hi) {
+  if constexpr (kBit < 32) {
+    const uint64_t m = __builtin_amdgcn_ballot_w64(((word >> kBit) & 1u) != 0u);
+    lo = write_lane<kBase + kBit>(lo, static_cast<uint32_t>(m));
+    hi = write_lane<kBase + kBit>(hi, static_cast<uint32_t>(m >> 32));
+    collect_word<kBase, kBit + 1>(word, lo, hi);
   }
 }
 
-__global__ __launch_bounds__(1024) void block_counts_kernel(const uint32_t* __restrict__ bm,
-                                                            int64_t T, int E, int words,
-                                                            int32_t* __restrict__ blk) {
-  extern __shared__ int cnt[];   // [kWaves][E]
+// masks[e] (LDS) <- column mask of expert e over this wavefront's 64 tokens.
+__device__ __forceinline__ void wave_column_masks(const uint32_t* __restrict__ bm, int64_t t0,
+                                                  int64_t T, int E, int words, int lane,
+                                                  uint64_t* __restrict__ masks) {
+  const int64_t t = t0 + lane;
+  const bool valid = t < T;
+  if (t0 >= T) {   // no token in this wavefront
+    for (int e = lane; e < E; e += 64) masks[e] = 0ull;
+    return;
+  }
+  for (int w0 = 0; w0 < words; w0 += 2) {
+    const uint32_t word0 = valid ? bm[t * words + w0] : 0u;
+    const uint32_t word1 = (valid && w0 + 1 < words) ? bm[t * words + w0 + 1] : 0u;
+    uint32_t lo = 0u, hi = 0u;
+    collect_word<0>(word0, lo, hi);
+    collect_word<32>(word1, lo, hi);
+    const int e = w0 * 32 + lane;
+    if (e < E) masks[e] = (static_cast<uint64_t>(hi) << 32) | lo;
+  }
+}
+
+// Rows of this wavefront's tokens: p = base[e] + rank of the token within e.
+__device__ __forceinline__ void write_permutations(const int32_t* __restrict__ ids, int64_t t,
+                                                   int64_t T, int k, int lane,
+                                                   const uint64_t* __restrict__ masks,
+                                                   const int32_t* __restrict__ base, int E,
+                                                   int32_t* __restrict__ gather,
+                                                   int32_t* __restrict__ scatter) {
+  if (t >= T) return;
+  const uint64_t below = (1ull << lane) - 1ull;
+  const int64_t n_slots = T * k;
+  for (int j = 0; j < k; ++j) {
+    const int64_t s = t * k + j;
+    const int e = ids[s];
+    if (static_cast<unsigned>(e) >= static_cast<unsigned>(E)) continue;
+    const int64_t p = static_cast<int64_t>(base[e]) + __popcll(masks[e] & below);
+    if (p < 0 || p >= n_slots) continue;
+    gather[p] = static_cast<int32_t>(s);
+    scatter[s] = static_cast<int32_t>(p);
+  }
+}
+
+// Exclusive scan of one value per thread over a workgroup of 512 threads.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* __restrict__ wave_tot, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * kOffsBlockTokens + threadIdx.x;
-  wave_expert_counts(bm, t, t < T, E, words, lane, cnt + wave * E);
+  int incl = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += o;
+  }
+  if (lane == 63) wave_tot[wave] = incl;
+  __syncthreads();
+  int before = 0, all = 0;
+  for (int w = 0; w < static_cast<int>(blockDim.x >> 6); ++w) {
+    const int tw = wave_tot[w];
+    before += w < wave ? tw : 0;
+    all += tw;
+  }
+  *total = all;
+  return before + incl - v;
+}
+
+// T <= 512: everything in one workgroup.
+__global__ __launch_bounds__(kOffsBlockTokens) void offsets_small_kernel(
+    const uint32_t* __restrict__ bm, const int32_t* __restrict__ ids, int64_t T, int E, int k,
+    int words, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ gather, int32_t* __restrict__ scatter) {
+  extern __shared__ uint64_t lds[];
+  uint64_t* masks = lds;                                                   // [kWaves][E]
+  int32_t* base = reinterpret_cast<int32_t*>(masks + kWaves * E);          // [kWaves][E]
+  __shared__ int wave_tot[kWaves];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  wave_column_masks(bm, static_cast<int64_t>(wave) * 64, T, E, words, lane, masks + wave * E);
+  __syncthreads();
+
+  // two experts per thread (E <= 1024): per-wavefront prefix, then scan over experts
+  const int e0 = 2 * threadIdx.x;
+  int c[2] = {0, 0};
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int e = e0 + q;
+    if (e < E) {
+      int run = 0;
+      for (int w = 0; w < kWaves; ++w) {
+        base[w * E + e] = run;
+        run += __popcll(masks[w * E + e]);
+      }
+      c[q] = run;
+    }
+  }
+  int total;
+  const int first = block_exclusive_scan(c[0] + c[1], wave_tot, &total);
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int e = e0 + q;
+    if (e < E) {
+      const int off = first + (q ? c[0] : 0);
+      counts[e] = c[q];
+      offsets[e] = off;
+      for (int w = 0; w < kWaves; ++w) base[w * E + e] += off;
+    }
+  }
+  if (threadIdx.x == 0) offsets[E] = total;
+  __syncthreads();
+  write_permutations(ids, static_cast<int64_t>(threadIdx.x), T, k, lane, masks + wave * E,
+                     base + wave * E, E, gather, scatter);
+}
+
+__global__ __launch_bounds__(kOffsBlockTokens) void block_counts_kernel(
+    const uint32_t* __restrict__ bm, int64_t T, int E, int words, int32_t* __restrict__ blk) {
+  extern __shared__ uint64_t masks[];   // [kWaves][E]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kOffsBlockTokens + wave * 64;
+  wave_column_masks(bm, t0, T, E, words, lane, masks + wave * E);
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
     int s = 0;
-    for (int w = 0; w < kWaves; ++w) s += cnt[w * E + e];
+    for (int w = 0; w < kWaves; ++w) s += __popcll(masks[w * E + e]);
     blk[static_cast<int64_t>(blockIdx.x) * E + e] = s;
   }
 }
 
+// One workgroup of 1024 threads: thread e turns expert e's per-block counts into
+// exclusive per-block bases (in place) and its total; a scan over e gives offsets.
 __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ blk, int64_t n_blocks,
                                                     int E, int32_t* __restrict__ counts,
                                                     int32_t* __restrict__ offsets) {
   __shared__ int wave_tot[16];
   const int e = threadIdx.x;
-  const int lane = e & 63, wave = e >> 6;
   int run = 0;
   if (e < E) {
     int64_t b = 0;
@@ -83,70 +200,33 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ blk, i
     }
     counts[e] = run;
   }
-  // exclusive scan of run over e: wavefront inclusive scan, then wavefront totals
-  int incl = run;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int o = __shfl_up(incl, d, 64);
-    if (lane >= d) incl += o;
-  }
-  if (lane == 63) wave_tot[wave] = incl;
-  __syncthreads();
-  int base = 0;
-  for (int w = 0; w < wave; ++w) base += wave_tot[w];
-  if (e < E) offsets[e] = base + incl - run;
-  if (e == E - 1) offsets[E] = base + incl;
+  int total;
+  const int first = block_exclusive_scan(run, wave_tot, &total);
+  if (e < E) offsets[e] = first;
+  if (e == 0) offsets[E] = total;
 }
 
-__global__ __launch_bounds__(1024) void ranks_kernel(const uint32_t* __restrict__ bm,
-                                                     const int32_t* __restrict__ ids, int64_t T,
-                                                     int E, int k, int words,
-                                                     const int32_t* __restrict__ blk,
-                                                     const int32_t* __restrict__ offsets,
-                                                     int32_t* __restrict__ gather,
-                                                     int32_t* __restrict__ scatter) {
-  extern __shared__ int cnt[];   // [kWaves][E] -> row bases
+__global__ __launch_bounds__(kOffsBlockTokens) void ranks_kernel(
+    const uint32_t* __restrict__ bm, const int32_t* __restrict__ ids, int64_t T, int E, int k,
+    int words, const int32_t* __restrict__ blk, const int32_t* __restrict__ offsets,
+    int32_t* __restrict__ gather, int32_t* __restrict__ scatter) {
+  extern __shared__ uint64_t lds[];
+  uint64_t* masks = lds;                                                   // [kWaves][E]
+  int32_t* base = reinterpret_cast<int32_t*>(masks + kWaves * E);          // [kWaves][E]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t t = static_cast<int64_t>(blockIdx.x) * kOffsBlockTokens + threadIdx.x;
-  const bool valid = t < T;
-  wave_expert_counts(bm, t, valid, E, words, lane, cnt + wave * E);
+  const int64_t t0 = static_cast<int64_t>(blockIdx.x) * kOffsBlockTokens + wave * 64;
+  wave_column_masks(bm, t0, T, E, words, lane, masks + wave * E);
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    int base = offsets[e] + blk[static_cast<int64_t>(blockIdx.x) * E + e];
+    int run = offsets[e] + blk[static_cast<int64_t>(blockIdx.x) * E + e];
     for (int w = 0; w < kWaves; ++w) {
-      const int c = cnt[w * E + e];
-      cnt[w * E + e] = base;
-      base += c;
+      base[w * E + e] = run;
+      run += __popcll(masks[w * E + e]);
     }
   }
   __syncthreads();
-
-  int my_ids[kMaxK];
-#pragma unroll
-  for (int j = 0; j < kMaxK; ++j) my_ids[j] = (valid && j < k) ? ids[t * k + j] : -1;
-  const int64_t n_slots = T * k;
-  const unsigned long long below = (1ull << lane) - 1ull;
-  for (int w = 0; w < words; ++w) {
-    const uint32_t word = valid ? bm[t * words + w] : 0u;
-    const int nbits = (E - w * 32) < 32 ? (E - w * 32) : 32;
-    for (int b = 0; b < nbits; ++b) {
-      const bool mine = (word >> b) & 1u;
-      const unsigned long long m = __ballot(mine);
-      if (mine) {
-        const int e = w * 32 + b;
-        const int64_t p = static_cast<int64_t>(cnt[wave * E + e]) + __popcll(m & below);
-        int j = -1;
-#pragma unroll
-        for (int q = 0; q < kMaxK; ++q)
-          if (my_ids[q] == e) j = q;
-        if (j >= 0 && p >= 0 && p < n_slots) {
-          const int64_t s = t * k + j;
-          gather[p] = static_cast<int32_t>(s);
-          scatter[s] = static_cast<int32_t>(p);
-        }
-      }
-    }
-  }
+  write_permutations(ids, t0 + lane, T, k, lane, masks + wave * E, base + wave * E, E, gather,
+                     scatter);
 }
 
 __global__ void zero_counts_kernel(int32_t* counts, int32_t* offsets, int E) {
@@ -166,18 +246,24 @@ hipError_t launch_offsets(const uint32_t* bm, const int32_t* ids, int64_t T, int
     return hipGetLastError();
   }
   const int words = (E + 31) / 32;
+  const size_t lds_masks = static_cast<size_t>(kWaves) * E * sizeof(uint64_t);
+  const size_t lds_base = static_cast<size_t>(kWaves) * E * sizeof(int32_t);
+  if (T <= kOffsBlockTokens) {
+    offsets_small_kernel<<<1, kOffsBlockTokens, lds_masks + lds_base, stream>>>(
+        bm, ids, T, E, k, words, counts, offsets, gather, scatter);
+    return hipGetLastError();
+  }
   const int64_t n_blocks = (T + kOffsBlockTokens - 1) / kOffsBlockTokens;
   int32_t* blk = static_cast<int32_t*>(ws);
-  const size_t lds = static_cast<size_t>(kWaves) * E * sizeof(int);
-  block_counts_kernel<<<dim3(static_cast<unsigned>(n_blocks)), dim3(kOffsBlockTokens), lds, stream>>>(
-      bm, T, E, words, blk);
+  const dim3 grid(static_cast<unsigned>(n_blocks)), block(kOffsBlockTokens);
+  block_counts_kernel<<<grid, block, lds_masks, stream>>>(bm, T, E, words, blk);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   scan_kernel<<<1, 1024, 0, stream>>>(blk, n_blocks, E, counts, offsets);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  ranks_kernel<<<dim3(static_cast<unsigned>(n_blocks)), dim3(kOffsBlockTokens), lds, stream>>>(
-      bm, ids, T, E, k, words, blk, offsets, gather, scatter);
+  ranks_kernel<<<grid, block, lds_masks + lds_base, stream>>>(bm, ids, T, E, k, words, blk,
+                                                              offsets, gather, scatter);
   return hipGetLastError();
 }
 

@@ -20,8 +20,16 @@ moe_status check_sizes(int64_t T, int32_t E, int32_t k) {
 
 moe_status check_dims(int32_t H, int32_t I) {
   if (H <= 0 || I <= 0) return MOE_ERR_INVALID_ARGUMENT;
-  if (H % 128 != 0 || I % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if (H % 128 != 0 || I % 128 != 0 || H > kMaxDim || I > kMaxDim) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
+}
+
+// Activation buffers (x: T*H bf16, h: T*k*I bf16) are addressed with 32-bit byte
+// offsets; keep them below 3.5 GiB.
+bool activations_fit(int64_t T, int32_t k, int32_t H, int32_t I) {
+  const int64_t lim = static_cast<int64_t>(kMaxActivationBytes);
+  return T * H * 2 <= lim && T * k * static_cast<int64_t>(I) * 2 <= lim &&
+         T * k * static_cast<int64_t>(H) * 2 <= lim;
 }
 
 }  // namespace
@@ -34,7 +42,7 @@ moe_status workspace_layout(int64_t T, int32_t E, int32_t k, int32_t H, int32_t 
   const int64_t slots = T * k;
   L.n_blocks = (T + kOffsBlockTokens - 1) / kOffsBlockTokens;
   L.offsets_bytes = align_up(static_cast<size_t>(L.n_blocks) * E * sizeof(int32_t), 256);
-  L.tile_bound = (slots < E ? slots : E) + slots / kFfnTileRows;
+  L.tile_bound = ffn_tile_bound(slots, E, kFfnMinTileRows);
   L.ffn_h_offset = 0;
   L.ffn_plan_offset = align_up(static_cast<size_t>(slots) * static_cast<size_t>(I) * 2, 256);
   L.ffn_bytes = L.ffn_plan_offset + align_up(256 + static_cast<size_t>(L.tile_bound) * sizeof(RowTile), 256);
@@ -87,6 +95,7 @@ moe_status check_ffn(const void* x, int64_t T, int32_t H, int32_t I, int32_t E, 
   if (s != MOE_OK) return s;
   s = check_dims(H, I);
   if (s != MOE_OK || T == 0) return s;
+  if (!activations_fit(T, k, H, I)) return MOE_ERR_UNSUPPORTED;
   if (!x || !w1 || !w1s || !w2 || !w2s || !counts || !offsets || !gather || !y_sorted || !ws)
     return MOE_ERR_INVALID_ARGUMENT;
   if (!aligned(x, 16) || !aligned(w1, 16) || !aligned(w2, 16) || !aligned(y_sorted, 16) ||

@@ -61,6 +61,8 @@ def to_device(inp: dict, device="cuda") -> dict:
         if key not in inp:
             continue
         a = np.ascontiguousarray(inp[key])
+        if not a.flags.writeable:
+            a = a.copy()
         if key == "x":
             a = a.view(np.int16)
         out[key] = torch.from_numpy(a).to(dev)

@@ -49,7 +49,7 @@ def run_gpu(inp, limit=10.0):
     wl = inp["workload"]
     dev = layer.to_device(inp)
     b = layer.LayerBuffers.allocate(T, wl.E, wl.k, wl.H, wl.I)
-    layer.run_layer(dev, b, limit)
+    layer.run_layer(dev, b, 0.0 if limit is None else limit)   # <= 0 turns the clamp off
     torch.cuda.synchronize()
     return b
 
@@ -184,8 +184,9 @@ def test_outputs_leave_guard_bytes_untouched():
     T, E, k, H, I = 37, 64, 6, 256, 128
     pad = 4096
     def guarded(n, dtype):
-        t = torch.full((n + pad,), 0x5A, dtype=torch.uint8, device="cuda")
-        return t, t[: n * torch.tensor([], dtype=dtype).element_size()].view(dtype)
+        nbytes = n * torch.tensor([], dtype=dtype).element_size()
+        t = torch.full((nbytes + pad,), 0x5A, dtype=torch.uint8, device="cuda")
+        return t, t[:nbytes].view(dtype)
     bufs = {}
     shapes = dict(ids=(T * k, torch.int32), w=(T * k, torch.float32), bm=(T * 2, torch.int32),
                   counts=(E, torch.int32), offsets=(E + 1, torch.int32), gather=(T * k, torch.int32),
