@@ -68,6 +68,24 @@ class HipEvents:
         return f.value
 
 
+def measured_traffic(profile_name: str, kernel_source: str):
+    """HBM bytes per launch from a committed rocprofv3 summary, or None when the
+    kernel source has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", profile_name)
+    try:
+        fields = dict(line.split(":", 1) for line in open(path) if line.count(":") == 1
+                      and line.split(":")[0] in ("traffic_bytes_per_launch",
+                                                  "kernel_source_sha256_prefix"))
+        want = fields["kernel_source_sha256_prefix"].strip()
+        have = hashlib.sha256(open(os.path.join(ROOT, kernel_source), "rb").read()).hexdigest()
+        if not have.startswith(want):
+            return None
+        return int(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(inp, n_tokens):
     """The oracle, as it stands, on the first n_tokens tokens of the workload."""
     import oracle
@@ -98,6 +116,9 @@ def main():
     ap.add_argument("--weight-copies", type=int, default=2)
     ap.add_argument("--cpu-tokens", type=int, default=4,
                     help="tokens in the CPU oracle sample (0: skip)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="instead of the layer, run a plain device-to-device copy of this many "
+                         "MiB (--steps times): the reference for HBM traffic counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer is "
@@ -110,7 +131,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    binding.load()
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": args.steps}), flush=True)
+        return
     lib = binding.load()
     wl = inputs.workload(args.workload)
     T, E, k, H, I = wl.T, wl.E, wl.k, wl.H, wl.I
@@ -222,7 +251,10 @@ def main():
         "touched_experts": touched,
         "roofline": {"bound": "hbm", "kernel": "gemm_kernel<true> (W1 gate|up + SwiGLU)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": (measured_traffic("ffn_w1_stream_verify-1+7.md",
+                                                  "mxfp4_routed_expert_route_amd/csrc/ffn.hip")
+                                 if wl.index == 1 else None),
                      "algorithmic_bytes_per_launch": w1_alg},
         "layer_hbm_frac": layer_alg / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "ffn_hbm_frac": (touched * (w1_bytes_per_expert + w2_bytes_per_expert))
