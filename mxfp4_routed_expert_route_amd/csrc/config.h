@@ -19,8 +19,6 @@ constexpr int kOffsBlockTokens = 512;
 constexpr int kFfnTileRows = 64;
 constexpr int kFfnMinTileRows = 16;
 constexpr int kFfnKChunk = 128;
-constexpr int kFfnW1ColsPerBlock = 64;   // gate columns per workgroup (plus the matching up columns)
-constexpr int kFfnW2ColsPerBlock = 128;  // output columns per workgroup
 // streaming path: LDS for the staged E8M0 scales of a workgroup (4 wavefronts x
 // 64 rows x K/32 bytes); above this the scales are read from memory
 constexpr size_t kStreamMaxScaleLds = 64 * 1024;

@@ -7,21 +7,23 @@
 // [-limit, +limit], both before the SwiGLU product.
 //
 // Work decomposition.  A plan kernel cuts each expert's rows [offsets[e],
-// offsets[e+1]) into row tiles of up to 64 rows; only experts with rows get
-// tiles.  A GEMM workgroup owns one (row tile, column block): 4 wavefronts, each
-// with two 16-column weight fragments (W1: 16 gate rows and the 16 matching up
-// rows, so the SwiGLU pairs meet in one lane; W2: 32 output rows) and all rows of
-// the tile as up to four 16-row MFMA subtiles.
+// offsets[e+1]) into row tiles (16, 32 or 64 rows, chosen from T and the mean
+// rows per expert); only experts with rows get tiles.  A wavefront always owns
+// 64 weight rows of one tile's expert -- for W1 32 gate rows and the 32 matching
+// up rows, so each SwiGLU pair meets in one lane; for W2 64 output rows -- as four
+// 16-column MFMA fragments.  Few rows per expert (decode shapes): the streaming
+// kernel, one independent wavefront per (tile, 64 weight rows), bound by HBM.
+// Many rows: the tiled kernel, four wavefronts sharing an LDS activation tile.
 //
-// Inner step (K chunk of 128): every lane streams 16 bytes (32 codes, exactly one
-// scale block) of one weight row straight from HBM, so a fragment row is read as
-// one 64-byte run per chunk.  The codes are dequantised in registers with the
-// gfx950 scaled FP4->BF16 convert (scale passed as an fp32 whose exponent field
-// is the E8M0 byte; 0xFF maps to a NaN scale) and fed to
-// v_mfma_f32_16x16x32_bf16 as the B operand; activations are the A operand.
-// Within one MFMA the K order of the 32 products does not matter as long as A
-// and B agree, so lane group g (lanes 16g..16g+15) takes K = chunk + 32g + 8s ..
-// +7 for sub-step s on both operands.  fp32 accumulation throughout.
+// Inner step (K chunk of 128): every lane loads 16 bytes (32 codes, exactly one
+// scale block) of one weight row straight from HBM, so a weight row is read in
+// 64-byte runs.  The codes are dequantised in registers with the gfx950 scaled
+// FP4->BF16 convert (scale passed as an fp32 whose exponent field is the E8M0
+// byte; 0xFF maps to a NaN scale) and fed to v_mfma_f32_16x16x32_bf16 as the B
+// operand; activations are the A operand.  Within one MFMA the K order of the 32
+// products does not matter as long as A and B agree, so lane group g (lanes
+// 16g..16g+15) takes K = chunk + 32g + 8s .. +7 for sub-step s on both operands.
+// fp32 accumulation throughout.
 #include "config.h"
 #include "device.h"
 #include "launch.h"
@@ -99,108 +101,6 @@ __device__ __forceinline__ float swiglu(float g, float u, float limit, bool clam
     u = u > limit ? limit : (u < -limit ? -limit : u);
   }
   return g / (1.0f + __expf(-g)) * u;
-}
-
-// kW1: act = x [T][K] gathered through gather[p] / k_top; out = h [n_slots][I] with
-//      column block of 64 gate columns; B fragments = gate rows and up rows.
-// !kW1: act = h [n_slots][K]; out = y_sorted [n_slots][N]; column block of 128.
-template <bool kW1>
-__global__ __launch_bounds__(256) void gemm_kernel(
-    const uint16_t* __restrict__ act, const int32_t* __restrict__ gather, int k_top,
-    int n_slots, const uint8_t* __restrict__ wq, const uint8_t* __restrict__ wsc,
-    const RowTile* __restrict__ tiles, const int32_t* __restrict__ n_tiles, int K, int n_rows,
-    int half, int blocks_per_tile, float limit, int clamp, uint16_t* __restrict__ out,
-    int ld_out) {
-  const int tile_id = blockIdx.x / blocks_per_tile;
-  const int nb = blockIdx.x - tile_id * blocks_per_tile;
-  if (tile_id >= *n_tiles) return;
-  const RowTile rt = tiles[tile_id];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int r16 = lane & 15, g = lane >> 4;
-  const int rows = rt.p_end - rt.p_begin;
-  const int msub = (rows + 15) >> 4;
-
-  // activation rows this lane feeds (A operand row r16 of each subtile)
-  const uint16_t* arow[4];
-  bool aval[4];
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi) {
-    const int p = rt.p_begin + mi * 16 + r16;
-    aval[mi] = p < rt.p_end;
-    int64_t src = 0;
-    if (aval[mi]) {
-      if (kW1) {
-        const int slot = gather[p];   // a slot id outside [0, T*k) feeds zeros, never an address
-        aval[mi] = static_cast<unsigned>(slot) < static_cast<unsigned>(n_slots);
-        src = aval[mi] ? slot / k_top : 0;
-      } else {
-        src = p;
-      }
-    }
-    arow[mi] = act + src * K + 32 * g;
-  }
-
-  // weight rows this lane streams (B operand column r16 of each fragment)
-  int n0, n1;
-  if (kW1) {
-    n0 = nb * kFfnW1ColsPerBlock + wave * 16 + r16;   // gate row
-    n1 = half + n0;                                   // matching up row
-  } else {
-    n0 = nb * kFfnW2ColsPerBlock + wave * 32 + r16;
-    n1 = n0 + 16;
-  }
-  const size_t row_q = static_cast<size_t>(K / 2), row_s = static_cast<size_t>(K / 32);
-  const size_t e_rows = static_cast<size_t>(rt.expert) * n_rows;
-  const uint8_t* bq0 = wq + (e_rows + n0) * row_q + 16 * g;
-  const uint8_t* bq1 = wq + (e_rows + n1) * row_q + 16 * g;
-  const uint8_t* bs0 = wsc + (e_rows + n0) * row_s + g;
-  const uint8_t* bs1 = wsc + (e_rows + n1) * row_s + g;
-
-  floatx4 acc[4][2];
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi) acc[mi][0] = acc[mi][1] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  const int n_chunks = K / kFfnKChunk;
-  for (int kc = 0; kc < n_chunks; ++kc) {
-    const uint4 q0 = *reinterpret_cast<const uint4*>(bq0 + kc * 64);
-    const uint4 q1 = *reinterpret_cast<const uint4*>(bq1 + kc * 64);
-    const float s0 = e8m0_as_f32(bs0[kc * 4]);
-    const float s1 = e8m0_as_f32(bs1[kc * 4]);
-    const uint32_t w0[4] = {q0.x, q0.y, q0.z, q0.w};
-    const uint32_t w1[4] = {q1.x, q1.y, q1.z, q1.w};
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const bf16x8 b0 = dequant8(w0[s], s0);
-      const bf16x8 b1 = dequant8(w1[s], s1);
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi) {
-        if (mi < msub) {
-          const bf16x8 a = aval[mi] ? load_bf16x8(arow[mi] + kc * kFfnKChunk + 8 * s) : bf16x8{};
-          acc[mi][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b0, acc[mi][0], 0, 0, 0);
-          acc[mi][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b1, acc[mi][1], 0, 0, 0);
-        }
-      }
-    }
-  }
-
-  // D layout of a 16x16 MFMA tile: lane holds column (lane & 15), rows 4*(lane>>4) + i.
-  const bool do_clamp = clamp != 0;
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi) {
-    if (mi >= msub) continue;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int p = rt.p_begin + mi * 16 + 4 * g + i;
-      if (p >= rt.p_end) continue;
-      uint16_t* orow = out + static_cast<int64_t>(p) * ld_out;
-      if (kW1) {
-        orow[n0] = f32_to_bf16_bits(swiglu(acc[mi][0][i], acc[mi][1][i], limit, do_clamp));
-      } else {
-        orow[n0] = f32_to_bf16_bits(acc[mi][0][i]);
-        orow[n1] = f32_to_bf16_bits(acc[mi][1][i]);
-      }
-    }
-  }
 }
 
 // ---------------------------------------------------------------- streaming GEMM (few rows)
@@ -426,6 +326,220 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
   }
 }
 
+// ---------------------------------------------------------------- tiled GEMM (many rows)
+//
+// For row tiles of up to 64 rows (prefill-shaped batches).  A workgroup of four
+// wavefronts owns one 64-row tile and 256 weight rows; each wavefront has 64
+// weight rows (same split as the streaming kernel: W1 32 gate + 32 up rows, W2
+// 64 output rows) and all four 16-row MFMA subtiles, so each dequantised weight
+// fragment feeds four MFMAs.  The activation tile of each K chunk (64 rows x 128
+// bf16) is loaded once per workgroup into LDS (double-buffered; rows padded by
+// 16 bytes so that the 16 lanes of a read group hit distinct banks) and read by
+// all four wavefronts.  Weights go straight to registers, prefetched about one
+// and a half chunks ahead; scales are staged in LDS as in the streaming kernel.
+//
+// Per chunk c: issue the activation loads of c+1, compute c (LDS activations,
+// register weights), issue the weight loads of c+2 into the registers c just
+// freed, store the activations of c+1 to the other LDS buffer, barrier.
+constexpr int kTileRows = 64;
+constexpr int kARowBytes = kFfnKChunk * 2 + 16;   // 256 B of bf16 + 16 B pad
+constexpr int kABufBytes = kTileRows * kARowBytes;
+
+template <bool kW1>
+__global__ __launch_bounds__(256, 2) void gemm_tile_kernel(
+    const uint16_t* __restrict__ act, uint32_t act_bytes, const int32_t* __restrict__ gather,
+    int k_top, int n_slots, const uint8_t* __restrict__ wq, const uint8_t* __restrict__ wsc,
+    const RowTile* __restrict__ tiles, const int32_t* __restrict__ n_tiles, int K, int n_rows,
+    int half, int waves_per_tile, int blocks_per_tile, float limit, int clamp,
+    uint16_t* __restrict__ out, int ld_out) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char tile_lds[];
+  const int tile_id = blockIdx.x / blocks_per_tile;
+  const int nb = blockIdx.x - tile_id * blocks_per_tile;
+  if (tile_id >= *n_tiles) return;   // uniform over the workgroup
+  const RowTile rt = tiles[tile_id];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int n_chunks = K / kFfnKChunk;
+  const int rows = rt.p_end - rt.p_begin;
+  const int msub = (rows + 15) >> 4;   // 1..4 subtiles hold rows
+
+  // column group of this wavefront; a wavefront past the last group repeats the
+  // last one (it still stages activations and meets every barrier) and stores nothing
+  const int cg_raw = nb * 4 + wave;
+  const bool store_cols = cg_raw < waves_per_tile;
+  const int cg = store_cols ? cg_raw : waves_per_tile - 1;
+
+  // --- activation staging: thread -> (row ar, 64-byte quarter aq) of the chunk
+  const __amdgpu_buffer_rsrc_t arsrc = make_rsrc(act, act_bytes);
+  const int ar = tid >> 2, aq = tid & 3;
+  uint32_t aoff;
+  {
+    const int p = rt.p_begin + ar;
+    bool valid = p < rt.p_end;
+    uint32_t row = 0;
+    if (valid) {
+      if (kW1) {
+        const int slot = gather[p];
+        valid = static_cast<unsigned>(slot) < static_cast<unsigned>(n_slots);
+        row = valid ? static_cast<uint32_t>(slot / k_top) : 0u;
+      } else {
+        row = static_cast<uint32_t>(p);
+      }
+    }
+    aoff = valid ? row * static_cast<uint32_t>(K) * 2u + 64u * aq : kRsrcOutOfRange;
+  }
+  unsigned char* a_lds = tile_lds;                       // [2][64][kARowBytes]
+  const int a_store = ar * kARowBytes + aq * 64;
+  auto load_a = [&](uint4 (&ra)[4], int kc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      ra[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            arsrc, aoff + kc * 256 + 16 * i, 0, 0));
+  };
+  auto store_a = [&](const uint4 (&ra)[4], int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<uint4*>(a_lds + buf * kABufBytes + a_store + 16 * i) = ra[i];
+  };
+
+  // --- weights: four fragments of 16 rows, this lane's row in each
+  auto wrow = [&](int f, int c16) {
+    return kW1 ? (f >= 2 ? half : 0) + cg * 32 + (f & 1) * 16 + c16 : cg * 64 + f * 16 + c16;
+  };
+  int nrow[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) nrow[f] = wrow(f, r16);
+  const size_t row_q = static_cast<size_t>(K / 2), row_s = static_cast<size_t>(K / 32);
+  const size_t e_rows = static_cast<size_t>(rt.expert) * n_rows;
+  const uint8_t* bq[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) bq[f] = wq + (e_rows + nrow[f]) * row_q + 16 * g;
+  auto load_w = [&](uint4 (&q)[4], int kc) {
+#pragma unroll
+    for (int f = 0; f < 4; ++f) q[f] = *reinterpret_cast<const uint4*>(bq[f] + kc * 64);
+  };
+
+  // --- scales of the wavefront's 64 rows, staged as [chunk][16][4] dwords
+  uint32_t* my_scales =
+      reinterpret_cast<uint32_t*>(tile_lds + 2 * kABufBytes) + wave * (n_chunks * 64);
+  {
+    const int f = lane >> 4;
+    const uint8_t* srow = wsc + (e_rows + wrow(f, r16)) * row_s;
+    int c = 0;
+    for (; c + 4 <= n_chunks; c += 4) {
+      const uint4 d = *reinterpret_cast<const uint4*>(srow + c * 4);
+      my_scales[((c + 0) * 16 + r16) * 4 + f] = d.x;
+      my_scales[((c + 1) * 16 + r16) * 4 + f] = d.y;
+      my_scales[((c + 2) * 16 + r16) * 4 + f] = d.z;
+      my_scales[((c + 3) * 16 + r16) * 4 + f] = d.w;
+    }
+    for (; c < n_chunks; ++c)
+      my_scales[(c * 16 + r16) * 4 + f] = *reinterpret_cast<const uint32_t*>(srow + c * 4);
+  }
+  auto lds_s = [&](uint32_t (&sc)[4], int kc) {
+    const uint4 d = *reinterpret_cast<const uint4*>(my_scales + (kc * 16 + r16) * 4);
+    const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+    for (int f = 0; f < 4; ++f) sc[f] = (dw[f] >> (8 * g)) & 0xFFu;
+  };
+
+  floatx4 acc[4][4];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int f = 0; f < 4; ++f) acc[mi][f] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  // one chunk: A from LDS buffer `buf`, weights in q
+  auto compute = [&](const uint4 (&q)[4], int kc, int buf) {
+    uint32_t sc[4];
+    lds_s(sc, kc);
+    float scl[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) scl[f] = e8m0_as_f32(sc[f]);
+    const uint32_t w[4][4] = {{q[0].x, q[0].y, q[0].z, q[0].w},
+                              {q[1].x, q[1].y, q[1].z, q[1].w},
+                              {q[2].x, q[2].y, q[2].z, q[2].w},
+                              {q[3].x, q[3].y, q[3].z, q[3].w}};
+    const unsigned char* abase = a_lds + buf * kABufBytes + r16 * kARowBytes + 64 * g;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      bf16x8 b[4];
+#pragma unroll
+      for (int f = 0; f < 4; ++f) b[f] = dequant8(w[f][s], scl[f]);
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi) {
+        if (mi < msub) {   // uniform
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(abase + mi * 16 * kARowBytes + 16 * s);
+#pragma unroll
+          for (int f = 0; f < 4; ++f)
+            acc[mi][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[f], acc[mi][f], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  // prologue: chunk 0 activations into buffer 0, weights of chunks 0 and 1
+  uint4 ra[4], q0[4], q1[4];
+  load_a(ra, 0);
+  load_w(q0, 0);
+  load_w(q1, n_chunks > 1 ? 1 : 0);
+  store_a(ra, 0);
+  __syncthreads();
+
+  const int last = n_chunks - 1;
+  int kc = 0;
+  for (; kc + 2 <= n_chunks; kc += 2) {
+    // chunk kc (buffer 0, weights q0)
+    load_a(ra, kc + 1);
+    compute(q0, kc, 0);
+    load_w(q0, kc + 2 <= last ? kc + 2 : last);
+    store_a(ra, 1);
+    __syncthreads();
+    // chunk kc+1 (buffer 1, weights q1)
+    load_a(ra, kc + 2 <= last ? kc + 2 : last);
+    compute(q1, kc + 1, 1);
+    load_w(q1, kc + 3 <= last ? kc + 3 : last);
+    store_a(ra, 0);
+    __syncthreads();
+  }
+  if (kc < n_chunks) compute(q0, kc, 0);   // odd chunk count: last chunk in buffer 0 / q0
+
+  if (!store_cols) return;
+  const bool do_clamp = clamp != 0;
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) {
+    if (mi >= msub) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int p = rt.p_begin + mi * 16 + 4 * g + i;
+      if (p >= rt.p_end) continue;
+      uint16_t* orow = out + static_cast<int64_t>(p) * ld_out;
+      if (kW1) {
+        orow[nrow[0]] = f32_to_bf16_bits(swiglu(acc[mi][0][i], acc[mi][2][i], limit, do_clamp));
+        orow[nrow[1]] = f32_to_bf16_bits(swiglu(acc[mi][1][i], acc[mi][3][i], limit, do_clamp));
+      } else {
+#pragma unroll
+        for (int f = 0; f < 4; ++f) orow[nrow[f]] = f32_to_bf16_bits(acc[mi][f][i]);
+      }
+    }
+  }
+}
+
+template <bool kW1>
+hipError_t launch_tile(int64_t tile_bound, hipStream_t stream, const uint16_t* act,
+                       uint32_t act_bytes, const int32_t* gather, int k_top, int n_slots,
+                       const uint8_t* wq, const uint8_t* wsc, const RowTile* tiles,
+                       const int32_t* n_tiles, int K, int n_rows, int half, int wpt, float limit,
+                       int clamp, uint16_t* out, int ld_out) {
+  const int bpt = (wpt + 3) / 4;
+  const size_t lds = 2 * static_cast<size_t>(kABufBytes) +
+                     static_cast<size_t>(4) * (K / kFfnKChunk) * 64 * sizeof(uint32_t);
+  gemm_tile_kernel<kW1><<<static_cast<unsigned>(tile_bound * bpt), 256, lds, stream>>>(
+      act, act_bytes, gather, k_top, n_slots, wq, wsc, tiles, n_tiles, K, n_rows, half, wpt, bpt,
+      limit, clamp, out, ld_out);
+  return hipGetLastError();
+}
+
 // Launch one streaming GEMM; picks the deep pipeline when K allows it.
 template <bool kW1, int MSUB>
 hipError_t launch_stream(unsigned grid, hipStream_t stream, const uint16_t* act, uint32_t act_bytes,
@@ -505,20 +619,17 @@ hipError_t launch_ffn(const uint16_t* x, int64_t T, int H, int I, int E, int k,
               : launch_stream<false, 2>(g2, stream, h, h_bytes, nullptr, k, slots_i, w2, w2s,
                                         tiles, n_tiles, I, H, 0, wpt2, limit, 0, y_sorted, H);
   } else {
-    const int bpt1 = I / kFfnW1ColsPerBlock;
-    gemm_kernel<true><<<dim3(static_cast<unsigned>(tile_bound * bpt1)), dim3(256), 0, stream>>>(
-        x, gather, k, slots_i, w1, w1s, tiles, n_tiles, H, 2 * I, I, bpt1, limit, clamp_i, h, I);
-    err = hipGetLastError();
+    const int wpt1 = I / 32, wpt2 = H / 64;
+    err = launch_tile<true>(tile_bound, stream, x, x_bytes, gather, k, slots_i, w1, w1s, tiles,
+                            n_tiles, H, 2 * I, I, wpt1, limit, clamp_i, h, I);
     if (err != hipSuccess) return err;
     if (events) {
       err = hipEventRecord(events[1], stream);
       if (err != hipSuccess) return err;
     }
-    const int bpt2 = H / kFfnW2ColsPerBlock;
-    gemm_kernel<false><<<dim3(static_cast<unsigned>(tile_bound * bpt2)), dim3(256), 0, stream>>>(
-        h, nullptr, k, slots_i, w2, w2s, tiles, n_tiles, I, H, 0, bpt2, limit, 0, y_sorted, H);
+    err = launch_tile<false>(tile_bound, stream, h, h_bytes, nullptr, k, slots_i, w2, w2s, tiles,
+                             n_tiles, I, H, 0, wpt2, limit, 0, y_sorted, H);
   }
-  err = hipGetLastError();
   if (err != hipSuccess || !events) return err;
   return hipEventRecord(events[2], stream);
 }
