@@ -14,9 +14,8 @@ constexpr int64_t kMaxActivationBytes = 3758096384LL;   // 3.5 GiB: 32-bit buffe
 // moe_expert_offsets: tokens per workgroup (8 wavefronts of 64 tokens)
 constexpr int kOffsBlockTokens = 512;
 
-// grouped FFN: rows per row tile of the 64-row path (4 MFMA subtiles of 16 rows),
-// the smallest row tile of any path, and the K chunk per step
-constexpr int kFfnTileRows = 64;
+// grouped FFN: the smallest row tile of any path (16, 32, 64 or 128 rows are
+// used), and the K chunk per step
 constexpr int kFfnMinTileRows = 16;
 constexpr int kFfnKChunk = 128;
 // streaming path: LDS for the staged E8M0 scales of a workgroup (4 wavefronts x

@@ -157,7 +157,9 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
         row = static_cast<uint32_t>(p);
       }
     }
-    aoff[mi] = valid ? row * static_cast<uint32_t>(K) * 2u + 64u * g : kRsrcOutOfRange;
+    // lane group g starts at element 32g (128-element chunks) or 64g (256-element chunks)
+    aoff[mi] = valid ? row * static_cast<uint32_t>(K) * 2u + (kDeep ? 128u : 64u) * g
+                     : kRsrcOutOfRange;
   }
 
   // weight row of fragment f for a lane whose MFMA column is c16
@@ -172,20 +174,22 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
   const size_t e_rows = static_cast<size_t>(rt.expert) * n_rows;
   const uint8_t* bq[4];
 #pragma unroll
-  for (int f = 0; f < 4; ++f) bq[f] = wq + (e_rows + nrow[f]) * row_q + 16 * g;
+  for (int f = 0; f < 4; ++f) bq[f] = wq + (e_rows + nrow[f]) * row_q + (kDeep ? 0 : 16 * g);
 
   uint32_t* my_scales = scale_lds + (threadIdx.x >> 6) * (n_chunks * 64);
   if (kDeep) {
-    // lane L stages the scales of row (f = L/16, column L%16): the dword of chunk c
-    // (one byte per lane group) goes to my_scales[(c*16 + L%16)*4 + f]
+    // lane L stages the scales of row (f = L/16, column L%16).  The 8 scale bytes
+    // of a 256-element chunk c2 (2 per lane group) go to the two dwords
+    // my_scales[((c2*16 + L%16)*4 + f)*2 + {0,1}]
     const int f = lane >> 4;
     const uint8_t* srow = wsc + (e_rows + wrow(f, r16)) * row_s;
-    for (int c = 0; c < n_chunks; c += 4) {
+    for (int c = 0; c < n_chunks; c += 4) {   // c counts 128-element chunks
       const uint4 d = *reinterpret_cast<const uint4*>(srow + c * 4);
-      my_scales[((c + 0) * 16 + r16) * 4 + f] = d.x;
-      my_scales[((c + 1) * 16 + r16) * 4 + f] = d.y;
-      my_scales[((c + 2) * 16 + r16) * 4 + f] = d.z;
-      my_scales[((c + 3) * 16 + r16) * 4 + f] = d.w;
+      const int c2 = c / 2;
+      my_scales[(((c2 + 0) * 16 + r16) * 4 + f) * 2 + 0] = d.x;
+      my_scales[(((c2 + 0) * 16 + r16) * 4 + f) * 2 + 1] = d.y;
+      my_scales[(((c2 + 1) * 16 + r16) * 4 + f) * 2 + 0] = d.z;
+      my_scales[(((c2 + 1) * 16 + r16) * 4 + f) * 2 + 1] = d.w;
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -244,34 +248,72 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
   };
 
   if constexpr (kDeep) {
-    // n_chunks is a multiple of 4 (>= 4).  Ring: weights q0..q3, activations a0/a1.
-    uint4 q0[4], q1[4], q2[4], q3[4];
-    bf16x8 a0[MSUB][4], a1[MSUB][4];
-    uint32_t sc[4];
-    const int last = n_chunks - 1;
-    // prologue in steady-state order (..., activations of c, weights of c+2), so the
-    // loop header sees the same outstanding-load count from entry and back edge
-    load_w(q0, 0);
-    load_w(q1, 1);
+    // 256-element chunks: each lane takes 32 bytes (two scale blocks) of each of its
+    // four rows, so a row is visited 128 bytes at a time (about 20% more HBM
+    // throughput than 64-byte visits for this many concurrent rows).  Weights:
+    // two register stages (the next chunk streams in while this one computes).
+    // Activations: loaded for the current chunk, issued before the weight
+    // prefetch, so waiting for them leaves the prefetch in flight.
+    const int n2 = n_chunks / 2;   // 256-element chunks (even: n_chunks % 4 == 0)
+    auto load_w2 = [&](uint4 (&q)[4][2], int c2) {
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        const uint8_t* src = bq[f] + c2 * 128 + 32 * g;   // lane group g: bytes 32g..32g+31
+        q[f][0] = *reinterpret_cast<const uint4*>(src);
+        q[f][1] = *reinterpret_cast<const uint4*>(src + 16);
+      }
+    };
+    auto load_a2 = [&](bf16x8 (&a)[MSUB][8], int c2) {
+#pragma unroll
+      for (int mi = 0; mi < MSUB; ++mi)
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+          a[mi][t] = __builtin_bit_cast(
+              bf16x8, __builtin_amdgcn_raw_buffer_load_b128(arsrc, aoff[mi] + c2 * 512 + 16 * t, 0, 0));
+    };
+    auto compute2 = [&](const uint4 (&q)[4][2], const bf16x8 (&a)[MSUB][8], int c2) {
+      const uint4 d0 = *reinterpret_cast<const uint4*>(my_scales + ((c2 * 16 + r16) * 4) * 2);
+      const uint4 d1 = *reinterpret_cast<const uint4*>(my_scales + ((c2 * 16 + r16) * 4) * 2 + 4);
+      const uint32_t sd[4][2] = {{d0.x, d0.y}, {d0.z, d0.w}, {d1.x, d1.y}, {d1.z, d1.w}};
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        float scl[4];
+#pragma unroll
+        for (int f = 0; f < 4; ++f)   // block 2g + j of the chunk: byte (2g+j)%4 of dword (2g+j)/4
+          scl[f] = e8m0_as_f32((sd[f][(2 * g + j) >> 2] >> (8 * ((2 * g + j) & 3))) & 0xFFu);
+        const uint32_t w[4][4] = {{q[0][j].x, q[0][j].y, q[0][j].z, q[0][j].w},
+                                  {q[1][j].x, q[1][j].y, q[1][j].z, q[1][j].w},
+                                  {q[2][j].x, q[2][j].y, q[2][j].z, q[2][j].w},
+                                  {q[3][j].x, q[3][j].y, q[3][j].z, q[3][j].w}};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+#pragma unroll
+          for (int f = 0; f < 4; ++f) {
+            const bf16x8 b = dequant8(w[f][s], scl[f]);
+#pragma unroll
+            for (int mi = 0; mi < MSUB; ++mi)
+              acc[mi][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mi][4 * j + s], b, acc[mi][f],
+                                                                   0, 0, 0);
+          }
+        }
+      }
+    };
+    uint4 q0[4][2], q1[4][2];
+    load_w2(q0, 0);
     __builtin_amdgcn_sched_barrier(0);
-    load_a(a0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    load_w(q2, 2);
-    __builtin_amdgcn_sched_barrier(0);
-    for (int kc = 0; kc < n_chunks; kc += 4) {
-#define MOE_STREAM_STEP(A_NEXT, KA, Q_NEXT, KQ, Q_CUR, A_CUR, KC) \
-  load_a(A_NEXT, KA);                                              \
-  __builtin_amdgcn_sched_barrier(0);                               \
-  load_w(Q_NEXT, KQ);                                              \
-  __builtin_amdgcn_sched_barrier(0);                               \
-  lds_s(sc, KC);                                                   \
-  compute(Q_CUR, sc, A_CUR);                                       \
-  __builtin_amdgcn_sched_barrier(0);
-      MOE_STREAM_STEP(a1, kc + 1, q3, kc + 3, q0, a0, kc)
-      MOE_STREAM_STEP(a0, kc + 2, q0, kc + 4 <= last ? kc + 4 : last, q1, a1, kc + 1)
-      MOE_STREAM_STEP(a1, kc + 3, q1, kc + 5 <= last ? kc + 5 : last, q2, a0, kc + 2)
-      MOE_STREAM_STEP(a0, kc + 4 <= last ? kc + 4 : last, q2, kc + 6 <= last ? kc + 6 : last, q3,
-                      a1, kc + 3)
+    for (int c2 = 0; c2 < n2; c2 += 2) {
+#define MOE_STREAM_STEP(Q_NEXT, KQ, Q_CUR, KC) \
+  {                                           \
+    bf16x8 a[MSUB][8];                        \
+    load_a2(a, KC);                           \
+    __builtin_amdgcn_sched_barrier(0);        \
+    load_w2(Q_NEXT, KQ);                      \
+    __builtin_amdgcn_sched_barrier(0);        \
+    compute2(Q_CUR, a, KC);                   \
+    __builtin_amdgcn_sched_barrier(0);        \
+  }
+      MOE_STREAM_STEP(q1, c2 + 1, q0, c2)
+      MOE_STREAM_STEP(q0, c2 + 2 < n2 ? c2 + 2 : n2 - 1, q1, c2 + 1)
 #undef MOE_STREAM_STEP
     }
   } else {
@@ -328,40 +370,67 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
 
 // ---------------------------------------------------------------- tiled GEMM (many rows)
 //
-// For row tiles of up to 64 rows (prefill-shaped batches).  A workgroup of four
-// wavefronts owns one 64-row tile and 256 weight rows; each wavefront has 64
-// weight rows (same split as the streaming kernel: W1 32 gate + 32 up rows, W2
-// 64 output rows) and all four 16-row MFMA subtiles, so each dequantised weight
-// fragment feeds four MFMAs.  The activation tile of each K chunk (64 rows x 128
-// bf16) is loaded once per workgroup into LDS (double-buffered; rows padded by
-// 16 bytes so that the 16 lanes of a read group hit distinct banks) and read by
-// all four wavefronts.  Weights go straight to registers, prefetched about one
-// and a half chunks ahead; scales are staged in LDS as in the streaming kernel.
+// For row tiles of 64 or 128 rows (prefill-shaped batches).  A workgroup of four
+// wavefronts owns one row tile and 256 weight rows; each wavefront has 64 weight
+// rows (same split as the streaming kernel: W1 32 gate + 32 up rows, W2 64 output
+// rows) and all 16-row MFMA subtiles of the tile (kMSub = 4 or 8), so each
+// dequantised weight fragment feeds kMSub MFMAs.  The activation tile of each K
+// chunk (kMSub*16 rows x 128 bf16) is loaded once per workgroup into LDS
+// (double-buffered; rows padded by 16 bytes so that the 16 lanes of a read group
+// hit distinct banks) and read by all four wavefronts.  Weights go straight to
+// registers, issued right after the chunk that frees their registers.  With 64-row
+// tiles the E8M0 scales are staged in LDS as in the streaming kernel; with
+// 128-row tiles the LDS holds only activations and the scales come with the
+// weights.
 //
-// Per chunk c: issue the activation loads of c+1, compute c (LDS activations,
-// register weights), issue the weight loads of c+2 into the registers c just
-// freed, store the activations of c+1 to the other LDS buffer, barrier.
-constexpr int kTileRows = 64;
+// Per chunk c: issue the activation loads of c+1 (128 rows) or c+2 (64 rows),
+// compute c, issue the weights of c+2, store the activations of c+1 to the other
+// LDS buffer, barrier.
+//
+// Workgroup order.  The hardware deals consecutive workgroups to the 8 XCDs in
+// turn, and each XCD has its own 4 MB L2.  Launch order (row tile major) gives
+// each XCD 2 of the 16 column blocks of every tile: a small weight slice per L2,
+// but every tile's activations fetched into all 8 L2s.  Measured alternatives:
+// whole tiles per XCD (each L2 then cycles an expert's full 8.9 MB W1) was 40%
+// slower; 4 column blocks x half the tiles per XCD is ~1% faster than launch
+// order and is what is used.
 constexpr int kARowBytes = kFfnKChunk * 2 + 16;   // 256 B of bf16 + 16 B pad
-constexpr int kABufBytes = kTileRows * kARowBytes;
+constexpr int kXcds = 8;
 
-template <bool kW1>
+template <int kMSub>
+constexpr int a_buf_bytes() { return kMSub * 16 * kARowBytes; }
+
+template <bool kW1, int kMSub>
 __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(
     const uint16_t* __restrict__ act, uint32_t act_bytes, const int32_t* __restrict__ gather,
     int k_top, int n_slots, const uint8_t* __restrict__ wq, const uint8_t* __restrict__ wsc,
     const RowTile* __restrict__ tiles, const int32_t* __restrict__ n_tiles, int K, int n_rows,
     int half, int waves_per_tile, int blocks_per_tile, float limit, int clamp,
     uint16_t* __restrict__ out, int ld_out) {
+  constexpr bool kLdsScales = kMSub == 4;
+  constexpr int kRows = kMSub * 16;
+  constexpr int kABuf = a_buf_bytes<kMSub>();
+  constexpr int kThreadsPerRow = 256 / kRows;          // 4 (64 rows) or 2 (128 rows)
+  constexpr int kPieces = kMSub;                       // 16-byte pieces per thread per chunk
   extern __shared__ __attribute__((aligned(16))) unsigned char tile_lds[];
-  const int tile_id = blockIdx.x / blocks_per_tile;
-  const int nb = blockIdx.x - tile_id * blocks_per_tile;
+
+  // work id: with 16 column blocks per tile, XCD x takes column blocks
+  // 4(x%4)..4(x%4)+3 of the row tiles of parity x/4 (its weight slice stays in its
+  // L2 while each tile's activations go to 4 XCDs, not 8); otherwise launch order
+  int work = blockIdx.x;
+  if (blocks_per_tile == 16) {
+    const int x = blockIdx.x % kXcds, l = blockIdx.x / kXcds;
+    work = ((l / 4) * 2 + x / 4) * 16 + (x % 4) * 4 + (l % 4);
+  }
+  const int tile_id = work / blocks_per_tile;
+  const int nb = work - tile_id * blocks_per_tile;
   if (tile_id >= *n_tiles) return;   // uniform over the workgroup
   const RowTile rt = tiles[tile_id];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r16 = lane & 15, g = lane >> 4;
   const int n_chunks = K / kFfnKChunk;
   const int rows = rt.p_end - rt.p_begin;
-  const int msub = (rows + 15) >> 4;   // 1..4 subtiles hold rows
+  const int msub = (rows + 15) >> 4;   // subtiles that hold rows
 
   // column group of this wavefront; a wavefront past the last group repeats the
   // last one (it still stages activations and meets every barrier) and stores nothing
@@ -369,9 +438,9 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(
   const bool store_cols = cg_raw < waves_per_tile;
   const int cg = store_cols ? cg_raw : waves_per_tile - 1;
 
-  // --- activation staging: thread -> (row ar, 64-byte quarter aq) of the chunk
+  // --- activation staging: thread -> (row ar, part aq) of the chunk
   const __amdgpu_buffer_rsrc_t arsrc = make_rsrc(act, act_bytes);
-  const int ar = tid >> 2, aq = tid & 3;
+  const int ar = tid / kThreadsPerRow, aq = tid % kThreadsPerRow;
   uint32_t aoff;
   {
     const int p = rt.p_begin + ar;
@@ -386,20 +455,20 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(
         row = static_cast<uint32_t>(p);
       }
     }
-    aoff = valid ? row * static_cast<uint32_t>(K) * 2u + 64u * aq : kRsrcOutOfRange;
+    aoff = valid ? row * static_cast<uint32_t>(K) * 2u + 16u * kPieces * aq : kRsrcOutOfRange;
   }
-  unsigned char* a_lds = tile_lds;                       // [2][64][kARowBytes]
-  const int a_store = ar * kARowBytes + aq * 64;
-  auto load_a = [&](uint4 (&ra)[4], int kc) {
+  unsigned char* a_lds = tile_lds;                       // [2][kRows][kARowBytes]
+  const int a_store = ar * kARowBytes + aq * 16 * kPieces;
+  auto load_a = [&](uint4 (&ra)[kPieces], int kc) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kPieces; ++i)
       ra[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                                             arsrc, aoff + kc * 256 + 16 * i, 0, 0));
   };
-  auto store_a = [&](const uint4 (&ra)[4], int buf) {
+  auto store_a = [&](const uint4 (&ra)[kPieces], int buf) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<uint4*>(a_lds + buf * kABufBytes + a_store + 16 * i) = ra[i];
+    for (int i = 0; i < kPieces; ++i)
+      *reinterpret_cast<uint4*>(a_lds + buf * kABuf + a_store + 16 * i) = ra[i];
   };
 
   // --- weights: four fragments of 16 rows, this lane's row in each
@@ -412,17 +481,25 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(
   const size_t row_q = static_cast<size_t>(K / 2), row_s = static_cast<size_t>(K / 32);
   const size_t e_rows = static_cast<size_t>(rt.expert) * n_rows;
   const uint8_t* bq[4];
+  const uint32_t* bs[4];   // scale dword of (row, chunk): one byte per lane group
 #pragma unroll
-  for (int f = 0; f < 4; ++f) bq[f] = wq + (e_rows + nrow[f]) * row_q + 16 * g;
-  auto load_w = [&](uint4 (&q)[4], int kc) {
+  for (int f = 0; f < 4; ++f) {
+    bq[f] = wq + (e_rows + nrow[f]) * row_q + 16 * g;
+    bs[f] = reinterpret_cast<const uint32_t*>(wsc + (e_rows + nrow[f]) * row_s);
+  }
+  auto load_w = [&](uint4 (&q)[4], uint32_t (&sd)[4], int kc) {
 #pragma unroll
     for (int f = 0; f < 4; ++f) q[f] = *reinterpret_cast<const uint4*>(bq[f] + kc * 64);
+    if constexpr (!kLdsScales) {
+#pragma unroll
+      for (int f = 0; f < 4; ++f) sd[f] = bs[f][kc];
+    }
   };
 
-  // --- scales of the wavefront's 64 rows, staged as [chunk][16][4] dwords
+  // --- 64-row tiles: scales of the wavefront's 64 rows, staged as [chunk][16][4] dwords
   uint32_t* my_scales =
-      reinterpret_cast<uint32_t*>(tile_lds + 2 * kABufBytes) + wave * (n_chunks * 64);
-  {
+      reinterpret_cast<uint32_t*>(tile_lds + 2 * kABuf) + wave * (n_chunks * 64);
+  if constexpr (kLdsScales) {
     const int f = lane >> 4;
     const uint8_t* srow = wsc + (e_rows + wrow(f, r16)) * row_s;
     int c = 0;
@@ -436,78 +513,100 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(
     for (; c < n_chunks; ++c)
       my_scales[(c * 16 + r16) * 4 + f] = *reinterpret_cast<const uint32_t*>(srow + c * 4);
   }
-  auto lds_s = [&](uint32_t (&sc)[4], int kc) {
-    const uint4 d = *reinterpret_cast<const uint4*>(my_scales + (kc * 16 + r16) * 4);
-    const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
-#pragma unroll
-    for (int f = 0; f < 4; ++f) sc[f] = (dw[f] >> (8 * g)) & 0xFFu;
-  };
 
-  floatx4 acc[4][4];
+  floatx4 acc[kMSub][4];
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+  for (int mi = 0; mi < kMSub; ++mi)
 #pragma unroll
     for (int f = 0; f < 4; ++f) acc[mi][f] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // one chunk: A from LDS buffer `buf`, weights in q
-  auto compute = [&](const uint4 (&q)[4], int kc, int buf) {
-    uint32_t sc[4];
-    lds_s(sc, kc);
+  // one chunk: activations from LDS buffer `buf`, weights in q, scale dwords in sd
+  auto compute = [&](const uint4 (&q)[4], const uint32_t (&sd)[4], int kc, int buf) {
+    uint32_t dw[4];
+    if constexpr (kLdsScales) {
+      const uint4 d = *reinterpret_cast<const uint4*>(my_scales + (kc * 16 + r16) * 4);
+      dw[0] = d.x; dw[1] = d.y; dw[2] = d.z; dw[3] = d.w;
+    } else {
+#pragma unroll
+      for (int f = 0; f < 4; ++f) dw[f] = sd[f];
+    }
     float scl[4];
 #pragma unroll
-    for (int f = 0; f < 4; ++f) scl[f] = e8m0_as_f32(sc[f]);
+    for (int f = 0; f < 4; ++f) scl[f] = e8m0_as_f32((dw[f] >> (8 * g)) & 0xFFu);
     const uint32_t w[4][4] = {{q[0].x, q[0].y, q[0].z, q[0].w},
                               {q[1].x, q[1].y, q[1].z, q[1].w},
                               {q[2].x, q[2].y, q[2].z, q[2].w},
                               {q[3].x, q[3].y, q[3].z, q[3].w}};
-    const unsigned char* abase = a_lds + buf * kABufBytes + r16 * kARowBytes + 64 * g;
+    const unsigned char* abase = a_lds + buf * kABuf + r16 * kARowBytes + 64 * g;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       bf16x8 b[4];
 #pragma unroll
       for (int f = 0; f < 4; ++f) b[f] = dequant8(w[f][s], scl[f]);
+      // every subtile, also those past the tile's rows (they hold zeros): a branch
+      // here would cut the MFMA stream into blocks that each wait on one LDS read
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi) {
-        if (mi < msub) {   // uniform
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(abase + mi * 16 * kARowBytes + 16 * s);
+      for (int mi = 0; mi < kMSub; ++mi) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(abase + mi * 16 * kARowBytes + 16 * s);
 #pragma unroll
-          for (int f = 0; f < 4; ++f)
-            acc[mi][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[f], acc[mi][f], 0, 0, 0);
-        }
+        for (int f = 0; f < 4; ++f)
+          acc[mi][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[f], acc[mi][f], 0, 0, 0);
       }
     }
   };
 
-  // prologue: chunk 0 activations into buffer 0, weights of chunks 0 and 1
-  uint4 ra[4], q0[4], q1[4];
-  load_a(ra, 0);
-  load_w(q0, 0);
-  load_w(q1, n_chunks > 1 ? 1 : 0);
-  store_a(ra, 0);
-  __syncthreads();
-
   const int last = n_chunks - 1;
+  uint4 q0[4], q1[4];
+  uint32_t s0[4], s1[4];
   int kc = 0;
-  for (; kc + 2 <= n_chunks; kc += 2) {
-    // chunk kc (buffer 0, weights q0)
-    load_a(ra, kc + 1);
-    compute(q0, kc, 0);
-    load_w(q0, kc + 2 <= last ? kc + 2 : last);
-    store_a(ra, 1);
+  if constexpr (kMSub == 4) {
+    // activations two chunks ahead in registers (ra0/ra1), one chunk ahead in LDS
+    uint4 ra0[kPieces], ra1[kPieces];
+    load_a(ra0, 0);
+    load_w(q0, s0, 0);
+    load_w(q1, s1, last >= 1 ? 1 : 0);
+    load_a(ra1, last >= 1 ? 1 : 0);
+    store_a(ra0, 0);
     __syncthreads();
-    // chunk kc+1 (buffer 1, weights q1)
-    load_a(ra, kc + 2 <= last ? kc + 2 : last);
-    compute(q1, kc + 1, 1);
-    load_w(q1, kc + 3 <= last ? kc + 3 : last);
+    for (; kc + 2 <= n_chunks; kc += 2) {
+      load_a(ra0, kc + 2 <= last ? kc + 2 : last);
+      compute(q0, s0, kc, 0);
+      load_w(q0, s0, kc + 2 <= last ? kc + 2 : last);
+      store_a(ra1, 1);
+      __syncthreads();
+      load_a(ra1, kc + 3 <= last ? kc + 3 : last);
+      compute(q1, s1, kc + 1, 1);
+      load_w(q1, s1, kc + 3 <= last ? kc + 3 : last);
+      store_a(ra0, 0);
+      __syncthreads();
+    }
+  } else {
+    // activations one chunk ahead (registers ra, then LDS)
+    uint4 ra[kPieces];
+    load_a(ra, 0);
+    load_w(q0, s0, 0);
+    load_w(q1, s1, last >= 1 ? 1 : 0);
     store_a(ra, 0);
     __syncthreads();
+    for (; kc + 2 <= n_chunks; kc += 2) {
+      load_a(ra, kc + 1);
+      compute(q0, s0, kc, 0);
+      load_w(q0, s0, kc + 2 <= last ? kc + 2 : last);
+      store_a(ra, 1);
+      __syncthreads();
+      load_a(ra, kc + 2 <= last ? kc + 2 : last);
+      compute(q1, s1, kc + 1, 1);
+      load_w(q1, s1, kc + 3 <= last ? kc + 3 : last);
+      store_a(ra, 0);
+      __syncthreads();
+    }
   }
-  if (kc < n_chunks) compute(q0, kc, 0);   // odd chunk count: last chunk in buffer 0 / q0
+  if (kc < n_chunks) compute(q0, s0, kc, 0);   // odd chunk count: last chunk in buffer 0 / q0
 
   if (!store_cols) return;
   const bool do_clamp = clamp != 0;
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi) {
+  for (int mi = 0; mi < kMSub; ++mi) {
     if (mi >= msub) continue;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -525,16 +624,18 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(
   }
 }
 
-template <bool kW1>
+template <bool kW1, int kMSub>
 hipError_t launch_tile(int64_t tile_bound, hipStream_t stream, const uint16_t* act,
                        uint32_t act_bytes, const int32_t* gather, int k_top, int n_slots,
                        const uint8_t* wq, const uint8_t* wsc, const RowTile* tiles,
                        const int32_t* n_tiles, int K, int n_rows, int half, int wpt, float limit,
                        int clamp, uint16_t* out, int ld_out) {
   const int bpt = (wpt + 3) / 4;
-  const size_t lds = 2 * static_cast<size_t>(kABufBytes) +
-                     static_cast<size_t>(4) * (K / kFfnKChunk) * 64 * sizeof(uint32_t);
-  gemm_tile_kernel<kW1><<<static_cast<unsigned>(tile_bound * bpt), 256, lds, stream>>>(
+  size_t lds = 2 * static_cast<size_t>(a_buf_bytes<kMSub>());
+  if (kMSub == 4) lds += static_cast<size_t>(4) * (K / kFfnKChunk) * 64 * sizeof(uint32_t);
+  // the column-block/XCD split covers row tiles in pairs: round up to whole pairs
+  const int64_t blocks = bpt == 16 ? (tile_bound + 1) / 2 * 2 * bpt : tile_bound * bpt;
+  gemm_tile_kernel<kW1, kMSub><<<static_cast<unsigned>(blocks), 256, lds, stream>>>(
       act, act_bytes, gather, k_top, n_slots, wq, wsc, tiles, n_tiles, K, n_rows, half, wpt, bpt,
       limit, clamp, out, ld_out);
   return hipGetLastError();
@@ -587,7 +688,7 @@ hipError_t launch_ffn(const uint16_t* x, int64_t T, int H, int I, int E, int k,
   else if (avg_rows <= 24)
     tile_rows = 32;
   else
-    tile_rows = kFfnTileRows;
+    tile_rows = 64;
   const int64_t tile_bound = ffn_tile_bound(n_slots, E, tile_rows);
 
   plan_kernel<<<1, 1024, 0, stream>>>(counts, offsets, E, tile_rows, n_slots, tile_bound, n_tiles,
@@ -620,15 +721,15 @@ hipError_t launch_ffn(const uint16_t* x, int64_t T, int H, int I, int E, int k,
                                         tiles, n_tiles, I, H, 0, wpt2, limit, 0, y_sorted, H);
   } else {
     const int wpt1 = I / 32, wpt2 = H / 64;
-    err = launch_tile<true>(tile_bound, stream, x, x_bytes, gather, k, slots_i, w1, w1s, tiles,
-                            n_tiles, H, 2 * I, I, wpt1, limit, clamp_i, h, I);
+    err = launch_tile<true, 4>(tile_bound, stream, x, x_bytes, gather, k, slots_i, w1, w1s, tiles,
+                               n_tiles, H, 2 * I, I, wpt1, limit, clamp_i, h, I);
     if (err != hipSuccess) return err;
     if (events) {
       err = hipEventRecord(events[1], stream);
       if (err != hipSuccess) return err;
     }
-    err = launch_tile<false>(tile_bound, stream, h, h_bytes, nullptr, k, slots_i, w2, w2s, tiles,
-                             n_tiles, I, H, 0, wpt2, limit, 0, y_sorted, H);
+    err = launch_tile<false, 4>(tile_bound, stream, h, h_bytes, nullptr, k, slots_i, w2, w2s,
+                                tiles, n_tiles, I, H, 0, wpt2, limit, 0, y_sorted, H);
   }
   if (err != hipSuccess || !events) return err;
   return hipEventRecord(events[2], stream);
