@@ -116,6 +116,9 @@ def main():
     ap.add_argument("--weight-copies", type=int, default=2)
     ap.add_argument("--cpu-tokens", type=int, default=4,
                     help="tokens in the CPU oracle sample (0: skip)")
+    ap.add_argument("--separate-routing", action="store_true",
+                    help="route with moe_route + moe_build_bitmatrix + moe_expert_offsets instead "
+                         "of the fused moe_route_and_group (same outputs)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="instead of the layer, run a plain device-to-device copy of this many "
                          "MiB (--steps times): the reference for HBM traffic counters")
@@ -155,74 +158,107 @@ def main():
     hip = HipEvents()
     n_ev = 8
     events = hip.create(n_ev * args.steps)
-    ev_arr = (ctypes.c_void_p * 3)()
 
-    def step(i, evs=None):
-        d = copies[i % len(copies)]
+    # Arguments are marshalled once per weight copy, so the timed loop makes only bare
+    # ctypes calls (a slower host loop would leave the GPU idle between launches).
+    from ctypes import c_void_p as P, c_int64 as I64, c_int32 as I32, c_size_t as SZ, c_float as F
+    for name, argt in (("moe_route", [P, I64, I32, I32, P, P, P]),
+                       ("moe_build_bitmatrix", [P, I64, I32, I32, P, P]),
+                       ("moe_expert_offsets", [P, P, I64, I32, I32, P, P, P, P, P, SZ, P]),
+                       ("moe_route_and_group", [P, I64, I32, I32] + [P] * 8 + [SZ, P]),
+                       ("moe_grouped_ffn_mxfp4_timed", [P, I64, I32, I32, I32, I32] + [P] * 7 +
+                        [F, P, P, SZ, P, P]),
+                       ("moe_combine", [P, P, P, I64, I32, I32, P, P])):
+        getattr(lib, name).argtypes = argt
+        getattr(lib, name).restype = ctypes.c_int
+    ptr = lambda t: P(t.data_ptr())
+    ev_arrs = [(ctypes.c_void_p * 3)(*events[i * n_ev + 4:i * n_ev + 7]) for i in range(args.steps)]
+    ev_null = (ctypes.c_void_p * 3)(*hip.create(3))
+    S = P(sh)
+    calls = []
+    for d in copies:
+        calls.append(dict(
+            route=(ptr(d["logits"]), T, E, k, ptr(b.topk_ids), ptr(b.topk_weights), S),
+            bitmatrix=(ptr(b.topk_ids), T, E, k, ptr(b.bitmatrix), S),
+            offsets=(ptr(b.bitmatrix), ptr(b.topk_ids), T, E, k, ptr(b.counts), ptr(b.offsets),
+                     ptr(b.gather), ptr(b.scatter), ptr(b.ws), b.ws.numel(), S),
+            front=(ptr(d["logits"]), T, E, k, ptr(b.topk_ids), ptr(b.topk_weights),
+                   ptr(b.bitmatrix), ptr(b.counts), ptr(b.offsets), ptr(b.gather),
+                   ptr(b.scatter), ptr(b.ws), b.ws.numel(), S),
+            ffn=(ptr(d["x"]), T, H, I, E, k, ptr(d["w1"]), ptr(d["w1_s"]), ptr(d["w2"]),
+                 ptr(d["w2_s"]), ptr(b.counts), ptr(b.offsets), ptr(b.gather), F(args.limit),
+                 ptr(b.y_sorted), ptr(b.ws), b.ws.numel()),
+            combine=(ptr(b.y_sorted), ptr(b.topk_weights), ptr(b.scatter), T, H, k, ptr(b.y), S)))
+    record = hip.rt.hipEventRecord
+    f_route, f_bm, f_offs = lib.moe_route, lib.moe_build_bitmatrix, lib.moe_expert_offsets
+    f_front, f_ffn, f_comb = lib.moe_route_and_group, lib.moe_grouped_ffn_mxfp4_timed, lib.moe_combine
+
+    def check(rc, name):
+        if rc != 0:
+            raise binding.MoeError(name, rc)
+
+    def step(i, evs=None, ffn_events=None):
+        """One layer.  evs: 8 events around every call (breakdown pass only);
+        ffn_events: the 3 events inside the FFN call (timed pass)."""
+        c = calls[i % len(calls)]
         if evs is not None:
-            hip.record(evs[0], sh)
-        binding.moe_route(d["logits"], k, b.topk_ids, b.topk_weights, stream)
-        if evs is not None:
-            hip.record(evs[1], sh)
-        binding.moe_build_bitmatrix(b.topk_ids, E, b.bitmatrix, stream)
-        if evs is not None:
-            hip.record(evs[2], sh)
-        binding.moe_expert_offsets(b.bitmatrix, b.topk_ids, E, b.counts, b.offsets, b.gather,
-                                   b.scatter, b.ws, stream)
-        if evs is None:
-            binding.moe_grouped_ffn_mxfp4(d["x"], k, d["w1"], d["w1_s"], d["w2"], d["w2_s"],
-                                          b.counts, b.offsets, b.gather, args.limit, b.y_sorted,
-                                          b.ws, stream)
+            record(evs[0], S)
+        if args.separate_routing:
+            check(f_route(*c["route"]), "moe_route")
+            if evs is not None:
+                record(evs[1], S)
+            check(f_bm(*c["bitmatrix"]), "moe_build_bitmatrix")
+            if evs is not None:
+                record(evs[2], S)
+            check(f_offs(*c["offsets"]), "moe_expert_offsets")
         else:
-            hip.record(evs[3], sh)
-            ev_arr[0], ev_arr[1], ev_arr[2] = evs[4], evs[5], evs[6]
-            rc = lib.moe_grouped_ffn_mxfp4_timed(
-                ctypes.c_void_p(d["x"].data_ptr()), T, H, I, E, k, ctypes.c_void_p(d["w1"].data_ptr()),
-                ctypes.c_void_p(d["w1_s"].data_ptr()), ctypes.c_void_p(d["w2"].data_ptr()),
-                ctypes.c_void_p(d["w2_s"].data_ptr()), ctypes.c_void_p(b.counts.data_ptr()),
-                ctypes.c_void_p(b.offsets.data_ptr()), ctypes.c_void_p(b.gather.data_ptr()),
-                ctypes.c_float(args.limit), ctypes.c_void_p(b.y_sorted.data_ptr()),
-                ctypes.c_void_p(b.ws.data_ptr()), ctypes.c_size_t(b.ws.numel()), ev_arr,
-                ctypes.c_void_p(sh))
-            if rc != 0:
-                raise binding.MoeError("moe_grouped_ffn_mxfp4_timed", rc)
-        binding.moe_combine(b.y_sorted, b.topk_weights, b.scatter, b.y, stream)
+            check(f_front(*c["front"]), "moe_route_and_group")
+            if evs is not None:
+                record(evs[1], S)
+                record(evs[2], S)
         if evs is not None:
-            hip.record(evs[7], sh)
-
-    lib.moe_grouped_ffn_mxfp4_timed.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
-                                                ctypes.c_int32, ctypes.c_int32, ctypes.c_int32] + \
-        [ctypes.c_void_p] * 7 + [ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
-                                 ctypes.c_void_p, ctypes.c_void_p]
-    lib.moe_grouped_ffn_mxfp4_timed.restype = ctypes.c_int
+            record(evs[3], S)
+        check(f_ffn(*c["ffn"], ffn_events, S), "moe_grouped_ffn_mxfp4_timed")
+        check(f_comb(*c["combine"]), "moe_combine")
+        if evs is not None:
+            record(evs[7], S)
 
     print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
     for i in range(args.warmup):
-        step(i)
+        step(i, ffn_events=ev_null)
     torch.cuda.synchronize()
+
+    # Timed region: K steps; only the three events of the instrumented FFN call
+    # (plan | W1 | W2) are recorded inside it, on the library's stream.
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    ffn_ev = [(ctypes.c_void_p * 3)(*hip.create(3)) for _ in range(args.steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, events[i * n_ev:(i + 1) * n_ev])
+        step(i, ffn_events=ffn_ev[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    w1_ms = float(np.mean([hip.ms(e[0], e[1]) for e in ffn_ev]))
+    w2_ms = float(np.mean([hip.ms(e[1], e[2]) for e in ffn_ev]))
 
-    # per-call and per-kernel durations (ms), averaged over the timed steps
+    # Breakdown pass (not timed as a whole): events around every call.
+    n_bd = min(args.steps, 20)
+    for i in range(n_bd):
+        step(i, events[i * n_ev:(i + 1) * n_ev], ev_arrs[i])
+    torch.cuda.synchronize()
     names = ["route", "bitmatrix", "offsets", "ffn_plan", "ffn_w1", "ffn_w2", "combine"]
-    per = np.zeros((args.steps, len(names)))
-    for i in range(args.steps):
+    if not args.separate_routing:   # one call for the three routing steps
+        names[0:3] = ["route_and_group", "-", "-"]
+    per = np.zeros((n_bd, len(names)))
+    for i in range(n_bd):
         ev = events[i * n_ev:(i + 1) * n_ev]
         per[i] = [hip.ms(ev[j], ev[j + 1]) for j in range(7)]
     avg_ms = per.mean(axis=0)
-    layer_ms_events = float(np.mean([hip.ms(events[i * n_ev], events[i * n_ev + 7])
-                                     for i in range(args.steps)]))
 
     counts = b.counts.cpu().numpy()
     touched = int((counts > 0).sum())
     w1_bytes_per_expert = 2 * I * H // 2 + 2 * I * H // 32
     w2_bytes_per_expert = H * I // 2 + H * I // 32
     w1_alg = touched * w1_bytes_per_expert + T * H * 2
-    w1_ms = float(avg_ms[names.index("ffn_w1")])
     achieved = w1_alg / (w1_ms * 1e-3) / 1e9
     layer_alg = touched * (w1_bytes_per_expert + w2_bytes_per_expert) + 2 * T * H * 2 + T * E * 4
     ms_per_step = elapsed * 1e3 / args.steps
@@ -245,9 +281,12 @@ def main():
         "config": {"workload": f"{wl.name}: T={T} E={E} k={k} H={H} I={I}, MXFP4 experts, "
                                f"seed {wl.index}",
                    "T": T, "E": E, "k": k, "H": H, "I": I, "swiglu_limit": args.limit,
-                   "weight_copies": args.weight_copies, "parallelism": "single GPU"},
-        "per_call_us": {n: float(v) * 1e3 for n, v in zip(names, avg_ms)},
-        "layer_us_events": layer_ms_events * 1e3,
+                   "weight_copies": args.weight_copies, "parallelism": "single GPU",
+                   "routing": "separate calls" if args.separate_routing else "moe_route_and_group"},
+        "per_call_us": {n: float(v) * 1e3 for n, v in zip(names, avg_ms) if n != "-"},
+        "per_call_note": "separate pass with events around every call (events add a few us each)",
+        "ffn_w1_us_timed": w1_ms * 1e3,
+        "ffn_w2_us_timed": w2_ms * 1e3,
         "touched_experts": touched,
         "roofline": {"bound": "hbm", "kernel": "gemm_kernel<true> (W1 gate|up + SwiGLU)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -258,7 +297,7 @@ def main():
                      "algorithmic_bytes_per_launch": w1_alg},
         "layer_hbm_frac": layer_alg / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "ffn_hbm_frac": (touched * (w1_bytes_per_expert + w2_bytes_per_expert))
-                        / (float(avg_ms[3:6].sum()) * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                        / ((w1_ms + w2_ms) * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "layer_mfma_frac_bf16": flops / (ms_per_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
     }
     if args.cpu_tokens > 0:

@@ -13,6 +13,7 @@
  *   moe_expert_offsets     -> counts, offsets, gather, scatter
  *   moe_grouped_ffn_mxfp4  -> y_sorted   (W1 gate|up, clamped SwiGLU, W2)
  *   moe_combine            -> y
+ * moe_route_and_group runs the first three as one call (one launch for small T).
  *
  * Conventions shared by every call
  *   - Every pointer argument is a DEVICE pointer (memory the GPU can read or
@@ -174,6 +175,21 @@ moe_status moe_grouped_ffn_mxfp4(const uint16_t* x, int64_t T, int32_t H, int32_
 moe_status moe_combine(const uint16_t* y_sorted, const float* topk_weights,
                        const int32_t* scatter, int64_t T, int32_t H, int32_t k, uint16_t* y,
                        void* stream);
+
+/*
+ * moe_route_and_group -- the routing front-end in one call: exactly the outputs of
+ * moe_route, moe_build_bitmatrix and moe_expert_offsets on the same arguments
+ * (see those calls for each output's definition, layout and citation).
+ *
+ * For T <= 64 the three steps run as one kernel launch (one workgroup; the
+ * bit matrix is built in LDS under the same logical-block mask); for larger T
+ * the three kernels of the separate calls run back to back.  ws is the
+ * workspace of moe_expert_offsets.  T = 0 writes zeros to counts and offsets.
+ */
+moe_status moe_route_and_group(const float* logits, int64_t T, int32_t E, int32_t k,
+                               int32_t* topk_ids, float* topk_weights, uint32_t* bitmatrix,
+                               int32_t* counts, int32_t* offsets, int32_t* gather,
+                               int32_t* scatter, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Workspace bytes that moe_expert_offsets and moe_grouped_ffn_mxfp4 need for

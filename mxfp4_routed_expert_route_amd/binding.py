@@ -20,8 +20,8 @@ LIB_PATH = os.path.join(_PKG, "libmoe_mxfp4.so")
 STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPORTED",
           3: "MOE_ERR_MISALIGNED", 4: "MOE_ERR_WORKSPACE_TOO_SMALL", 5: "MOE_ERR_HIP"}
 
-EXPORTS = ("moe_route", "moe_build_bitmatrix", "moe_expert_offsets", "moe_grouped_ffn_mxfp4",
-           "moe_combine", "moe_workspace_bytes", "moe_status_string")
+EXPORTS = ("moe_route", "moe_build_bitmatrix", "moe_expert_offsets", "moe_route_and_group",
+           "moe_grouped_ffn_mxfp4", "moe_combine", "moe_workspace_bytes", "moe_status_string")
 
 
 # bf16 buffers may be given as bfloat16 tensors or as int16 tensors of bit patterns
@@ -43,6 +43,8 @@ _SIG = {
     "moe_route": [_P, _I64, _I32, _I32, _P, _P, _P],
     "moe_build_bitmatrix": [_P, _I64, _I32, _I32, _P, _P],
     "moe_expert_offsets": [_P, _P, _I64, _I32, _I32, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "moe_route_and_group": [_P, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
+                            _P],
     "moe_grouped_ffn_mxfp4": [_P, _I64, _I32, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P,
                               ctypes.c_float, _P, _P, ctypes.c_size_t, _P],
     "moe_combine": [_P, _P, _P, _I64, _I32, _I32, _P, _P],
@@ -122,6 +124,17 @@ def moe_expert_offsets(bitmatrix, topk_ids, E: int, counts, offsets, gather, sca
     T, k = topk_ids.shape
     _check("moe_expert_offsets", load().moe_expert_offsets(
         _ptr(bitmatrix, torch.int32, "bitmatrix"), _ptr(topk_ids, torch.int32, "topk_ids"), T, E, k,
+        _ptr(counts, torch.int32, "counts"), _ptr(offsets, torch.int32, "offsets"),
+        _ptr(gather, torch.int32, "gather"), _ptr(scatter, torch.int32, "scatter"),
+        _ptr(ws, torch.uint8, "ws"), ws.numel() if ws is not None else 0, _stream(stream)))
+
+
+def moe_route_and_group(logits, k: int, topk_ids, topk_weights, bitmatrix, counts, offsets,
+                        gather, scatter, ws, stream=None):
+    T, E = logits.shape
+    _check("moe_route_and_group", load().moe_route_and_group(
+        _ptr(logits, torch.float32, "logits"), T, E, k, _ptr(topk_ids, torch.int32, "topk_ids"),
+        _ptr(topk_weights, torch.float32, "topk_weights"), _ptr(bitmatrix, torch.int32, "bitmatrix"),
         _ptr(counts, torch.int32, "counts"), _ptr(offsets, torch.int32, "offsets"),
         _ptr(gather, torch.int32, "gather"), _ptr(scatter, torch.int32, "scatter"),
         _ptr(ws, torch.uint8, "ws"), ws.numel() if ws is not None else 0, _stream(stream)))

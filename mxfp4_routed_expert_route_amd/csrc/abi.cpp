@@ -40,6 +40,25 @@ moe_status moe_expert_offsets(const uint32_t* bitmatrix, const int32_t* topk_ids
                                       scatter, ws, as_stream(stream)));
 }
 
+moe_status moe_route_and_group(const float* logits, int64_t T, int32_t E, int32_t k,
+                               int32_t* topk_ids, float* topk_weights, uint32_t* bitmatrix,
+                               int32_t* counts, int32_t* offsets, int32_t* gather,
+                               int32_t* scatter, void* ws, size_t ws_bytes, void* stream) {
+  moe_status s = moe::check_route(logits, T, E, k, topk_ids, topk_weights);
+  if (s != MOE_OK) return s;
+  s = moe::check_bitmatrix(topk_ids, T, E, k, bitmatrix);
+  if (s != MOE_OK) return s;
+  s = moe::check_offsets(bitmatrix, topk_ids, T, E, k, counts, offsets, gather, scatter, ws,
+                         ws_bytes);
+  if (s != MOE_OK) return s;
+  if (T == 0)
+    return from_hip(moe::launch_offsets(nullptr, nullptr, 0, E, k, counts, offsets, nullptr,
+                                        nullptr, nullptr, as_stream(stream)));
+  return from_hip(moe::launch_route_and_group(logits, T, E, k, topk_ids, topk_weights, bitmatrix,
+                                              counts, offsets, gather, scatter, ws,
+                                              as_stream(stream)));
+}
+
 moe_status moe_grouped_ffn_mxfp4(const uint16_t* x, int64_t T, int32_t H, int32_t I, int32_t E,
                                  int32_t k, const uint8_t* w1, const uint8_t* w1_scale,
                                  const uint8_t* w2, const uint8_t* w2_scale,

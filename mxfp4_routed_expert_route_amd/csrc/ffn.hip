@@ -704,21 +704,26 @@ hipError_t launch_ffn(const uint16_t* x, int64_t T, int H, int I, int E, int k,
     const int wpt1 = I / 32, wpt2 = H / 64;
     const unsigned g1 = static_cast<unsigned>((tile_bound * wpt1 + 3) / 4);
     const unsigned g2 = static_cast<unsigned>((tile_bound * wpt2 + 3) / 4);
+    const RowTile* t = tiles;
     err = tile_rows == 16
-              ? launch_stream<true, 1>(g1, stream, x, x_bytes, gather, k, slots_i, w1, w1s, tiles,
-                                       n_tiles, H, 2 * I, I, wpt1, limit, clamp_i, h, I)
-              : launch_stream<true, 2>(g1, stream, x, x_bytes, gather, k, slots_i, w1, w1s, tiles,
-                                       n_tiles, H, 2 * I, I, wpt1, limit, clamp_i, h, I);
+              ? launch_stream<true, 1>(g1, stream, x, x_bytes, gather, k, slots_i, w1, w1s, t,
+                                       n_tiles, H, 2 * I, I, wpt1, limit,
+                                       clamp_i, h, I)
+              : launch_stream<true, 2>(g1, stream, x, x_bytes, gather, k, slots_i, w1, w1s, t,
+                                       n_tiles, H, 2 * I, I, wpt1, limit,
+                                       clamp_i, h, I);
     if (err != hipSuccess) return err;
     if (events) {
       err = hipEventRecord(events[1], stream);
       if (err != hipSuccess) return err;
     }
     err = tile_rows == 16
-              ? launch_stream<false, 1>(g2, stream, h, h_bytes, nullptr, k, slots_i, w2, w2s,
-                                        tiles, n_tiles, I, H, 0, wpt2, limit, 0, y_sorted, H)
-              : launch_stream<false, 2>(g2, stream, h, h_bytes, nullptr, k, slots_i, w2, w2s,
-                                        tiles, n_tiles, I, H, 0, wpt2, limit, 0, y_sorted, H);
+              ? launch_stream<false, 1>(g2, stream, h, h_bytes, nullptr, k, slots_i, w2, w2s, t,
+                                        n_tiles, I, H, 0, wpt2, limit, 0,
+                                        y_sorted, H)
+              : launch_stream<false, 2>(g2, stream, h, h_bytes, nullptr, k, slots_i, w2, w2s, t,
+                                        n_tiles, I, H, 0, wpt2, limit, 0,
+                                        y_sorted, H);
   } else {
     const int wpt1 = I / 32, wpt2 = H / 64;
     err = launch_tile<true, 4>(tile_bound, stream, x, x_bytes, gather, k, slots_i, w1, w1s, tiles,

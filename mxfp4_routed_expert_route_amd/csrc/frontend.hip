@@ -1,0 +1,143 @@
+// The routing front-end in one launch for small batches: top-k routing, the
+// token x expert bit matrix and the expert offsets / permutations, with exactly
+// the outputs of moe_route, moe_build_bitmatrix and moe_expert_offsets.
+//
+// One workgroup of 16 wavefronts, for T <= 64 tokens:
+//   1. wavefront w routes tokens w, w+16, w+32, w+48 (route_token);
+//   2. the bit matrix is built in LDS: thread i owns entry i = t*k + j; the logical
+//      block is the T*k entries, and threads past it (padding) stay inactive
+//      (txtmix.com article, §3; aihot.vn README translation, "Định tuyến MXFP4");
+//   3. wavefront 0 (lane = token) takes the expert column masks of the T rows,
+//      scans their popcounts into counts and offsets, and writes each slot's row
+//      p = offsets[e] + rank of the token within e.
+// Larger batches run the three separate kernels.
+#include "config.h"
+#include "launch.h"
+#include "routing_core.h"
+
+namespace moe {
+namespace {
+
+constexpr int kFrontMaxTokens = 64;
+
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int EPL>
+__global__ __launch_bounds__(1024) void frontend_small_kernel(
+    const float* __restrict__ logits, int T, int E, int k, int words, int32_t* __restrict__ ids,
+    float* __restrict__ weights, uint32_t* __restrict__ bm, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ gather, int32_t* __restrict__ scatter) {
+  __shared__ int ids_lds[kFrontMaxTokens * kMaxK];
+  __shared__ uint32_t rows_lds[kFrontMaxTokens * (kMaxE / 32)];
+  __shared__ uint64_t masks[kMaxE];
+  __shared__ int off_lds[kMaxE];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n_waves = blockDim.x >> 6;
+
+  // 1. routing
+  for (int t = wave; t < T; t += n_waves) {
+    int id;
+    float w;
+    route_token<EPL>(logits + static_cast<int64_t>(t) * E, E, k, lane, id, w);
+    if (lane < k) {
+      ids[t * k + lane] = id;
+      weights[t * k + lane] = w;
+      ids_lds[t * k + lane] = id;
+    }
+  }
+  for (int i = threadIdx.x; i < T * words; i += blockDim.x) rows_lds[i] = 0u;
+  __syncthreads();
+
+  // 2. bit matrix: entries past T*k are padding lanes of the logical block
+  const int n_entries = T * k;
+  if (static_cast<int>(threadIdx.x) < n_entries) {
+    const int e = ids_lds[threadIdx.x];
+    if (static_cast<unsigned>(e) < static_cast<unsigned>(E))
+      atomicOr(&rows_lds[(threadIdx.x / k) * words + (e >> 5)], 1u << (e & 31));
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < T * words; i += blockDim.x) bm[i] = rows_lds[i];
+
+  // 3. counts, offsets, permutations (wavefront 0, lane = token)
+  if (wave != 0) return;
+  wave_column_masks(rows_lds, 0, T, E, words, lane, masks);
+  wave_sync_lds();
+  int c[EPL];
+  int sum = 0;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane * EPL + i;
+    c[i] = e < E ? __popcll(masks[e]) : 0;
+    sum += c[i];
+  }
+  int incl = sum;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += o;
+  }
+  int run = incl - sum;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane * EPL + i;
+    if (e < E) {
+      counts[e] = c[i];
+      offsets[e] = run;
+      off_lds[e] = run;
+    }
+    run += c[i];
+  }
+  if (lane == 63) offsets[E] = incl;
+  wave_sync_lds();
+  if (lane < T) {
+    const uint64_t below = (1ull << lane) - 1ull;
+    for (int j = 0; j < k; ++j) {
+      const int s = lane * k + j;
+      const int e = ids_lds[s];
+      if (static_cast<unsigned>(e) >= static_cast<unsigned>(E)) continue;
+      const int p = off_lds[e] + __popcll(masks[e] & below);
+      if (p < 0 || p >= n_entries) continue;
+      gather[p] = s;
+      scatter[s] = p;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_route_and_group(const float* logits, int64_t T, int E, int k, int32_t* ids,
+                                  float* weights, uint32_t* bm, int32_t* counts, int32_t* offsets,
+                                  int32_t* gather, int32_t* scatter, void* ws, hipStream_t stream) {
+  if (T > kFrontMaxTokens) {
+    hipError_t err = launch_route(logits, T, E, k, ids, weights, stream);
+    if (err != hipSuccess) return err;
+    err = launch_bitmatrix(ids, T, E, k, bm, stream);
+    if (err != hipSuccess) return err;
+    return launch_offsets(bm, ids, T, E, k, counts, offsets, gather, scatter, ws, stream);
+  }
+  const int words = (E + 31) / 32;
+  const int epl = (E + 63) / 64;
+  const int t = static_cast<int>(T);
+  if (epl <= 1)
+    frontend_small_kernel<1><<<1, 1024, 0, stream>>>(logits, t, E, k, words, ids, weights, bm,
+                                                     counts, offsets, gather, scatter);
+  else if (epl <= 2)
+    frontend_small_kernel<2><<<1, 1024, 0, stream>>>(logits, t, E, k, words, ids, weights, bm,
+                                                     counts, offsets, gather, scatter);
+  else if (epl <= 4)
+    frontend_small_kernel<4><<<1, 1024, 0, stream>>>(logits, t, E, k, words, ids, weights, bm,
+                                                     counts, offsets, gather, scatter);
+  else if (epl <= 8)
+    frontend_small_kernel<8><<<1, 1024, 0, stream>>>(logits, t, E, k, words, ids, weights, bm,
+                                                     counts, offsets, gather, scatter);
+  else
+    frontend_small_kernel<16><<<1, 1024, 0, stream>>>(logits, t, E, k, words, ids, weights, bm,
+                                                      counts, offsets, gather, scatter);
+  return hipGetLastError();
+}
+
+}  // namespace moe

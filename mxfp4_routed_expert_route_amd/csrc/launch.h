@@ -24,6 +24,10 @@ hipError_t launch_ffn(const uint16_t* x, int64_t T, int H, int I, int E, int k,
                       size_t h_offset, size_t plan_offset, int64_t tile_bound,
                       hipStream_t stream, hipEvent_t const* events = nullptr);
 
+hipError_t launch_route_and_group(const float* logits, int64_t T, int E, int k, int32_t* ids,
+                                  float* weights, uint32_t* bm, int32_t* counts, int32_t* offsets,
+                                  int32_t* gather, int32_t* scatter, void* ws, hipStream_t stream);
+
 hipError_t launch_combine(const uint16_t* ys, const float* w, const int32_t* scatter, int64_t T,
                           int H, int k, uint16_t* y, hipStream_t stream);
 

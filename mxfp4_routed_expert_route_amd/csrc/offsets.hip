@@ -5,72 +5,23 @@
 // Everything is integer work with no order-dependent atomics, so results are
 // deterministic.
 //
-// Core step, per wavefront of 64 consecutive tokens (one per lane): for every
-// expert e, a ballot of "my token's bit e is set" gives the 64-bit column mask of
-// e over those tokens.  Lane (e mod 64) collects that mask with writelane, so a
-// group of 64 experts costs about four instructions per expert and one 64-bit
-// LDS store per lane.  From the masks:
-//   count of e in the wavefront       = popcount(mask[e])
-//   rank of my token among e's tokens = popcount(mask[e] & lanes-below-me)
-// which orders the rows of an expert by token, as the definition asks.
+// Core step (wave_column_masks in routing_core.h): per wavefront of 64
+// consecutive tokens, the 64-bit column mask of every expert; its popcount is
+// the expert's count and popcount(mask & lanes-below) a token's rank among the
+// expert's tokens, so an expert's rows come out in token order.
 //
 // Workgroups own 512 consecutive tokens (8 wavefronts).  T <= 512: one fused
 // kernel does counts, offsets and permutations.  Larger T: block_counts writes
 // per-workgroup expert counts, scan turns them into per-workgroup bases and
 // offsets, and ranks writes the permutations.
 #include "config.h"
-#include "device.h"
 #include "launch.h"
+#include "routing_core.h"
 
 namespace moe {
 namespace {
 
 constexpr int kWaves = kOffsBlockTokens / 64;   // 8
-
-// The LLVM writelane intrinsic (v_writelane_b32), which this clang does not expose
-// as a builtin.  Going through the intrinsic, rather than inline assembly, lets
-// the compiler see the instruction and insert the wait state it needs after a
-// VALU write of the SGPR it reads (the ballot's compare).
-extern "C" __device__ int llvm_amdgcn_writelane(int src, int lane, int old)
-    __asm("llvm.amdgcn.writelane.i32");
-
-// v <- v with lane `kLane` replaced by the wave-uniform value s.
-template <int kLane>
-__device__ __forceinline__ uint32_t write_lane(uint32_t v, uint32_t s) {
-  return static_cast<uint32_t>(
-      llvm_amdgcn_writelane(static_cast<int>(s), kLane, static_cast<int>(v)));
-}
-
-template <int kBase, int kBit = 0>
-__device__ __forceinline__ void collect_word(uint32_t word, uint32_t& lo, uint32_t& hi) {
-  if constexpr (kBit < 32) {
-    const uint64_t m = __builtin_amdgcn_ballot_w64(((word >> kBit) & 1u) != 0u);
-    lo = write_lane<kBase + kBit>(lo, static_cast<uint32_t>(m));
-    hi = write_lane<kBase + kBit>(hi, static_cast<uint32_t>(m >> 32));
-    collect_word<kBase, kBit + 1>(word, lo, hi);
-  }
-}
-
-// masks[e] (LDS) <- column mask of expert e over this wavefront's 64 tokens.
-__device__ __forceinline__ void wave_column_masks(const uint32_t* __restrict__ bm, int64_t t0,
-                                                  int64_t T, int E, int words, int lane,
-                                                  uint64_t* __restrict__ masks) {
-  const int64_t t = t0 + lane;
-  const bool valid = t < T;
-  if (t0 >= T) {   // no token in this wavefront
-    for (int e = lane; e < E; e += 64) masks[e] = 0ull;
-    return;
-  }
-  for (int w0 = 0; w0 < words; w0 += 2) {
-    const uint32_t word0 = valid ? bm[t * words + w0] : 0u;
-    const uint32_t word1 = (valid && w0 + 1 < words) ? bm[t * words + w0 + 1] : 0u;
-    uint32_t lo = 0u, hi = 0u;
-    collect_word<0>(word0, lo, hi);
-    collect_word<32>(word1, lo, hi);
-    const int e = w0 * 32 + lane;
-    if (e < E) masks[e] = (static_cast<uint64_t>(hi) << 32) | lo;
-  }
-}
 
 // Rows of this wavefront's tokens: p = base[e] + rank of the token within e.
 __device__ __forceinline__ void write_permutations(const int32_t* __restrict__ ids, int64_t t,
@@ -91,27 +42,6 @@ __device__ __forceinline__ void write_permutations(const int32_t* __restrict__ i
     gather[p] = static_cast<int32_t>(s);
     scatter[s] = static_cast<int32_t>(p);
   }
-}
-
-// Exclusive scan of one value per thread over a workgroup of 512 threads.
-__device__ __forceinline__ int block_exclusive_scan(int v, int* __restrict__ wave_tot, int* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int incl = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int o = __shfl_up(incl, d, 64);
-    if (lane >= d) incl += o;
-  }
-  if (lane == 63) wave_tot[wave] = incl;
-  __syncthreads();
-  int before = 0, all = 0;
-  for (int w = 0; w < static_cast<int>(blockDim.x >> 6); ++w) {
-    const int tw = wave_tot[w];
-    before += w < wave ? tw : 0;
-    all += tw;
-  }
-  *total = all;
-  return before + incl - v;
 }
 
 // T <= 512: everything in one workgroup.

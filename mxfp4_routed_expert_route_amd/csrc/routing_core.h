@@ -1,0 +1,142 @@
+// Device routines shared by the routing kernels (separate and fused).
+#pragma once
+#include "device.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------- top-k of one token
+//
+// Selection rule (txtmix.com article, §1 and §3: top-6 of 256 experts per token,
+// the "fast DeepSeek routing" step): the k largest logits, ordered by logit
+// descending then expert index ascending; -0.0 ranks equal to +0.0.  Weights:
+// softmax over the k chosen logits.
+//
+// Each lane holds EPL logits (expert e = i*64 + lane, coalesced loads) as 64-bit
+// keys (order-preserving logit bits << 32 | ~e), so one unsigned max picks the
+// larger logit and, on a tie, the lower index.  k rounds of a wave-wide max
+// (butterfly) take the winners in order; the winner's key is retired in the lane
+// that holds it.  Lane j < k returns slot j's id and weight.
+
+__device__ __forceinline__ uint32_t order_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) == 0u) u = 0u;   // -0.0 ranks as +0.0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float order_bits_to_f32(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+template <int EPL>
+__device__ __forceinline__ void route_token(const float* __restrict__ row, int E, int k, int lane,
+                                            int& my_id, float& my_weight) {
+  uint64_t key[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = i * 64 + lane;
+    key[i] = (e < E) ? ((static_cast<uint64_t>(order_bits(row[e])) << 32) | static_cast<uint32_t>(~e))
+                     : 0ull;   // below every real key
+  }
+  my_id = 0;
+  float my_logit = 0.f, top = 0.f;
+  for (int j = 0; j < k; ++j) {
+    uint64_t best = key[0];
+#pragma unroll
+    for (int i = 1; i < EPL; ++i) best = key[i] > best ? key[i] : best;
+#pragma unroll
+    for (int m = 32; m > 0; m >>= 1) {
+      const uint64_t o = shfl_xor_u64(best, m);
+      best = o > best ? o : best;
+    }
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      if (key[i] == best) key[i] = 0ull;
+    const float l = order_bits_to_f32(static_cast<uint32_t>(best >> 32));
+    if (j == 0) top = l;
+    if (lane == j) {
+      my_id = static_cast<int>(~static_cast<uint32_t>(best));
+      my_logit = l;
+    }
+  }
+  // softmax over the selection: fp32 exponentials, fp64 sum in j order
+  const float ex = (lane < k) ? expf(my_logit - top) : 0.f;
+  double sum = 0.0;
+  for (int j = 0; j < k; ++j) sum += static_cast<double>(__shfl(ex, j, 64));
+  my_weight = static_cast<float>(static_cast<double>(ex) / sum);
+}
+
+// ---------------------------------------------------------------- expert column masks
+//
+// For a wavefront of 64 consecutive tokens (one per lane): for every expert e, a
+// ballot of "my token's bit e is set" is the 64-bit column mask of e over those
+// tokens.  Lane (e mod 64) collects that mask, so a group of 64 experts costs
+// about five instructions per expert and one 64-bit store per lane.  From the
+// masks: count of e = popcount(mask[e]); rank of a token among e's tokens =
+// popcount(mask[e] & lanes-below-it), which orders an expert's rows by token.
+
+// The LLVM writelane intrinsic (v_writelane_b32), which this clang does not expose
+// as a builtin.  Going through the intrinsic, rather than inline assembly, lets
+// the compiler see the instruction and insert the wait state it needs after a
+// VALU write of the SGPR it reads (the ballot's compare).
+extern "C" __device__ int llvm_amdgcn_writelane(int src, int lane, int old)
+    __asm("llvm.amdgcn.writelane.i32");
+
+template <int kLane>
+__device__ __forceinline__ uint32_t write_lane(uint32_t v, uint32_t s) {
+  return static_cast<uint32_t>(
+      llvm_amdgcn_writelane(static_cast<int>(s), kLane, static_cast<int>(v)));
+}
+
+template <int kBase, int kBit = 0>
+__device__ __forceinline__ void collect_word(uint32_t word, uint32_t& lo, uint32_t& hi) {
+  if constexpr (kBit < 32) {
+    const uint64_t m = __builtin_amdgcn_ballot_w64(((word >> kBit) & 1u) != 0u);
+    lo = write_lane<kBase + kBit>(lo, static_cast<uint32_t>(m));
+    hi = write_lane<kBase + kBit>(hi, static_cast<uint32_t>(m >> 32));
+    collect_word<kBase, kBit + 1>(word, lo, hi);
+  }
+}
+
+// masks[e] <- column mask of expert e over rows[t0 .. t0+63] (rows past T are empty).
+// `bm` points at row 0 of a [T][words] bit matrix (global or LDS).
+__device__ __forceinline__ void wave_column_masks(const uint32_t* bm, int64_t t0, int64_t T, int E,
+                                                  int words, int lane, uint64_t* masks) {
+  const int64_t t = t0 + lane;
+  const bool valid = t < T;
+  if (t0 >= T) {   // no token in this wavefront
+    for (int e = lane; e < E; e += 64) masks[e] = 0ull;
+    return;
+  }
+  for (int w0 = 0; w0 < words; w0 += 2) {
+    const uint32_t word0 = valid ? bm[t * words + w0] : 0u;
+    const uint32_t word1 = (valid && w0 + 1 < words) ? bm[t * words + w0 + 1] : 0u;
+    uint32_t lo = 0u, hi = 0u;
+    collect_word<0>(word0, lo, hi);
+    collect_word<32>(word1, lo, hi);
+    const int e = w0 * 32 + lane;
+    if (e < E) masks[e] = (static_cast<uint64_t>(hi) << 32) | lo;
+  }
+}
+
+// Exclusive scan of one value per thread over the workgroup (blockDim.x <= 1024).
+__device__ __forceinline__ int block_exclusive_scan(int v, int* __restrict__ wave_tot, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += o;
+  }
+  if (lane == 63) wave_tot[wave] = incl;
+  __syncthreads();
+  int before = 0, all = 0;
+  for (int w = 0; w < static_cast<int>(blockDim.x >> 6); ++w) {
+    const int tw = wave_tot[w];
+    before += w < wave ? tw : 0;
+    all += tw;
+  }
+  *total = all;
+  return before + incl - v;
+}
+
+}  // namespace moe

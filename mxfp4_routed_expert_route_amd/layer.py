@@ -71,7 +71,12 @@ def to_device(inp: dict, device="cuda") -> dict:
     return out
 
 
-def run_routing(dev: dict, b: LayerBuffers, stream=None):
+def run_routing(dev: dict, b: LayerBuffers, stream=None, fused: bool = False):
+    """A1-A3: three calls, or the fused front-end entry point (same outputs)."""
+    if fused:
+        binding.moe_route_and_group(dev["logits"], b.k, b.topk_ids, b.topk_weights, b.bitmatrix,
+                                    b.counts, b.offsets, b.gather, b.scatter, b.ws, stream)
+        return
     binding.moe_route(dev["logits"], b.k, b.topk_ids, b.topk_weights, stream)
     binding.moe_build_bitmatrix(b.topk_ids, b.E, b.bitmatrix, stream)
     binding.moe_expert_offsets(b.bitmatrix, b.topk_ids, b.E, b.counts, b.offsets, b.gather,
@@ -84,8 +89,8 @@ def run_ffn(dev: dict, b: LayerBuffers, limit: float, stream=None):
     binding.moe_combine(b.y_sorted, b.topk_weights, b.scatter, b.y, stream)
 
 
-def run_layer(dev: dict, b: LayerBuffers, limit: float, stream=None):
-    run_routing(dev, b, stream)
+def run_layer(dev: dict, b: LayerBuffers, limit: float, stream=None, fused: bool = False):
+    run_routing(dev, b, stream, fused)
     run_ffn(dev, b, limit, stream)
 
 

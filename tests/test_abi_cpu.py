@@ -12,13 +12,13 @@ import pytest
 from mxfp4_routed_expert_route_amd import build as build_mod
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "moe_mxfp4.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("moe_mxfp4.h", "moe_mxfp4_profiling.h")]
 
 OK, INVALID, UNSUPPORTED, MISALIGNED, WS_SMALL = 0, 1, 2, 3, 4
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", text)))
 
@@ -32,8 +32,9 @@ def lib():
 
 def test_header_declares_the_five_calls():
     names = declared_functions()
-    for n in ("moe_route", "moe_build_bitmatrix", "moe_expert_offsets", "moe_grouped_ffn_mxfp4",
-              "moe_combine", "moe_workspace_bytes", "moe_status_string"):
+    for n in ("moe_route", "moe_build_bitmatrix", "moe_expert_offsets", "moe_route_and_group",
+              "moe_grouped_ffn_mxfp4", "moe_combine", "moe_workspace_bytes", "moe_status_string",
+              "moe_grouped_ffn_mxfp4_timed"):
         assert n in names
 
 

@@ -43,13 +43,13 @@ def _layer():
     return layer
 
 
-def run_gpu(inp, limit=10.0):
+def run_gpu(inp, limit=10.0, fused=False):
     layer = _layer()
     T = inp["logits"].shape[0]
     wl = inp["workload"]
     dev = layer.to_device(inp)
     b = layer.LayerBuffers.allocate(T, wl.E, wl.k, wl.H, wl.I)
-    layer.run_layer(dev, b, 0.0 if limit is None else limit)   # <= 0 turns the clamp off
+    layer.run_layer(dev, b, 0.0 if limit is None else limit, fused=fused)   # <= 0: no clamp
     torch.cuda.synchronize()
     return b
 
@@ -107,11 +107,11 @@ def tiny(T, E, k, H, I, seed, skew=False):
         w2_s=rng.integers(120, 127, (E, H, I // 32), dtype=np.uint8))
 
 
-def whole_layer_parity(inp, limit):
+def whole_layer_parity(inp, limit, fused=False):
     wl = inp["workload"]
     T = inp["logits"].shape[0]
-    _say(f"[parity] T={T} E={wl.E} k={wl.k} H={wl.H} I={wl.I} limit={limit}")
-    b = run_gpu(inp, limit)
+    _say(f"[parity] T={T} E={wl.E} k={wl.k} H={wl.H} I={wl.I} limit={limit} fused={fused}")
+    b = run_gpu(inp, limit, fused)
     ref = oracle.moe_layer(inp, limit)
     check_routing(b, ref, wl.E, wl.k)
     r1 = ffn_close(b.y_sorted.float().cpu().numpy(), ref["y_sorted"])
@@ -136,6 +136,22 @@ def test_workload0_whole_layer(limit):
 ])
 def test_ragged_shapes_whole_layer(T, E, k, H, I, seed):
     whole_layer_parity(tiny(T, E, k, H, I, seed), 10.0)
+
+
+@pytest.mark.parametrize("T,E,k,seed", [
+    (1, 256, 6, 31), (8, 256, 6, 32), (16, 256, 6, 33), (63, 256, 6, 34), (64, 256, 6, 35),
+    (65, 256, 6, 36),                # past the one-launch limit: the separate kernels
+    (64, 1024, 8, 37), (20, 40, 3, 38), (10, 64, 1, 39),
+])
+def test_fused_front_end(T, E, k, seed):
+    whole_layer_parity(tiny(T, E, k, 128, 128, seed), 10.0, fused=True)
+
+
+def test_fused_front_end_ties():
+    inp = tiny(50, 64, 6, 128, 128, 40)
+    inp["logits"][:] = 0.0
+    inp["logits"][1::2, 9] = -0.0
+    whole_layer_parity(inp, 10.0, fused=True)
 
 
 def test_skewed_small_whole_layer():
@@ -225,7 +241,7 @@ def test_full_size_workload(index):
     wl = inputs.workload(index)
     _say(f"[full] workload {index} ({wl.name}) T={wl.T}: generating inputs")
     inp = inputs.make_inputs(index)
-    b = run_gpu(inp, 10.0)
+    b = run_gpu(inp, 10.0, fused=True)   # the launch configuration bench.py times
     _say(f"[full] workload {index}: routing parity")
     ref = oracle_routing(inp["logits"], wl.E, wl.k)
     check_routing(b, ref, wl.E, wl.k)
