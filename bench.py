@@ -68,6 +68,15 @@ class HipEvents:
         return f.value
 
 
+def ffn_kernel_name(T: int, E: int, k: int) -> str:
+    """The W1 kernel the library picks for these sizes (its row-tile rule)."""
+    if T <= 16:
+        return "gemm_stream_kernel<true, 1, true>"
+    if T * k // E <= 24:
+        return "gemm_stream_kernel<true, 2, true>"
+    return "gemm_tile_kernel<true, 4>"
+
+
 def measured_traffic(profile_name: str, kernel_source: str):
     """HBM bytes per launch from a committed rocprofv3 summary, or None when the
     kernel source has changed since the counters were taken."""
@@ -288,11 +297,12 @@ def main():
         "ffn_w1_us_timed": w1_ms * 1e3,
         "ffn_w2_us_timed": w2_ms * 1e3,
         "touched_experts": touched,
-        "roofline": {"bound": "hbm", "kernel": "gemm_kernel<true> (W1 gate|up + SwiGLU)",
+        "roofline": {"bound": "hbm",
+                     "kernel": "W1 gate|up + clamped SwiGLU (" + ffn_kernel_name(T, E, k) + ")",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": (measured_traffic("ffn_w1_stream_verify-1+7.md",
-                                                  "mxfp4_routed_expert_route_amd/csrc/ffn.hip")
+                                                  "mxfp4_routed_expert_route_amd/csrc/ffn_stream.hip")
                                  if wl.index == 1 else None),
                      "algorithmic_bytes_per_launch": w1_alg},
         "layer_hbm_frac": layer_alg / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,

@@ -1,0 +1,315 @@
+// Streaming grouped GEMM for decode-shaped batches (row tiles of <= 32 rows).
+#include "ffn_common.h"
+
+namespace moe {
+namespace {
+
+// ---------------------------------------------------------------- streaming GEMM (few rows)
+//
+// For row tiles of at most 16*MSUB rows (decode-shaped batches, where each
+// expert has a handful of rows and the weights are read once): one wavefront
+// owns a row tile and 64 weight rows (W1: 32 gate rows and the 32 matching up
+// rows; W2: 64 output rows) and needs no barrier, so many wavefronts stay
+// resident per CU.
+//
+// Memory pipeline (kDeep, K a multiple of 512).  K advances in chunks of 256
+// elements: each lane takes 32 bytes (two scale blocks) of each of its four rows,
+// so a weight row is visited 128 bytes at a time -- measured on MI355X, 128-byte
+// visits of this many concurrent rows stream about 20% faster than 64-byte ones.
+// Vector-memory loads retire in issue order and a wait is a count of loads still
+// allowed in flight, so the issue order decides what a wait drains: per chunk the
+// loop issues the chunk's activations, then the next chunk's weights, then
+// computes; the wait for the activations leaves the weight prefetch in flight.
+// Every load in the loop is unconditional (rows past the tile read zeros through
+// a bounded buffer resource; the last prefetch re-reads the last chunk), which
+// keeps those wait counts exact.  The E8M0 scales of the wavefront's 64 rows are
+// staged in LDS once, laid out so that two 16-byte LDS reads per chunk give a
+// lane the scales of its four rows; they never enter the vector-memory queue.
+// Otherwise (small K): 128-element chunks, one-chunk prefetch, scales from memory.
+template <bool kW1, int MSUB, bool kDeep>
+__global__ __launch_bounds__(256) void gemm_stream_kernel(
+    const uint16_t* __restrict__ act, uint32_t act_bytes, const int32_t* __restrict__ gather,
+    int k_top, int n_slots, const uint8_t* __restrict__ wq, const uint8_t* __restrict__ wsc,
+    const RowTile* __restrict__ tiles, const int32_t* __restrict__ n_tiles, int K, int n_rows,
+    int half, int waves_per_tile, float limit, int clamp, uint16_t* __restrict__ out,
+    int ld_out) {
+  extern __shared__ uint32_t scale_lds[];   // kDeep: per wavefront [K/128][16][4] dwords
+  const int lane = threadIdx.x & 63;
+  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int tile_id = gw / waves_per_tile;
+  const int cg = gw - tile_id * waves_per_tile;
+  if (tile_id >= *n_tiles) return;   // per wavefront: no workgroup barrier in this kernel
+  const RowTile rt = tiles[tile_id];
+  const int r16 = lane & 15, g = lane >> 4;
+  const int n_chunks = K / kFfnKChunk;
+
+  const __amdgpu_buffer_rsrc_t arsrc = make_rsrc(act, act_bytes);
+  uint32_t aoff[MSUB];   // byte offset of this lane's activation run in chunk 0
+#pragma unroll
+  for (int mi = 0; mi < MSUB; ++mi) {
+    const int p = rt.p_begin + mi * 16 + r16;
+    bool valid = p < rt.p_end;
+    uint32_t row = 0;
+    if (valid) {
+      if (kW1) {
+        const int slot = gather[p];   // a slot id outside [0, T*k) feeds zeros, never an address
+        valid = static_cast<unsigned>(slot) < static_cast<unsigned>(n_slots);
+        row = valid ? static_cast<uint32_t>(slot / k_top) : 0u;
+      } else {
+        row = static_cast<uint32_t>(p);
+      }
+    }
+    // lane group g starts at element 32g (128-element chunks) or 64g (256-element chunks)
+    aoff[mi] = valid ? row * static_cast<uint32_t>(K) * 2u + (kDeep ? 128u : 64u) * g
+                     : kRsrcOutOfRange;
+  }
+
+  // weight row of fragment f for a lane whose MFMA column is c16
+  auto wrow = [&](int f, int c16) {
+    return kW1 ? (f >= 2 ? half : 0) + cg * 32 + (f & 1) * 16 + c16   // gate, gate, up, up
+               : cg * 64 + f * 16 + c16;
+  };
+  int nrow[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) nrow[f] = wrow(f, r16);
+  const size_t row_q = static_cast<size_t>(K / 2), row_s = static_cast<size_t>(K / 32);
+  const size_t e_rows = static_cast<size_t>(rt.expert) * n_rows;
+  const uint8_t* bq[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) bq[f] = wq + (e_rows + nrow[f]) * row_q + (kDeep ? 0 : 16 * g);
+
+  uint32_t* my_scales = scale_lds + (threadIdx.x >> 6) * (n_chunks * 64);
+  if (kDeep) {
+    // lane L stages the scales of row (f = L/16, column L%16).  The 8 scale bytes
+    // of a 256-element chunk c2 (2 per lane group) go to the two dwords
+    // my_scales[((c2*16 + L%16)*4 + f)*2 + {0,1}]
+    const int f = lane >> 4;
+    const uint8_t* srow = wsc + (e_rows + wrow(f, r16)) * row_s;
+    for (int c = 0; c < n_chunks; c += 4) {   // c counts 128-element chunks
+      const uint4 d = *reinterpret_cast<const uint4*>(srow + c * 4);
+      const int c2 = c / 2;
+      my_scales[(((c2 + 0) * 16 + r16) * 4 + f) * 2 + 0] = d.x;
+      my_scales[(((c2 + 0) * 16 + r16) * 4 + f) * 2 + 1] = d.y;
+      my_scales[(((c2 + 1) * 16 + r16) * 4 + f) * 2 + 0] = d.z;
+      my_scales[(((c2 + 1) * 16 + r16) * 4 + f) * 2 + 1] = d.w;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+  const uint8_t* bs[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) bs[f] = wsc + (e_rows + nrow[f]) * row_s + g;
+
+  floatx4 acc[MSUB][4];
+#pragma unroll
+  for (int mi = 0; mi < MSUB; ++mi)
+#pragma unroll
+    for (int f = 0; f < 4; ++f) acc[mi][f] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  auto load_w = [&](uint4 (&q)[4], int kc) {
+#pragma unroll
+    for (int f = 0; f < 4; ++f) q[f] = *reinterpret_cast<const uint4*>(bq[f] + kc * 64);
+  };
+  auto load_s = [&](uint32_t (&sc)[4], int kc) {   // from memory (shallow pipeline)
+#pragma unroll
+    for (int f = 0; f < 4; ++f) sc[f] = bs[f][kc * 4];
+  };
+  auto lds_s = [&](uint32_t (&sc)[4], int kc) {    // from the staged copy
+    const uint4 d = *reinterpret_cast<const uint4*>(my_scales + (kc * 16 + r16) * 4);
+    const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+    for (int f = 0; f < 4; ++f) sc[f] = (dw[f] >> (8 * g)) & 0xFFu;
+  };
+  auto load_a = [&](bf16x8 (&a)[MSUB][4], int kc) {
+#pragma unroll
+    for (int mi = 0; mi < MSUB; ++mi)
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        a[mi][s] = __builtin_bit_cast(
+            bf16x8, __builtin_amdgcn_raw_buffer_load_b128(arsrc, aoff[mi] + kc * 256 + 16 * s, 0, 0));
+  };
+  auto compute = [&](const uint4 (&q)[4], const uint32_t (&sc)[4], const bf16x8 (&a)[MSUB][4]) {
+    const uint32_t w[4][4] = {{q[0].x, q[0].y, q[0].z, q[0].w},
+                              {q[1].x, q[1].y, q[1].z, q[1].w},
+                              {q[2].x, q[2].y, q[2].z, q[2].w},
+                              {q[3].x, q[3].y, q[3].z, q[3].w}};
+    float scl[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) scl[f] = e8m0_as_f32(sc[f]);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        const bf16x8 b = dequant8(w[f][s], scl[f]);
+#pragma unroll
+        for (int mi = 0; mi < MSUB; ++mi)
+          acc[mi][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mi][s], b, acc[mi][f], 0, 0, 0);
+      }
+    }
+  };
+
+  if constexpr (kDeep) {
+    // 256-element chunks: each lane takes 32 bytes (two scale blocks) of each of its
+    // four rows, so a row is visited 128 bytes at a time (about 20% more HBM
+    // throughput than 64-byte visits for this many concurrent rows).  Weights:
+    // two register stages (the next chunk streams in while this one computes).
+    // Activations: loaded for the current chunk, issued before the weight
+    // prefetch, so waiting for them leaves the prefetch in flight.
+    const int n2 = n_chunks / 2;   // 256-element chunks (even: n_chunks % 4 == 0)
+    auto load_w2 = [&](uint4 (&q)[4][2], int c2) {
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        const uint8_t* src = bq[f] + c2 * 128 + 32 * g;   // lane group g: bytes 32g..32g+31
+        q[f][0] = *reinterpret_cast<const uint4*>(src);
+        q[f][1] = *reinterpret_cast<const uint4*>(src + 16);
+      }
+    };
+    auto load_a2 = [&](bf16x8 (&a)[MSUB][8], int c2) {
+#pragma unroll
+      for (int mi = 0; mi < MSUB; ++mi)
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+          a[mi][t] = __builtin_bit_cast(
+              bf16x8, __builtin_amdgcn_raw_buffer_load_b128(arsrc, aoff[mi] + c2 * 512 + 16 * t, 0, 0));
+    };
+    auto compute2 = [&](const uint4 (&q)[4][2], const bf16x8 (&a)[MSUB][8], int c2) {
+      const uint4 d0 = *reinterpret_cast<const uint4*>(my_scales + ((c2 * 16 + r16) * 4) * 2);
+      const uint4 d1 = *reinterpret_cast<const uint4*>(my_scales + ((c2 * 16 + r16) * 4) * 2 + 4);
+      const uint32_t sd[4][2] = {{d0.x, d0.y}, {d0.z, d0.w}, {d1.x, d1.y}, {d1.z, d1.w}};
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        float scl[4];
+#pragma unroll
+        for (int f = 0; f < 4; ++f)   // block 2g + j of the chunk: byte (2g+j)%4 of dword (2g+j)/4
+          scl[f] = e8m0_as_f32((sd[f][(2 * g + j) >> 2] >> (8 * ((2 * g + j) & 3))) & 0xFFu);
+        const uint32_t w[4][4] = {{q[0][j].x, q[0][j].y, q[0][j].z, q[0][j].w},
+                                  {q[1][j].x, q[1][j].y, q[1][j].z, q[1][j].w},
+                                  {q[2][j].x, q[2][j].y, q[2][j].z, q[2][j].w},
+                                  {q[3][j].x, q[3][j].y, q[3][j].z, q[3][j].w}};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+#pragma unroll
+          for (int f = 0; f < 4; ++f) {
+            const bf16x8 b = dequant8(w[f][s], scl[f]);
+#pragma unroll
+            for (int mi = 0; mi < MSUB; ++mi)
+              acc[mi][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mi][4 * j + s], b, acc[mi][f],
+                                                                   0, 0, 0);
+          }
+        }
+      }
+    };
+    uint4 q0[4][2], q1[4][2];
+    load_w2(q0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int c2 = 0; c2 < n2; c2 += 2) {
+#define MOE_STREAM_STEP(Q_NEXT, KQ, Q_CUR, KC) \
+  {                                           \
+    bf16x8 a[MSUB][8];                        \
+    load_a2(a, KC);                           \
+    __builtin_amdgcn_sched_barrier(0);        \
+    load_w2(Q_NEXT, KQ);                      \
+    __builtin_amdgcn_sched_barrier(0);        \
+    compute2(Q_CUR, a, KC);                   \
+    __builtin_amdgcn_sched_barrier(0);        \
+  }
+      MOE_STREAM_STEP(q1, c2 + 1, q0, c2)
+      MOE_STREAM_STEP(q0, c2 + 2 < n2 ? c2 + 2 : n2 - 1, q1, c2 + 1)
+#undef MOE_STREAM_STEP
+    }
+  } else {
+    uint4 qa[4], qb[4];
+    uint32_t sa[4], sb[4];
+    load_w(qa, 0);
+    load_s(sa, 0);
+    int kc = 0;
+    for (; kc + 2 <= n_chunks; kc += 2) {
+      bf16x8 a0[MSUB][4];
+      load_a(a0, kc);
+      __builtin_amdgcn_sched_barrier(0);
+      load_w(qb, kc + 1);
+      load_s(sb, kc + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(qa, sa, a0);
+      __builtin_amdgcn_sched_barrier(0);
+      bf16x8 a1[MSUB][4];
+      load_a(a1, kc + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      const int kn = kc + 2 < n_chunks ? kc + 2 : kc + 1;   // last pass re-reads a valid chunk
+      load_w(qa, kn);
+      load_s(sa, kn);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(qb, sb, a1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (kc < n_chunks) {   // odd chunk count: the last chunk is in qa
+      bf16x8 a0[MSUB][4];
+      load_a(a0, kc);
+      compute(qa, sa, a0);
+    }
+  }
+
+  // D layout of a 16x16 MFMA tile: lane holds column (lane & 15), rows 4*(lane>>4) + i.
+  const bool do_clamp = clamp != 0;
+#pragma unroll
+  for (int mi = 0; mi < MSUB; ++mi) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int p = rt.p_begin + mi * 16 + 4 * g + i;
+      if (p >= rt.p_end) continue;
+      uint16_t* orow = out + static_cast<int64_t>(p) * ld_out;
+      if (kW1) {
+        orow[nrow[0]] = f32_to_bf16_bits(swiglu(acc[mi][0][i], acc[mi][2][i], limit, do_clamp));
+        orow[nrow[1]] = f32_to_bf16_bits(swiglu(acc[mi][1][i], acc[mi][3][i], limit, do_clamp));
+      } else {
+#pragma unroll
+        for (int f = 0; f < 4; ++f) orow[nrow[f]] = f32_to_bf16_bits(acc[mi][f][i]);
+      }
+    }
+  }
+}
+
+// Launch one streaming GEMM; picks the deep pipeline when K allows it.
+template <bool kW1, int MSUB>
+hipError_t launch_stream_t(unsigned grid, hipStream_t stream, const uint16_t* act, uint32_t act_bytes,
+                         const int32_t* gather, int k_top, int n_slots, const uint8_t* wq,
+                         const uint8_t* wsc, const RowTile* tiles, const int32_t* n_tiles, int K,
+                         int n_rows, int half, int wpt, float limit, int clamp, uint16_t* out,
+                         int ld_out) {
+  const int n_chunks = K / kFfnKChunk;
+  const size_t lds = static_cast<size_t>(4) * n_chunks * 64 * sizeof(uint32_t);
+  if (n_chunks % 4 == 0 && lds <= kStreamMaxScaleLds)
+    gemm_stream_kernel<kW1, MSUB, true><<<grid, 256, lds, stream>>>(
+        act, act_bytes, gather, k_top, n_slots, wq, wsc, tiles, n_tiles, K, n_rows, half, wpt,
+        limit, clamp, out, ld_out);
+  else
+    gemm_stream_kernel<kW1, MSUB, false><<<grid, 256, 0, stream>>>(
+        act, act_bytes, gather, k_top, n_slots, wq, wsc, tiles, n_tiles, K, n_rows, half, wpt,
+        limit, clamp, out, ld_out);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_stream(bool w1, int msub, unsigned grid, hipStream_t stream, const uint16_t* act,
+                         uint32_t act_bytes, const int32_t* gather, int k_top, int n_slots,
+                         const uint8_t* wq, const uint8_t* wsc, const RowTile* tiles,
+                         const int32_t* n_tiles, int K, int n_rows, int half, int wpt, float limit,
+                         int clamp, uint16_t* out, int ld_out) {
+  if (w1)
+    return msub == 1 ? launch_stream_t<true, 1>(grid, stream, act, act_bytes, gather, k_top,
+                                                n_slots, wq, wsc, tiles, n_tiles, K, n_rows, half,
+                                                wpt, limit, clamp, out, ld_out)
+                     : launch_stream_t<true, 2>(grid, stream, act, act_bytes, gather, k_top,
+                                                n_slots, wq, wsc, tiles, n_tiles, K, n_rows, half,
+                                                wpt, limit, clamp, out, ld_out);
+  return msub == 1 ? launch_stream_t<false, 1>(grid, stream, act, act_bytes, gather, k_top,
+                                               n_slots, wq, wsc, tiles, n_tiles, K, n_rows, half,
+                                               wpt, limit, clamp, out, ld_out)
+                   : launch_stream_t<false, 2>(grid, stream, act, act_bytes, gather, k_top,
+                                               n_slots, wq, wsc, tiles, n_tiles, K, n_rows, half,
+                                               wpt, limit, clamp, out, ld_out);
+}
+
+}  // namespace moe

@@ -1,0 +1,295 @@
+// Tiled grouped GEMM for prefill-shaped batches (64-row tiles).
+#include "ffn_common.h"
+
+namespace moe {
+namespace {
+
+// ---------------------------------------------------------------- tiled GEMM (many rows)
+//
+// For row tiles of 64 or 128 rows (prefill-shaped batches).  A workgroup of four
+// wavefronts owns one row tile and 256 weight rows; each wavefront has 64 weight
+// rows (same split as the streaming kernel: W1 32 gate + 32 up rows, W2 64 output
+// rows) and all 16-row MFMA subtiles of the tile (kMSub = 4 or 8), so each
+// dequantised weight fragment feeds kMSub MFMAs.  The activation tile of each K
+// chunk (kMSub*16 rows x 128 bf16) is loaded once per workgroup into LDS
+// (double-buffered; rows padded by 16 bytes so that the 16 lanes of a read group
+// hit distinct banks) and read by all four wavefronts.  Weights go straight to
+// registers, issued right after the chunk that frees their registers.  With 64-row
+// tiles the E8M0 scales are staged in LDS as in the streaming kernel; with
+// 128-row tiles the LDS holds only activations and the scales come with the
+// weights.
+//
+// Per chunk c: issue the activation loads of c+1 (128 rows) or c+2 (64 rows),
+// compute c, issue the weights of c+2, store the activations of c+1 to the other
+// LDS buffer, barrier.
+//
+// Workgroup order.  The hardware deals consecutive workgroups to the 8 XCDs in
+// turn, and each XCD has its own 4 MB L2.  Launch order (row tile major) gives
+// each XCD 2 of the 16 column blocks of every tile: a small weight slice per L2,
+// but every tile's activations fetched into all 8 L2s.  Measured alternatives:
+// whole tiles per XCD (each L2 then cycles an expert's full 8.9 MB W1) was 40%
+// slower; 4 column blocks x half the tiles per XCD is ~1% faster than launch
+// order and is what is used.
+constexpr int kARowBytes = kFfnKChunk * 2 + 16;   // 256 B of bf16 + 16 B pad
+constexpr int kXcds = 8;
+
+template <int kMSub>
+constexpr int a_buf_bytes() { return kMSub * 16 * kARowBytes; }
+
+template <bool kW1, int kMSub>
+__global__ __launch_bounds__(256, 2) void gemm_tile_kernel(
+    const uint16_t* __restrict__ act, uint32_t act_bytes, const int32_t* __restrict__ gather,
+    int k_top, int n_slots, const uint8_t* __restrict__ wq, const uint8_t* __restrict__ wsc,
+    const RowTile* __restrict__ tiles, const int32_t* __restrict__ n_tiles, int K, int n_rows,
+    int half, int waves_per_tile, int blocks_per_tile, float limit, int clamp,
+    uint16_t* __restrict__ out, int ld_out) {
+  constexpr bool kLdsScales = kMSub == 4;
+  constexpr int kRows = kMSub * 16;
+  constexpr int kABuf = a_buf_bytes<kMSub>();
+  constexpr int kThreadsPerRow = 256 / kRows;          // 4 (64 rows) or 2 (128 rows)
+  constexpr int kPieces = kMSub;                       // 16-byte pieces per thread per chunk
+  extern __shared__ __attribute__((aligned(16))) unsigned char tile_lds[];
+
+  // work id: with 16 column blocks per tile, XCD x takes column blocks
+  // 4(x%4)..4(x%4)+3 of the row tiles of parity x/4 (its weight slice stays in its
+  // L2 while each tile's activations go to 4 XCDs, not 8); otherwise launch order
+  int work = blockIdx.x;
+  if (blocks_per_tile == 16) {
+    const int x = blockIdx.x % kXcds, l = blockIdx.x / kXcds;
+    work = ((l / 4) * 2 + x / 4) * 16 + (x % 4) * 4 + (l % 4);
+  }
+  const int tile_id = work / blocks_per_tile;
+  const int nb = work - tile_id * blocks_per_tile;
+  if (tile_id >= *n_tiles) return;   // uniform over the workgroup
+  const RowTile rt = tiles[tile_id];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int n_chunks = K / kFfnKChunk;
+  const int rows = rt.p_end - rt.p_begin;
+  const int msub = (rows + 15) >> 4;   // subtiles that hold rows
+
+  // column group of this wavefront; a wavefront past the last group repeats the
+  // last one (it still stages activations and meets every barrier) and stores nothing
+  const int cg_raw = nb * 4 + wave;
+  const bool store_cols = cg_raw < waves_per_tile;
+  const int cg = store_cols ? cg_raw : waves_per_tile - 1;
+
+  // --- activation staging: thread -> (row ar, part aq) of the chunk
+  const __amdgpu_buffer_rsrc_t arsrc = make_rsrc(act, act_bytes);
+  const int ar = tid / kThreadsPerRow, aq = tid % kThreadsPerRow;
+  uint32_t aoff;
+  {
+    const int p = rt.p_begin + ar;
+    bool valid = p < rt.p_end;
+    uint32_t row = 0;
+    if (valid) {
+      if (kW1) {
+        const int slot = gather[p];
+        valid = static_cast<unsigned>(slot) < static_cast<unsigned>(n_slots);
+        row = valid ? static_cast<uint32_t>(slot / k_top) : 0u;
+      } else {
+        row = static_cast<uint32_t>(p);
+      }
+    }
+    aoff = valid ? row * static_cast<uint32_t>(K) * 2u + 16u * kPieces * aq : kRsrcOutOfRange;
+  }
+  unsigned char* a_lds = tile_lds;                       // [2][kRows][kARowBytes]
+  const int a_store = ar * kARowBytes + aq * 16 * kPieces;
+  auto load_a = [&](uint4 (&ra)[kPieces], int kc) {
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i)
+      ra[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            arsrc, aoff + kc * 256 + 16 * i, 0, 0));
+  };
+  auto store_a = [&](const uint4 (&ra)[kPieces], int buf) {
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i)
+      *reinterpret_cast<uint4*>(a_lds + buf * kABuf + a_store + 16 * i) = ra[i];
+  };
+
+  // --- weights: four fragments of 16 rows, this lane's row in each
+  auto wrow = [&](int f, int c16) {
+    return kW1 ? (f >= 2 ? half : 0) + cg * 32 + (f & 1) * 16 + c16 : cg * 64 + f * 16 + c16;
+  };
+  int nrow[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) nrow[f] = wrow(f, r16);
+  const size_t row_q = static_cast<size_t>(K / 2), row_s = static_cast<size_t>(K / 32);
+  const size_t e_rows = static_cast<size_t>(rt.expert) * n_rows;
+  const uint8_t* bq[4];
+  const uint32_t* bs[4];   // scale dword of (row, chunk): one byte per lane group
+#pragma unroll
+  for (int f = 0; f < 4; ++f) {
+    bq[f] = wq + (e_rows + nrow[f]) * row_q + 16 * g;
+    bs[f] = reinterpret_cast<const uint32_t*>(wsc + (e_rows + nrow[f]) * row_s);
+  }
+  auto load_w = [&](uint4 (&q)[4], uint32_t (&sd)[4], int kc) {
+#pragma unroll
+    for (int f = 0; f < 4; ++f) q[f] = *reinterpret_cast<const uint4*>(bq[f] + kc * 64);
+    if constexpr (!kLdsScales) {
+#pragma unroll
+      for (int f = 0; f < 4; ++f) sd[f] = bs[f][kc];
+    }
+  };
+
+  // --- 64-row tiles: scales of the wavefront's 64 rows, staged as [chunk][16][4] dwords
+  uint32_t* my_scales =
+      reinterpret_cast<uint32_t*>(tile_lds + 2 * kABuf) + wave * (n_chunks * 64);
+  if constexpr (kLdsScales) {
+    const int f = lane >> 4;
+    const uint8_t* srow = wsc + (e_rows + wrow(f, r16)) * row_s;
+    int c = 0;
+    for (; c + 4 <= n_chunks; c += 4) {
+      const uint4 d = *reinterpret_cast<const uint4*>(srow + c * 4);
+      my_scales[((c + 0) * 16 + r16) * 4 + f] = d.x;
+      my_scales[((c + 1) * 16 + r16) * 4 + f] = d.y;
+      my_scales[((c + 2) * 16 + r16) * 4 + f] = d.z;
+      my_scales[((c + 3) * 16 + r16) * 4 + f] = d.w;
+    }
+    for (; c < n_chunks; ++c)
+      my_scales[(c * 16 + r16) * 4 + f] = *reinterpret_cast<const uint32_t*>(srow + c * 4);
+  }
+
+  floatx4 acc[kMSub][4];
+#pragma unroll
+  for (int mi = 0; mi < kMSub; ++mi)
+#pragma unroll
+    for (int f = 0; f < 4; ++f) acc[mi][f] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  // one chunk: activations from LDS buffer `buf`, weights in q, scale dwords in sd
+  auto compute = [&](const uint4 (&q)[4], const uint32_t (&sd)[4], int kc, int buf) {
+    uint32_t dw[4];
+    if constexpr (kLdsScales) {
+      const uint4 d = *reinterpret_cast<const uint4*>(my_scales + (kc * 16 + r16) * 4);
+      dw[0] = d.x; dw[1] = d.y; dw[2] = d.z; dw[3] = d.w;
+    } else {
+#pragma unroll
+      for (int f = 0; f < 4; ++f) dw[f] = sd[f];
+    }
+    float scl[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) scl[f] = e8m0_as_f32((dw[f] >> (8 * g)) & 0xFFu);
+    const uint32_t w[4][4] = {{q[0].x, q[0].y, q[0].z, q[0].w},
+                              {q[1].x, q[1].y, q[1].z, q[1].w},
+                              {q[2].x, q[2].y, q[2].z, q[2].w},
+                              {q[3].x, q[3].y, q[3].z, q[3].w}};
+    const unsigned char* abase = a_lds + buf * kABuf + r16 * kARowBytes + 64 * g;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      bf16x8 b[4];
+#pragma unroll
+      for (int f = 0; f < 4; ++f) b[f] = dequant8(w[f][s], scl[f]);
+      // every subtile, also those past the tile's rows (they hold zeros): a branch
+      // here would cut the MFMA stream into blocks that each wait on one LDS read
+#pragma unroll
+      for (int mi = 0; mi < kMSub; ++mi) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(abase + mi * 16 * kARowBytes + 16 * s);
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+          acc[mi][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[f], acc[mi][f], 0, 0, 0);
+      }
+    }
+  };
+
+  const int last = n_chunks - 1;
+  uint4 q0[4], q1[4];
+  uint32_t s0[4], s1[4];
+  int kc = 0;
+  if constexpr (kMSub == 4) {
+    // activations two chunks ahead in registers (ra0/ra1), one chunk ahead in LDS
+    uint4 ra0[kPieces], ra1[kPieces];
+    load_a(ra0, 0);
+    load_w(q0, s0, 0);
+    load_w(q1, s1, last >= 1 ? 1 : 0);
+    load_a(ra1, last >= 1 ? 1 : 0);
+    store_a(ra0, 0);
+    __syncthreads();
+    for (; kc + 2 <= n_chunks; kc += 2) {
+      load_a(ra0, kc + 2 <= last ? kc + 2 : last);
+      compute(q0, s0, kc, 0);
+      load_w(q0, s0, kc + 2 <= last ? kc + 2 : last);
+      store_a(ra1, 1);
+      __syncthreads();
+      load_a(ra1, kc + 3 <= last ? kc + 3 : last);
+      compute(q1, s1, kc + 1, 1);
+      load_w(q1, s1, kc + 3 <= last ? kc + 3 : last);
+      store_a(ra0, 0);
+      __syncthreads();
+    }
+  } else {
+    // activations one chunk ahead (registers ra, then LDS)
+    uint4 ra[kPieces];
+    load_a(ra, 0);
+    load_w(q0, s0, 0);
+    load_w(q1, s1, last >= 1 ? 1 : 0);
+    store_a(ra, 0);
+    __syncthreads();
+    for (; kc + 2 <= n_chunks; kc += 2) {
+      load_a(ra, kc + 1);
+      compute(q0, s0, kc, 0);
+      load_w(q0, s0, kc + 2 <= last ? kc + 2 : last);
+      store_a(ra, 1);
+      __syncthreads();
+      load_a(ra, kc + 2 <= last ? kc + 2 : last);
+      compute(q1, s1, kc + 1, 1);
+      load_w(q1, s1, kc + 3 <= last ? kc + 3 : last);
+      store_a(ra, 0);
+      __syncthreads();
+    }
+  }
+  if (kc < n_chunks) compute(q0, s0, kc, 0);   // odd chunk count: last chunk in buffer 0 / q0
+
+  if (!store_cols) return;
+  const bool do_clamp = clamp != 0;
+#pragma unroll
+  for (int mi = 0; mi < kMSub; ++mi) {
+    if (mi >= msub) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int p = rt.p_begin + mi * 16 + 4 * g + i;
+      if (p >= rt.p_end) continue;
+      uint16_t* orow = out + static_cast<int64_t>(p) * ld_out;
+      if (kW1) {
+        orow[nrow[0]] = f32_to_bf16_bits(swiglu(acc[mi][0][i], acc[mi][2][i], limit, do_clamp));
+        orow[nrow[1]] = f32_to_bf16_bits(swiglu(acc[mi][1][i], acc[mi][3][i], limit, do_clamp));
+      } else {
+#pragma unroll
+        for (int f = 0; f < 4; ++f) orow[nrow[f]] = f32_to_bf16_bits(acc[mi][f][i]);
+      }
+    }
+  }
+}
+
+template <bool kW1, int kMSub>
+hipError_t launch_tile_t(int64_t tile_bound, hipStream_t stream, const uint16_t* act,
+                       uint32_t act_bytes, const int32_t* gather, int k_top, int n_slots,
+                       const uint8_t* wq, const uint8_t* wsc, const RowTile* tiles,
+                       const int32_t* n_tiles, int K, int n_rows, int half, int wpt, float limit,
+                       int clamp, uint16_t* out, int ld_out) {
+  const int bpt = (wpt + 3) / 4;
+  size_t lds = 2 * static_cast<size_t>(a_buf_bytes<kMSub>());
+  if (kMSub == 4) lds += static_cast<size_t>(4) * (K / kFfnKChunk) * 64 * sizeof(uint32_t);
+  // the column-block/XCD split covers row tiles in pairs: round up to whole pairs
+  const int64_t blocks = bpt == 16 ? (tile_bound + 1) / 2 * 2 * bpt : tile_bound * bpt;
+  gemm_tile_kernel<kW1, kMSub><<<static_cast<unsigned>(blocks), 256, lds, stream>>>(
+      act, act_bytes, gather, k_top, n_slots, wq, wsc, tiles, n_tiles, K, n_rows, half, wpt, bpt,
+      limit, clamp, out, ld_out);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_tile(bool w1, int64_t tile_bound, hipStream_t stream, const uint16_t* act,
+                       uint32_t act_bytes, const int32_t* gather, int k_top, int n_slots,
+                       const uint8_t* wq, const uint8_t* wsc, const RowTile* tiles,
+                       const int32_t* n_tiles, int K, int n_rows, int half, int wpt, float limit,
+                       int clamp, uint16_t* out, int ld_out) {
+  return w1 ? launch_tile_t<true, 4>(tile_bound, stream, act, act_bytes, gather, k_top, n_slots, wq,
+                                     wsc, tiles, n_tiles, K, n_rows, half, wpt, limit, clamp, out,
+                                     ld_out)
+            : launch_tile_t<false, 4>(tile_bound, stream, act, act_bytes, gather, k_top, n_slots,
+                                      wq, wsc, tiles, n_tiles, K, n_rows, half, wpt, limit, clamp,
+                                      out, ld_out);
+}
+
+}  // namespace moe
