@@ -133,6 +133,9 @@ def test_workload0_whole_layer(limit):
     (1030, 48, 8, 128, 128, 6),      # crosses a 1024-token offsets block
     (33, 1024, 8, 128, 128, 7),      # maximum E and k
     (40, 8, 1, 128, 128, 8),         # k = 1
+    (400, 16, 4, 768, 512, 14),      # 256-K tiled GEMM: W1 3 chunks (odd), W2 2 chunks
+    (260, 8, 3, 512, 768, 15),       # 256-K tiled GEMM: W1 2 chunks, W2 3 chunks, ragged tiles
+    (300, 8, 2, 1536, 1024, 16),     # wide tiled GEMM: W1 6 chunks (one loop pass), W2 4 (tail)
 ])
 def test_ragged_shapes_whole_layer(T, E, k, H, I, seed):
     whole_layer_parity(tiny(T, E, k, H, I, seed), 10.0)
