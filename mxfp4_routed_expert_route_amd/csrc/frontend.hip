@@ -7,9 +7,9 @@
 //   2. the bit matrix is built in LDS: thread i owns entry i = t*k + j; the logical
 //      block is the T*k entries, and threads past it (padding) stay inactive
 //      (txtmix.com article, §3; aihot.vn README translation, "Định tuyến MXFP4");
-//   3. wavefront 0 (lane = token) takes the expert column masks of the T rows,
-//      scans their popcounts into counts and offsets, and writes each slot's row
-//      p = offsets[e] + rank of the token within e.
+//   3. every wavefront takes the column masks of 64 experts over the T rows
+//      (lane = token); wavefront 0 scans their popcounts into counts and offsets
+//      and writes each slot's row p = offsets[e] + rank of the token within e.
 // Larger batches run the three separate kernels.
 #include "config.h"
 #include "launch.h"
@@ -62,10 +62,12 @@ __global__ __launch_bounds__(1024) void frontend_small_kernel(
   __syncthreads();
   for (int i = threadIdx.x; i < T * words; i += blockDim.x) bm[i] = rows_lds[i];
 
-  // 3. counts, offsets, permutations (wavefront 0, lane = token)
+  // 3. expert column masks, 64 experts per wavefront (lane = token), then counts,
+  // offsets and permutations in wavefront 0
+  for (int w0 = 2 * wave; w0 < words; w0 += 2 * n_waves)
+    column_masks_64(rows_lds, lane, lane < T, E, words, lane, masks, w0);
+  __syncthreads();
   if (wave != 0) return;
-  wave_column_masks(rows_lds, 0, T, E, words, lane, masks);
-  wave_sync_lds();
   int c[EPL];
   int sum = 0;
 #pragma unroll

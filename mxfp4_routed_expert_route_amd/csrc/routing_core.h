@@ -97,6 +97,19 @@ __device__ __forceinline__ void collect_word(uint32_t word, uint32_t& lo, uint32
   }
 }
 
+// masks[e] for the 64 experts of bit-matrix words w0, w0+1, for the token of this
+// lane (t, valid = t < T).
+__device__ __forceinline__ void column_masks_64(const uint32_t* bm, int64_t t, bool valid, int E,
+                                                int words, int lane, uint64_t* masks, int w0) {
+  const uint32_t word0 = valid ? bm[t * words + w0] : 0u;
+  const uint32_t word1 = (valid && w0 + 1 < words) ? bm[t * words + w0 + 1] : 0u;
+  uint32_t lo = 0u, hi = 0u;
+  collect_word<0>(word0, lo, hi);
+  collect_word<32>(word1, lo, hi);
+  const int e = w0 * 32 + lane;
+  if (e < E) masks[e] = (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
 // masks[e] <- column mask of expert e over rows[t0 .. t0+63] (rows past T are empty).
 // `bm` points at row 0 of a [T][words] bit matrix (global or LDS).
 __device__ __forceinline__ void wave_column_masks(const uint32_t* bm, int64_t t0, int64_t T, int E,
@@ -107,15 +120,7 @@ __device__ __forceinline__ void wave_column_masks(const uint32_t* bm, int64_t t0
     for (int e = lane; e < E; e += 64) masks[e] = 0ull;
     return;
   }
-  for (int w0 = 0; w0 < words; w0 += 2) {
-    const uint32_t word0 = valid ? bm[t * words + w0] : 0u;
-    const uint32_t word1 = (valid && w0 + 1 < words) ? bm[t * words + w0 + 1] : 0u;
-    uint32_t lo = 0u, hi = 0u;
-    collect_word<0>(word0, lo, hi);
-    collect_word<32>(word1, lo, hi);
-    const int e = w0 * 32 + lane;
-    if (e < E) masks[e] = (static_cast<uint64_t>(hi) << 32) | lo;
-  }
+  for (int w0 = 0; w0 < words; w0 += 2) column_masks_64(bm, t, valid, E, words, lane, masks, w0);
 }
 
 // Exclusive scan of one value per thread over the workgroup (blockDim.x <= 1024).

@@ -174,6 +174,14 @@ def test_one_expert_takes_every_token():
     whole_layer_parity(inp, None)
 
 
+def test_streaming_path_expert_spanning_several_tiles():
+    # 3.1 rows per expert on average -> 32-row streaming tiles; expert 5 takes every
+    # token (100 rows = tiles of 32, 32, 32, 4), found by each wavefront's tile scan
+    inp = tiny(100, 64, 2, 256, 128, 17)
+    inp["logits"][:, 5] += 100.0
+    whole_layer_parity(inp, 10.0)
+
+
 def test_nan_and_extreme_scales():
     inp = tiny(24, 16, 3, 128, 128, 12)
     w1_s = inp["w1_s"].copy()
