@@ -128,6 +128,13 @@ def main():
     ap.add_argument("--separate-routing", action="store_true",
                     help="route with moe_route + moe_build_bitmatrix + moe_expert_offsets instead "
                          "of the fused moe_route_and_group (same outputs)")
+    ap.add_argument("--event-every", type=int, default=10,
+                    help="in the timed region, every n-th step runs the FFN call that records "
+                         "HIP events around W1 and W2 (an event costs GPU time, so the others "
+                         "run without)")
+    ap.add_argument("--graph-steps", type=int, default=200,
+                    help="after the timed region, replay the layer captured as HIP graphs this "
+                         "many times and report graph_us_per_layer (0: skip)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="instead of the layer, run a plain device-to-device copy of this many "
                          "MiB (--steps times): the reference for HBM traffic counters")
@@ -177,6 +184,8 @@ def main():
                        ("moe_route_and_group", [P, I64, I32, I32] + [P] * 8 + [SZ, P]),
                        ("moe_grouped_ffn_mxfp4_timed", [P, I64, I32, I32, I32, I32] + [P] * 7 +
                         [F, P, P, SZ, P, P]),
+                       ("moe_grouped_ffn_mxfp4", [P, I64, I32, I32, I32, I32] + [P] * 7 +
+                        [F, P, P, SZ, P]),
                        ("moe_combine", [P, P, P, I64, I32, I32, P, P])):
         getattr(lib, name).argtypes = argt
         getattr(lib, name).restype = ctypes.c_int
@@ -184,9 +193,9 @@ def main():
     ev_arrs = [(ctypes.c_void_p * 3)(*events[i * n_ev + 4:i * n_ev + 7]) for i in range(args.steps)]
     ev_null = (ctypes.c_void_p * 3)(*hip.create(3))
     S = P(sh)
-    calls = []
-    for d in copies:
-        calls.append(dict(
+
+    def marshal(d, S):
+        return dict(
             route=(ptr(d["logits"]), T, E, k, ptr(b.topk_ids), ptr(b.topk_weights), S),
             bitmatrix=(ptr(b.topk_ids), T, E, k, ptr(b.bitmatrix), S),
             offsets=(ptr(b.bitmatrix), ptr(b.topk_ids), T, E, k, ptr(b.counts), ptr(b.offsets),
@@ -197,19 +206,22 @@ def main():
             ffn=(ptr(d["x"]), T, H, I, E, k, ptr(d["w1"]), ptr(d["w1_s"]), ptr(d["w2"]),
                  ptr(d["w2_s"]), ptr(b.counts), ptr(b.offsets), ptr(b.gather), F(args.limit),
                  ptr(b.y_sorted), ptr(b.ws), b.ws.numel()),
-            combine=(ptr(b.y_sorted), ptr(b.topk_weights), ptr(b.scatter), T, H, k, ptr(b.y), S)))
+            combine=(ptr(b.y_sorted), ptr(b.topk_weights), ptr(b.scatter), T, H, k, ptr(b.y), S))
+
+    calls = [marshal(d, S) for d in copies]
     record = hip.rt.hipEventRecord
     f_route, f_bm, f_offs = lib.moe_route, lib.moe_build_bitmatrix, lib.moe_expert_offsets
     f_front, f_ffn, f_comb = lib.moe_route_and_group, lib.moe_grouped_ffn_mxfp4_timed, lib.moe_combine
+    f_ffn_plain = lib.moe_grouped_ffn_mxfp4
 
     def check(rc, name):
         if rc != 0:
             raise binding.MoeError(name, rc)
 
-    def step(i, evs=None, ffn_events=None):
+    def step(i, evs=None, ffn_events=None, c=None):
         """One layer.  evs: 8 events around every call (breakdown pass only);
-        ffn_events: the 3 events inside the FFN call (timed pass)."""
-        c = calls[i % len(calls)]
+        ffn_events: the 3 events inside the FFN call (None: the plain FFN call)."""
+        c = calls[i % len(calls)] if c is None else c
         if evs is not None:
             record(evs[0], S)
         if args.separate_routing:
@@ -227,27 +239,54 @@ def main():
                 record(evs[2], S)
         if evs is not None:
             record(evs[3], S)
-        check(f_ffn(*c["ffn"], ffn_events, S), "moe_grouped_ffn_mxfp4_timed")
+        if ffn_events is None:
+            check(f_ffn_plain(*c["ffn"], c["combine"][-1]), "moe_grouped_ffn_mxfp4")
+        else:
+            check(f_ffn(*c["ffn"], ffn_events, c["combine"][-1]), "moe_grouped_ffn_mxfp4_timed")
         check(f_comb(*c["combine"]), "moe_combine")
         if evs is not None:
             record(evs[7], S)
 
     print(f"[bench] warmup {args.warmup} steps", file=sys.stderr, flush=True)
     for i in range(args.warmup):
-        step(i, ffn_events=ev_null)
+        step(i, ffn_events=ev_null if i % 2 else None)
     torch.cuda.synchronize()
 
-    # Timed region: K steps; only the three events of the instrumented FFN call
-    # (plan | W1 | W2) are recorded inside it, on the library's stream.
+    # Timed region: K steps.  Every event_every-th step runs the instrumented FFN
+    # call, which records three events (plan | W1 | W2) on the library's stream;
+    # W1 and W2 durations are averaged over those steps.
+    every = max(1, args.event_every)
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
-    ffn_ev = [(ctypes.c_void_p * 3)(*hip.create(3)) for _ in range(args.steps)]
+    ffn_ev = [(ctypes.c_void_p * 3)(*hip.create(3)) for _ in range(0, args.steps, every)]
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, ffn_events=ffn_ev[i])
+        step(i, ffn_events=ffn_ev[i // every] if i % every == 0 else None)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     w1_ms = float(np.mean([hip.ms(e[0], e[1]) for e in ffn_ev]))
     w2_ms = float(np.mean([hip.ms(e[1], e[2]) for e in ffn_ev]))
+
+    # Graph pass (not the timed region): the layer captured once per weight copy as a
+    # HIP graph on a side stream, then replayed back to back.
+    graph_us = None
+    if args.graph_steps > 0:
+        gstream = torch.cuda.Stream()
+        gcalls = [marshal(d, P(gstream.cuda_stream)) for d in copies]
+        graphs = []
+        for gc in gcalls:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=gstream):
+                step(0, c=gc)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for i in range(min(args.warmup, 20)):
+            graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+        g0 = time.perf_counter()
+        for i in range(args.graph_steps):
+            graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+        graph_us = (time.perf_counter() - g0) * 1e6 / args.graph_steps
 
     # Breakdown pass (not timed as a whole): events around every call.
     n_bd = min(args.steps, 20)
@@ -294,6 +333,8 @@ def main():
                    "routing": "separate calls" if args.separate_routing else "moe_route_and_group"},
         "per_call_us": {n: float(v) * 1e3 for n, v in zip(names, avg_ms) if n != "-"},
         "per_call_note": "separate pass with events around every call (events add a few us each)",
+        "event_every": every,
+        "graph_us_per_layer": graph_us,
         "ffn_w1_us_timed": w1_ms * 1e3,
         "ffn_w2_us_timed": w2_ms * 1e3,
         "touched_experts": touched,
