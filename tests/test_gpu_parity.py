@@ -182,6 +182,33 @@ def test_streaming_path_expert_spanning_several_tiles():
     whole_layer_parity(inp, 10.0)
 
 
+def test_single_expert():
+    # E = 1, k = 1: every token routes to expert 0 with weight 1
+    whole_layer_parity(tiny(50, 1, 1, 128, 128, 18), 10.0)
+
+
+def test_every_token_picks_every_expert():
+    # k = E: the selection is a full sort of each row
+    whole_layer_parity(tiny(20, 4, 4, 128, 128, 19), 10.0, fused=True)
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_empty_batch(fused):
+    # T = 0: every call returns OK; counts and offsets come back zero, nothing else
+    # is written
+    layer = _layer()
+    E, k, H, I = 64, 6, 256, 128
+    inp = tiny(0, E, k, H, I, 20)
+    dev = layer.to_device(inp)
+    b = layer.LayerBuffers.allocate(0, E, k, H, I)
+    b.counts.fill_(-7)
+    b.offsets.fill_(-7)
+    layer.run_layer(dev, b, 10.0, fused=fused)
+    torch.cuda.synchronize()
+    assert (b.counts.cpu().numpy() == 0).all()
+    assert (b.offsets.cpu().numpy() == 0).all()
+
+
 def test_nan_and_extreme_scales():
     inp = tiny(24, 16, 3, 128, 128, 12)
     w1_s = inp["w1_s"].copy()
