@@ -143,9 +143,9 @@ moe_status moe_expert_offsets(const uint32_t* bitmatrix, const int32_t* topk_ids
  *
  *   x         bf16  [T][H]            16-byte aligned
  *   w1        uint8 [E][2I][H/2]      W1 codes; rows 0..I-1 gate, I..2I-1 up; 16-byte aligned
- *   w1_scale  uint8 [E][2I][H/32]     E8M0 scales of W1
+ *   w1_scale  uint8 [E][2I][H/32]     E8M0 scales of W1; 16-byte aligned
  *   w2        uint8 [E][H][I/2]       W2 codes; 16-byte aligned
- *   w2_scale  uint8 [E][H][I/32]      E8M0 scales of W2
+ *   w2_scale  uint8 [E][H][I/32]      E8M0 scales of W2; 16-byte aligned
  *   counts, offsets, gather           as written by moe_expert_offsets
  *   y_sorted  bf16  [T*k][H]          out; 16-byte aligned
  *   ws        workspace of at least moe_workspace_bytes(T, E, k, H, I) bytes,

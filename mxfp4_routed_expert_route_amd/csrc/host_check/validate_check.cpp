@@ -68,6 +68,8 @@ int main() {
   expect("ffn small ws", check_ffn(p, 16, 256, 128, 256, 6, p, p, p, p, p, p, p, p, p, F.ffn_bytes - 1), MOE_ERR_WORKSPACE_TOO_SMALL);
   expect("ffn x misaligned", check_ffn(p4, 16, 256, 128, 256, 6, p, p, p, p, p, p, p, p, p, F.ffn_bytes), MOE_ERR_MISALIGNED);
   expect("ffn w1 misaligned", check_ffn(p, 16, 256, 128, 256, 6, p4, p, p, p, p, p, p, p, p, F.ffn_bytes), MOE_ERR_MISALIGNED);
+  expect("ffn w1 scales misaligned", check_ffn(p, 16, 256, 128, 256, 6, p, p4, p, p, p, p, p, p, p, F.ffn_bytes), MOE_ERR_MISALIGNED);
+  expect("ffn w2 scales misaligned", check_ffn(p, 16, 256, 128, 256, 6, p, p, p, p4, p, p, p, p, p, F.ffn_bytes), MOE_ERR_MISALIGNED);
   expect("ffn null w2s", check_ffn(p, 16, 256, 128, 256, 6, p, p, p, nullptr, p, p, p, p, p, F.ffn_bytes), MOE_ERR_INVALID_ARGUMENT);
   expect("ffn T=0", check_ffn(nullptr, 0, 256, 128, 256, 6, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0), MOE_OK);
 

@@ -98,8 +98,9 @@ moe_status check_ffn(const void* x, int64_t T, int32_t H, int32_t I, int32_t E, 
   if (!activations_fit(T, k, H, I)) return MOE_ERR_UNSUPPORTED;
   if (!x || !w1 || !w1s || !w2 || !w2s || !counts || !offsets || !gather || !y_sorted || !ws)
     return MOE_ERR_INVALID_ARGUMENT;
-  if (!aligned(x, 16) || !aligned(w1, 16) || !aligned(w2, 16) || !aligned(y_sorted, 16) ||
-      !aligned(ws, 16) || !aligned(counts, 4) || !aligned(offsets, 4) || !aligned(gather, 4))
+  if (!aligned(x, 16) || !aligned(w1, 16) || !aligned(w1s, 16) || !aligned(w2, 16) ||
+      !aligned(w2s, 16) || !aligned(y_sorted, 16) || !aligned(ws, 16) || !aligned(counts, 4) ||
+      !aligned(offsets, 4) || !aligned(gather, 4))
     return MOE_ERR_MISALIGNED;
   WsLayout L;
   s = workspace_layout(T, E, k, H, I, &L);
