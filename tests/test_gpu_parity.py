@@ -175,11 +175,16 @@ def test_one_expert_takes_every_token():
 
 
 def test_streaming_path_expert_spanning_several_tiles():
-    # 3.1 rows per expert on average -> 32-row streaming tiles; expert 5 takes every
-    # token (100 rows = tiles of 32, 32, 32, 4), found by each wavefront's tile scan
+    # 3.1 rows per expert on average -> 16-row streaming tiles; expert 5 takes every
+    # token (100 rows = six tiles of 16 and one of 4)
     inp = tiny(100, 64, 2, 256, 128, 17)
     inp["logits"][:, 5] += 100.0
     whole_layer_parity(inp, 10.0)
+
+
+def test_streaming_path_32_row_tiles():
+    # 18.75 rows per expert on average -> 32-row streaming tiles (two 16-row subtiles)
+    whole_layer_parity(tiny(120, 32, 5, 256, 128, 21), 10.0)
 
 
 def test_single_expert():
