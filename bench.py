@@ -186,6 +186,8 @@ def main():
                         [F, P, P, SZ, P, P]),
                        ("moe_grouped_ffn_mxfp4", [P, I64, I32, I32, I32, I32] + [P] * 7 +
                         [F, P, P, SZ, P]),
+                       ("moe_forward_mxfp4", [P, P, I64, I32, I32, I32, I32, P, P, P, P, F] +
+                        [P] * 10 + [SZ, P]),
                        ("moe_combine", [P, P, P, I64, I32, I32, P, P])):
         getattr(lib, name).argtypes = argt
         getattr(lib, name).restype = ctypes.c_int
@@ -206,13 +208,18 @@ def main():
             ffn=(ptr(d["x"]), T, H, I, E, k, ptr(d["w1"]), ptr(d["w1_s"]), ptr(d["w2"]),
                  ptr(d["w2_s"]), ptr(b.counts), ptr(b.offsets), ptr(b.gather), F(args.limit),
                  ptr(b.y_sorted), ptr(b.ws), b.ws.numel()),
-            combine=(ptr(b.y_sorted), ptr(b.topk_weights), ptr(b.scatter), T, H, k, ptr(b.y), S))
+            combine=(ptr(b.y_sorted), ptr(b.topk_weights), ptr(b.scatter), T, H, k, ptr(b.y), S),
+            forward=(ptr(d["logits"]), ptr(d["x"]), T, H, I, E, k, ptr(d["w1"]), ptr(d["w1_s"]),
+                     ptr(d["w2"]), ptr(d["w2_s"]), F(args.limit), ptr(b.topk_ids),
+                     ptr(b.topk_weights), ptr(b.bitmatrix), ptr(b.counts), ptr(b.offsets),
+                     ptr(b.gather), ptr(b.scatter), ptr(b.y_sorted), ptr(b.y), ptr(b.ws),
+                     b.ws.numel(), S))
 
     calls = [marshal(d, S) for d in copies]
     record = hip.rt.hipEventRecord
     f_route, f_bm, f_offs = lib.moe_route, lib.moe_build_bitmatrix, lib.moe_expert_offsets
     f_front, f_ffn, f_comb = lib.moe_route_and_group, lib.moe_grouped_ffn_mxfp4_timed, lib.moe_combine
-    f_ffn_plain = lib.moe_grouped_ffn_mxfp4
+    f_ffn_plain, f_forward = lib.moe_grouped_ffn_mxfp4, lib.moe_forward_mxfp4
 
     def check(rc, name):
         if rc != 0:
@@ -220,8 +227,12 @@ def main():
 
     def step(i, evs=None, ffn_events=None, c=None):
         """One layer.  evs: 8 events around every call (breakdown pass only);
-        ffn_events: the 3 events inside the FFN call (None: the plain FFN call)."""
+        ffn_events: the 3 events inside the FFN call.  With neither (and the default
+        routing), the layer is one moe_forward_mxfp4 call."""
         c = calls[i % len(calls)] if c is None else c
+        if evs is None and ffn_events is None and not args.separate_routing:
+            check(f_forward(*c["forward"]), "moe_forward_mxfp4")
+            return
         if evs is not None:
             record(evs[0], S)
         if args.separate_routing:
@@ -330,7 +341,10 @@ def main():
                                f"seed {wl.index}",
                    "T": T, "E": E, "k": k, "H": H, "I": I, "swiglu_limit": args.limit,
                    "weight_copies": args.weight_copies, "parallelism": "single GPU",
-                   "routing": "separate calls" if args.separate_routing else "moe_route_and_group"},
+                   "calls": ("moe_route + moe_build_bitmatrix + moe_expert_offsets + "
+                             "moe_grouped_ffn_mxfp4 + moe_combine" if args.separate_routing else
+                             "moe_forward_mxfp4 (every event_every-th step: moe_route_and_group + "
+                             "moe_grouped_ffn_mxfp4_timed + moe_combine)")},
         "per_call_us": {n: float(v) * 1e3 for n, v in zip(names, avg_ms) if n != "-"},
         "per_call_note": "separate pass with events around every call (events add a few us each)",
         "event_every": every,

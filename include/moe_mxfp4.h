@@ -13,7 +13,8 @@
  *   moe_expert_offsets     -> counts, offsets, gather, scatter
  *   moe_grouped_ffn_mxfp4  -> y_sorted   (W1 gate|up, clamped SwiGLU, W2)
  *   moe_combine            -> y
- * moe_route_and_group runs the first three as one call (one launch for small T).
+ * moe_route_and_group runs the first three as one call (one launch for small T);
+ * moe_forward_mxfp4 runs all five.
  *
  * Conventions shared by every call
  *   - Every pointer argument is a DEVICE pointer (memory the GPU can read or
@@ -192,8 +193,26 @@ moe_status moe_route_and_group(const float* logits, int64_t T, int32_t E, int32_
                                int32_t* scatter, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * moe_forward_mxfp4 -- the whole layer in one call: exactly the outputs of
+ * moe_route_and_group, moe_grouped_ffn_mxfp4 and moe_combine on the same
+ * arguments (see those calls for each output's definition, layout, alignment
+ * and citation).  For T <= 64 the one-launch front-end also writes the FFN's
+ * row-tile plan, so the layer is four kernel launches instead of five.  ws is
+ * the workspace of those calls (moe_workspace_bytes).  T = 0 writes zeros to
+ * counts and offsets and nothing else.
+ */
+moe_status moe_forward_mxfp4(const float* logits, const uint16_t* x, int64_t T, int32_t H,
+                             int32_t I, int32_t E, int32_t k, const uint8_t* w1,
+                             const uint8_t* w1_scale, const uint8_t* w2, const uint8_t* w2_scale,
+                             float swiglu_limit, int32_t* topk_ids, float* topk_weights,
+                             uint32_t* bitmatrix, int32_t* counts, int32_t* offsets,
+                             int32_t* gather, int32_t* scatter, uint16_t* y_sorted, uint16_t* y,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Workspace bytes that moe_expert_offsets and moe_grouped_ffn_mxfp4 need for
- * these sizes (one buffer of this size serves both calls, used one at a time).
+ * these sizes (one buffer of this size serves both calls, used one at a time,
+ * and moe_route_and_group and moe_forward_mxfp4).
  * Returns 0 for invalid sizes.  Pure host function.
  */
 size_t moe_workspace_bytes(int64_t T, int32_t E, int32_t k, int32_t H, int32_t I);

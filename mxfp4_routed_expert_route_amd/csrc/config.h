@@ -28,6 +28,18 @@ inline int64_t ffn_tile_bound(int64_t n_slots, int E, int tile_rows) {
   return (n_slots < E ? n_slots : E) + n_slots / tile_rows;
 }
 
+// Rows per FFN row tile for T tokens, E experts, k experts per token.  A token
+// picks an expert at most once, so no expert has more than T rows.  Up to 16 rows
+// per expert on average: 16-row streaming tiles (an expert past 16 rows takes a
+// second tile, but the 16-row kernel keeps 12 wavefronts per CU against 8 for 32
+// rows: 3 % faster on the 512-token burst); up to 24: 32-row streaming tiles;
+// more: 64-row tiles of the LDS-tiled kernel.
+inline int ffn_tile_rows(int64_t T, int E, int k) {
+  const int64_t avg_rows = T * k / E;
+  if (T <= 16 || avg_rows <= 16) return 16;
+  return avg_rows <= 24 ? 32 : 64;
+}
+
 struct RowTile {
   int32_t expert;
   int32_t p_begin;

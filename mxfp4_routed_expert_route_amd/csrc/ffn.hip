@@ -64,7 +64,7 @@ hipError_t launch_ffn(const uint16_t* x, int64_t T, int H, int I, int E, int k,
                       const uint8_t* w2s, const int32_t* counts, const int32_t* offsets,
                       const int32_t* gather, float limit, uint16_t* y_sorted, void* ws,
                       size_t h_offset, size_t plan_offset, int64_t /*tile_bound_min_rows*/,
-                      hipStream_t stream, hipEvent_t const* events) {
+                      hipStream_t stream, hipEvent_t const* events, bool plan_ready) {
   const int64_t n_slots = T * k;
   uint16_t* h = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + h_offset);
   int32_t* n_tiles = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + plan_offset);
@@ -75,26 +75,19 @@ hipError_t launch_ffn(const uint16_t* x, int64_t T, int H, int I, int E, int k,
   const uint32_t x_bytes = static_cast<uint32_t>(T * H * 2);         // < 2^32 - 2^20 (host check)
   const uint32_t h_bytes = static_cast<uint32_t>(n_slots * I * 2);
 
-  // Path: a token picks an expert at most once, so no expert has more than T rows.
-  // Few rows per expert -> weight streaming with 16- or 32-row tiles; else 64-row tiles.
-  // Up to 16 rows per expert on average, 16-row tiles: an expert past 16 rows takes
-  // a second tile (its weights read twice), but the 16-row kernel keeps 12
-  // wavefronts per CU against 8 for 32 rows (measured 3 % faster on the 512-token
-  // burst, 12 rows per expert).
-  const int64_t avg_rows = n_slots / E;
-  int tile_rows;
-  if (T <= 16 || avg_rows <= 16)
-    tile_rows = 16;
-  else if (avg_rows <= 24)
-    tile_rows = 32;
-  else
-    tile_rows = 64;
+  // Few rows per expert -> weight streaming with 16- or 32-row tiles; else 64-row
+  // tiles (ffn_tile_rows).  The plan may already be in the workspace (written by
+  // the one-launch front-end of moe_forward_mxfp4 under the same rule).
+  const int tile_rows = ffn_tile_rows(T, E, k);
   const int64_t tile_bound = ffn_tile_bound(n_slots, E, tile_rows);
 
-  plan_kernel<<<1, 1024, 0, stream>>>(counts, offsets, E, tile_rows, n_slots, tile_bound, n_tiles,
-                                      tiles);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  hipError_t err = hipSuccess;
+  if (!plan_ready) {
+    plan_kernel<<<1, 1024, 0, stream>>>(counts, offsets, E, tile_rows, n_slots, tile_bound,
+                                        n_tiles, tiles);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
   if (events) {
     err = hipEventRecord(events[0], stream);
     if (err != hipSuccess) return err;

@@ -10,7 +10,9 @@
 //   3. every wavefront takes the column masks of 64 experts over the T rows
 //      (lane = token); wavefront 0 scans their popcounts into counts and offsets
 //      and writes each slot's row p = offsets[e] + rank of the token within e.
-// Larger batches run the three separate kernels.
+// With a plan buffer, wavefront 0 also writes the grouped FFN's row-tile plan
+// (moe_forward_mxfp4), which saves the FFN its plan launch.  Larger batches run
+// the three separate kernels.
 #include "config.h"
 #include "launch.h"
 #include "routing_core.h"
@@ -30,7 +32,8 @@ template <int EPL>
 __global__ __launch_bounds__(1024) void frontend_small_kernel(
     const float* __restrict__ logits, int T, int E, int k, int words, int32_t* __restrict__ ids,
     float* __restrict__ weights, uint32_t* __restrict__ bm, int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ gather, int32_t* __restrict__ scatter) {
+    int32_t* __restrict__ offsets, int32_t* __restrict__ gather, int32_t* __restrict__ scatter,
+    int tile_rows, int tile_bound, int32_t* __restrict__ n_tiles, RowTile* __restrict__ tiles) {
   __shared__ int ids_lds[kFrontMaxTokens * kMaxK];
   __shared__ uint32_t rows_lds[kFrontMaxTokens * (kMaxE / 32)];
   __shared__ uint64_t masks[kMaxE];
@@ -94,6 +97,37 @@ __global__ __launch_bounds__(1024) void frontend_small_kernel(
     run += c[i];
   }
   if (lane == 63) offsets[E] = incl;
+  if (tiles != nullptr) {
+    // the FFN's row-tile plan (same tiles and order as its plan kernel): expert e
+    // cut into ceil(count / tile_rows) tiles, experts in index order
+    int nt[EPL], tsum = 0;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      nt[i] = (c[i] + tile_rows - 1) / tile_rows;
+      tsum += nt[i];
+    }
+    int tincl = tsum;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(tincl, d, 64);
+      if (lane >= d) tincl += o;
+    }
+    int slot = tincl - tsum;
+    int off = incl - sum;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      for (int t = 0; t < nt[i] && slot < tile_bound; ++t, ++slot) {
+        RowTile rt;
+        rt.expert = lane * EPL + i;
+        rt.p_begin = off + t * tile_rows;
+        rt.p_end = (t + 1) * tile_rows < c[i] ? off + (t + 1) * tile_rows : off + c[i];
+        rt.pad = 0;
+        tiles[slot] = rt;
+      }
+      off += c[i];
+    }
+    if (lane == 63) *n_tiles = tincl < tile_bound ? tincl : tile_bound;
+  }
   wave_sync_lds();
   if (lane < T) {
     const uint64_t below = (1ull << lane) - 1ull;
@@ -113,7 +147,9 @@ __global__ __launch_bounds__(1024) void frontend_small_kernel(
 
 hipError_t launch_route_and_group(const float* logits, int64_t T, int E, int k, int32_t* ids,
                                   float* weights, uint32_t* bm, int32_t* counts, int32_t* offsets,
-                                  int32_t* gather, int32_t* scatter, void* ws, hipStream_t stream) {
+                                  int32_t* gather, int32_t* scatter, void* ws, hipStream_t stream,
+                                  const PlanOut* plan, bool* plan_written) {
+  if (plan_written) *plan_written = false;
   if (T > kFrontMaxTokens) {
     hipError_t err = launch_route(logits, T, E, k, ids, weights, stream);
     if (err != hipSuccess) return err;
@@ -124,22 +160,33 @@ hipError_t launch_route_and_group(const float* logits, int64_t T, int E, int k, 
   const int words = (E + 31) / 32;
   const int epl = (E + 63) / 64;
   const int t = static_cast<int>(T);
+  const int tile_rows = plan ? plan->tile_rows : 1;
+  const int tile_bound = plan ? static_cast<int>(plan->tile_bound) : 0;
+  int32_t* n_tiles = plan ? plan->n_tiles : nullptr;
+  RowTile* tiles = plan ? static_cast<RowTile*>(plan->tiles) : nullptr;
   if (epl <= 1)
     frontend_small_kernel<1><<<1, 1024, 0, stream>>>(logits, t, E, k, words, ids, weights, bm,
-                                                     counts, offsets, gather, scatter);
+                                                     counts, offsets, gather, scatter,
+                                                     tile_rows, tile_bound, n_tiles, tiles);
   else if (epl <= 2)
     frontend_small_kernel<2><<<1, 1024, 0, stream>>>(logits, t, E, k, words, ids, weights, bm,
-                                                     counts, offsets, gather, scatter);
+                                                     counts, offsets, gather, scatter,
+                                                     tile_rows, tile_bound, n_tiles, tiles);
   else if (epl <= 4)
     frontend_small_kernel<4><<<1, 1024, 0, stream>>>(logits, t, E, k, words, ids, weights, bm,
-                                                     counts, offsets, gather, scatter);
+                                                     counts, offsets, gather, scatter,
+                                                     tile_rows, tile_bound, n_tiles, tiles);
   else if (epl <= 8)
     frontend_small_kernel<8><<<1, 1024, 0, stream>>>(logits, t, E, k, words, ids, weights, bm,
-                                                     counts, offsets, gather, scatter);
+                                                     counts, offsets, gather, scatter,
+                                                     tile_rows, tile_bound, n_tiles, tiles);
   else
     frontend_small_kernel<16><<<1, 1024, 0, stream>>>(logits, t, E, k, words, ids, weights, bm,
-                                                      counts, offsets, gather, scatter);
-  return hipGetLastError();
+                                                      counts, offsets, gather, scatter,
+                                                      tile_rows, tile_bound, n_tiles, tiles);
+  const hipError_t err = hipGetLastError();
+  if (err == hipSuccess && plan_written) *plan_written = tiles != nullptr;
+  return err;
 }
 
 }  // namespace moe

@@ -22,11 +22,24 @@ hipError_t launch_ffn(const uint16_t* x, int64_t T, int H, int I, int E, int k,
                       const uint8_t* w2s, const int32_t* counts, const int32_t* offsets,
                       const int32_t* gather, float limit, uint16_t* y_sorted, void* ws,
                       size_t h_offset, size_t plan_offset, int64_t tile_bound,
-                      hipStream_t stream, hipEvent_t const* events = nullptr);
+                      hipStream_t stream, hipEvent_t const* events = nullptr,
+                      bool plan_ready = false);
 
+// Where the one-launch front-end also writes the FFN's row-tile plan (count, then
+// the tile list; see ffn.hip).
+struct PlanOut {
+  int tile_rows;
+  int64_t tile_bound;
+  int32_t* n_tiles;
+  void* tiles;   // RowTile[tile_bound]
+};
+
+// With plan != nullptr the one-launch path (T <= 64) also writes the FFN plan and
+// sets *plan_written; larger T runs the separate kernels and writes no plan.
 hipError_t launch_route_and_group(const float* logits, int64_t T, int E, int k, int32_t* ids,
                                   float* weights, uint32_t* bm, int32_t* counts, int32_t* offsets,
-                                  int32_t* gather, int32_t* scatter, void* ws, hipStream_t stream);
+                                  int32_t* gather, int32_t* scatter, void* ws, hipStream_t stream,
+                                  const PlanOut* plan = nullptr, bool* plan_written = nullptr);
 
 hipError_t launch_combine(const uint16_t* ys, const float* w, const int32_t* scatter, int64_t T,
                           int H, int k, uint16_t* y, hipStream_t stream);

@@ -94,6 +94,14 @@ def run_layer(dev: dict, b: LayerBuffers, limit: float, stream=None, fused: bool
     run_ffn(dev, b, limit, stream)
 
 
+def run_forward(dev: dict, b: LayerBuffers, limit: float, stream=None):
+    """The whole layer through the one-call entry point (same outputs as run_layer)."""
+    binding.moe_forward_mxfp4(dev["logits"], dev["x"], b.k, dev["w1"], dev["w1_s"], dev["w2"],
+                              dev["w2_s"], limit, b.topk_ids, b.topk_weights, b.bitmatrix,
+                              b.counts, b.offsets, b.gather, b.scatter, b.y_sorted, b.y, b.ws,
+                              stream)
+
+
 def bf16_tensor_to_f32(t: torch.Tensor) -> np.ndarray:
     """Exact bf16 -> fp32 on the host (for comparisons)."""
     return t.float().cpu().numpy()

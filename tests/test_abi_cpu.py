@@ -34,7 +34,7 @@ def test_header_declares_the_five_calls():
     names = declared_functions()
     for n in ("moe_route", "moe_build_bitmatrix", "moe_expert_offsets", "moe_route_and_group",
               "moe_grouped_ffn_mxfp4", "moe_combine", "moe_workspace_bytes", "moe_status_string",
-              "moe_grouped_ffn_mxfp4_timed"):
+              "moe_grouped_ffn_mxfp4_timed", "moe_forward_mxfp4"):
         assert n in names
 
 
@@ -76,3 +76,12 @@ def test_error_codes_through_the_abi(lib):
     assert lib.moe_workspace_bytes(8191, 256, 6, 4096, 2048) >= 49146 * 2048 * 2
     assert lib.moe_workspace_bytes(-1, 256, 6, 4096, 2048) == 0
     assert lib.moe_status_string(WS_SMALL) == b"MOE_ERR_WORKSPACE_TOO_SMALL"
+    lib.moe_forward_mxfp4.argtypes = [P, P, I64, I32, I32, I32, I32, P, P, P, P, ctypes.c_float] + \
+        [P] * 10 + [ctypes.c_size_t, P]
+    fwd = lambda T, H, I, E, k, ptrs, ws_bytes: lib.moe_forward_mxfp4(
+        *ptrs[:2], T, H, I, E, k, *ptrs[2:6], 10.0, *ptrs[6:16], ws_bytes, None)
+    nulls = [None] * 16   # logits, x, 4 weight buffers, 9 outputs, workspace
+    assert fwd(16, 4096, 2048, 256, 6, nulls, 0) == INVALID          # null pointers
+    assert fwd(16, 4100, 2048, 256, 6, nulls, 0) == INVALID          # nulls are checked first
+    assert fwd(-1, 4096, 2048, 256, 6, nulls, 0) == INVALID
+    assert fwd(16, 4096, 2048, 256, 9, nulls, 0) == UNSUPPORTED      # k > 8

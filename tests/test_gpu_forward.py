@@ -1,0 +1,85 @@
+"""moe_forward_mxfp4 (the whole layer in one call) against the separate calls.
+
+Every output must match the separate-call chain (moe_route_and_group,
+moe_grouped_ffn_mxfp4, moe_combine) bit for bit: the same kernels run, except
+that for T <= 64 the one-launch front-end also writes the FFN's row-tile plan in
+place of the FFN's plan kernel.  The cases cover each tile kind the plan can
+hold (16- and 32-row streaming tiles, 64-row LDS tiles) on both sides of the
+T = 64 front-end limit, and T = 0.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from mxfp4_routed_expert_route_amd import inputs
+from tests.test_gpu_parity import tiny
+
+pytestmark = pytest.mark.gpu
+
+OUTPUTS = ("topk_ids", "topk_weights", "bitmatrix", "counts", "offsets", "gather", "scatter",
+           "y_sorted", "y")
+
+
+def _bits(t):
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+def _compare(inp, limit=10.0):
+    from mxfp4_routed_expert_route_amd import binding, layer
+    binding.load()
+    wl = inp["workload"]
+    T = inp["logits"].shape[0]
+    print(f"[forward] T={T} E={wl.E} k={wl.k} H={wl.H} I={wl.I}", file=sys.stderr, flush=True)
+    dev = layer.to_device(inp)
+    a = layer.LayerBuffers.allocate(T, wl.E, wl.k, wl.H, wl.I)
+    b = layer.LayerBuffers.allocate(T, wl.E, wl.k, wl.H, wl.I)
+    for buf in (a, b):   # stale values must not leak into either result
+        for name in OUTPUTS:
+            _bits(getattr(buf, name)).fill_(-3)
+        buf.ws.fill_(0x5A)
+    layer.run_layer(dev, a, limit, fused=True)
+    layer.run_forward(dev, b, limit)
+    torch.cuda.synchronize()
+    for name in OUTPUTS:
+        assert torch.equal(_bits(getattr(a, name)), _bits(getattr(b, name))), name
+
+
+@pytest.mark.parametrize("index", [0, 1])
+def test_forward_matches_separate_calls_workloads(index):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    _compare(inputs.make_inputs(index))
+
+
+@pytest.mark.parametrize("T,E,k,H,I,seed", [
+    (1, 256, 6, 256, 128, 41),       # one token, 16-row tiles
+    (40, 8, 1, 128, 128, 42),        # 5 rows per expert: 16-row tiles, several per expert
+    (64, 24, 7, 256, 128, 43),       # 18.7 rows per expert: 32-row tiles, front-end plan
+    (64, 16, 8, 256, 256, 44),       # 32 rows per expert: 64-row LDS tiles, front-end plan
+    (65, 16, 8, 256, 256, 45),       # past the one-launch limit: plan kernel
+    (33, 1024, 8, 128, 128, 46),     # maximum E and k
+])
+def test_forward_matches_separate_calls(T, E, k, H, I, seed):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    _compare(tiny(T, E, k, H, I, seed))
+
+
+def test_forward_empty_batch():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from mxfp4_routed_expert_route_amd import binding, layer
+    binding.load()
+    inp = tiny(0, 64, 6, 256, 128, 47)
+    dev = layer.to_device(inp)
+    b = layer.LayerBuffers.allocate(0, 64, 6, 256, 128)
+    b.counts.fill_(-7)
+    b.offsets.fill_(-7)
+    layer.run_forward(dev, b, 10.0)
+    torch.cuda.synchronize()
+    assert (b.counts.cpu().numpy() == 0).all() and (b.offsets.cpu().numpy() == 0).all()

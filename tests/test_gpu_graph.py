@@ -28,10 +28,11 @@ def _bits(t):
 
 
 @pytest.mark.parametrize("index,fused", [
-    (0, False),   # tiny: separate routing calls, streaming FFN
-    (0, True),    # tiny: one-launch front-end
-    (1, True),    # decode verify, full size: streaming FFN
-    (3, True),    # prefill 2048, full size: three routing kernels, plan + tiled FFN
+    (0, False),       # tiny: separate routing calls, streaming FFN
+    (0, True),        # tiny: one-launch front-end
+    (1, True),        # decode verify, full size: streaming FFN
+    (1, "forward"),   # decode verify through moe_forward_mxfp4 (front-end writes the plan)
+    (3, True),        # prefill 2048, full size: three routing kernels, plan + tiled FFN
 ])
 def test_graph_replay_matches_eager(index, fused):
     if not torch.cuda.is_available():
@@ -45,7 +46,13 @@ def test_graph_replay_matches_eager(index, fused):
     other = dict(dev, logits=torch.flip(dev["logits"], dims=[1]).contiguous())
     b = layer.LayerBuffers.allocate(wl.T, wl.E, wl.k, wl.H, wl.I)
 
-    layer.run_layer(dev, b, 10.0, fused=fused)
+    def run(d, limit):
+        if fused == "forward":
+            layer.run_forward(d, b, limit)
+        else:
+            layer.run_layer(d, b, limit, fused=fused)
+
+    run(dev, 10.0)
     torch.cuda.synchronize()
     ref = {name: _bits(getattr(b, name)).clone() for name in OUTPUTS}
 
@@ -53,7 +60,7 @@ def test_graph_replay_matches_eager(index, fused):
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.graph(g, stream=side):
-        layer.run_layer(dev, b, 10.0, fused=fused)
+        run(dev, 10.0)
     torch.cuda.synchronize()
 
     for rep in range(3):
@@ -61,7 +68,7 @@ def test_graph_replay_matches_eager(index, fused):
         # other routing logits, synchronise
         for name in OUTPUTS:
             _bits(getattr(b, name)).fill_(-1)
-        layer.run_layer(other, b, 0.0, fused=fused)
+        run(other, 0.0)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
