@@ -31,12 +31,4 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
          (static_cast<uint32_t>(f32_to_bf16_bits(hi)) << 16);
 }
 
-// 64-lane butterfly helpers on 32-bit halves (ds_swizzle / DPP chosen by the compiler).
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
-  uint32_t lo = static_cast<uint32_t>(v), hi = static_cast<uint32_t>(v >> 32);
-  lo = __shfl_xor(lo, mask, 64);
-  hi = __shfl_xor(hi, mask, 64);
-  return (static_cast<uint64_t>(hi) << 32) | lo;
-}
-
 }  // namespace moe

@@ -14,8 +14,8 @@ namespace moe {
 // Each lane holds EPL logits (expert e = i*64 + lane, coalesced loads) as 64-bit
 // keys (order-preserving logit bits << 32 | ~e), so one unsigned max picks the
 // larger logit and, on a tie, the lower index.  k rounds of a wave-wide max
-// (butterfly) take the winners in order; the winner's key is retired in the lane
-// that holds it.  Lane j < k returns slot j's id and weight.
+// (wave_max_u64) take the winners in order; the winner's key is retired in the
+// lane that holds it.  Lane j < k returns slot j's id and weight.
 
 __device__ __forceinline__ uint32_t order_bits(float f) {
   uint32_t u = __float_as_uint(f);
@@ -25,6 +25,36 @@ __device__ __forceinline__ uint32_t order_bits(float f) {
 
 __device__ __forceinline__ float order_bits_to_f32(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// Wave-wide unsigned maximum through DPP (every lane active): prefix maxima
+// within each row of 16 lanes by row shifts of 1, 2, 4, 8, then row broadcasts of
+// lanes 15 and 31 carry them across rows, so lane 63 holds the maximum, returned as
+// a wave-uniform value.  Six VALU steps, against six LDS round trips for a
+// butterfly of lane shuffles.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v),
+                                                           kCtrl, kRowMask, 0xF, false));
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  uint32_t o;
+  o = dpp_u32<0x111, 0xF>(v); v = o > v ? o : v;   // row_shr:1
+  o = dpp_u32<0x112, 0xF>(v); v = o > v ? o : v;   // row_shr:2
+  o = dpp_u32<0x114, 0xF>(v); v = o > v ? o : v;   // row_shr:4
+  o = dpp_u32<0x118, 0xF>(v); v = o > v ? o : v;   // row_shr:8
+  o = dpp_u32<0x142, 0xA>(v); v = o > v ? o : v;   // row_bcast:15 into rows 1 and 3
+  o = dpp_u32<0x143, 0xC>(v); v = o > v ? o : v;   // row_bcast:31 into rows 2 and 3
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
+// 64-bit maximum: the largest high word, then the largest low word among the lanes
+// that hold it.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  const uint32_t hi = wave_max_u32(static_cast<uint32_t>(v >> 32));
+  const uint32_t lo = wave_max_u32(static_cast<uint32_t>(v >> 32) == hi ? static_cast<uint32_t>(v) : 0u);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
 }
 
 template <int EPL>
@@ -40,14 +70,10 @@ __device__ __forceinline__ void route_token(const float* __restrict__ row, int E
   my_id = 0;
   float my_logit = 0.f, top = 0.f;
   for (int j = 0; j < k; ++j) {
-    uint64_t best = key[0];
+    uint64_t mine = key[0];
 #pragma unroll
-    for (int i = 1; i < EPL; ++i) best = key[i] > best ? key[i] : best;
-#pragma unroll
-    for (int m = 32; m > 0; m >>= 1) {
-      const uint64_t o = shfl_xor_u64(best, m);
-      best = o > best ? o : best;
-    }
+    for (int i = 1; i < EPL; ++i) mine = key[i] > mine ? key[i] : mine;
+    const uint64_t best = wave_max_u64(mine);   // wave-uniform
 #pragma unroll
     for (int i = 0; i < EPL; ++i)
       if (key[i] == best) key[i] = 0ull;
@@ -61,7 +87,8 @@ __device__ __forceinline__ void route_token(const float* __restrict__ row, int E
   // softmax over the selection: fp32 exponentials, fp64 sum in j order
   const float ex = (lane < k) ? expf(my_logit - top) : 0.f;
   double sum = 0.0;
-  for (int j = 0; j < k; ++j) sum += static_cast<double>(__shfl(ex, j, 64));
+  for (int j = 0; j < k; ++j)   // lane j's exponential, read as a scalar
+    sum += static_cast<double>(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), j)));
   my_weight = static_cast<float>(static_cast<double>(ex) / sum);
 }
 
