@@ -135,6 +135,9 @@ def main():
     ap.add_argument("--graph-steps", type=int, default=200,
                     help="after the timed region, replay the layer captured as HIP graphs this "
                          "many times and report graph_us_per_layer (0: skip)")
+    ap.add_argument("--copy-marker-mib", type=int, default=1024,
+                    help="device-to-device copy timed after the layer, as the achievable-HBM "
+                         "marker of the same run (0: skip)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="instead of the layer, run a plain device-to-device copy of this many "
                          "MiB (--steps times): the reference for HBM traffic counters")
@@ -312,6 +315,22 @@ def main():
         ev = events[i * n_ev:(i + 1) * n_ev]
         per[i] = [hip.ms(ev[j], ev[j + 1]) for j in range(7)]
     avg_ms = per.mean(axis=0)
+    layer_ev_us = np.array([hip.ms(events[i * n_ev], events[i * n_ev + 7]) for i in range(n_bd)]) * 1e3
+
+    # Achievable-HBM marker of the same run: a plain device copy (read + write).
+    copy_gbs = None
+    if args.copy_marker_mib > 0:
+        n = args.copy_marker_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        c0 = time.perf_counter()
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        copy_gbs = 2 * n * 10 / (time.perf_counter() - c0) / 1e9
+        del src, dst
 
     counts = b.counts.cpu().numpy()
     touched = int((counts > 0).sum())
@@ -349,6 +368,8 @@ def main():
         "per_call_note": "separate pass with events around every call (events add a few us each)",
         "event_every": every,
         "graph_us_per_layer": graph_us,
+        "layer_us_with_events_p10_p50_p90": [float(np.percentile(layer_ev_us, q)) for q in (10, 50, 90)],
+        "hbm_copy_marker_gbs": copy_gbs,
         "ffn_w1_us_timed": w1_ms * 1e3,
         "ffn_w2_us_timed": w2_ms * 1e3,
         "touched_experts": touched,
