@@ -21,6 +21,9 @@ constexpr int kFfnKChunk = 128;
 // streaming path: LDS for the staged E8M0 scales of a workgroup (4 wavefronts x
 // 64 rows x K/32 bytes); above this the scales are read from memory
 constexpr size_t kStreamMaxScaleLds = 64 * 1024;
+// streaming path: row tiles whose activation rows (all of K) fit beside the
+// staged scales within this much LDS per workgroup (three per CU) keep them in LDS
+constexpr size_t kStreamMaxLds = 53 * 1024;
 
 // Upper bound on the row tiles of n_slots rows over E experts cut into tiles of
 // tile_rows rows: at most one partial tile per non-empty expert.

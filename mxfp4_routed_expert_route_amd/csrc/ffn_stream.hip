@@ -27,13 +27,15 @@ namespace {
 // lane the scales of its four rows; they never enter the vector-memory queue.
 // Otherwise (small K): 128-element chunks, one-chunk prefetch, scales from memory.
 template <bool kW1, int MSUB, bool kDeep>
-__global__ __launch_bounds__(256) void gemm_stream_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MSUB == 1 ? 3 : 2))) void gemm_stream_kernel(
     const uint16_t* __restrict__ act, uint32_t act_bytes, const int32_t* __restrict__ gather,
     int k_top, int n_slots, const uint8_t* __restrict__ wq, const uint8_t* __restrict__ wsc,
     const RowTile* __restrict__ tiles, const int32_t* __restrict__ n_tiles, int K, int n_rows,
     int half, int waves_per_tile, float limit, int clamp, uint16_t* __restrict__ out,
-    int ld_out) {
-  extern __shared__ uint32_t scale_lds[];   // kDeep: per wavefront [K/128][16][4] dwords
+    int ld_out, int a_lds_rows) {
+  // kDeep: per wavefront [K/128][16][4] dwords of scales; then, with a_lds_rows > 0,
+  // a_lds_rows activation rows of K bf16 and a 512-byte zero block
+  extern __shared__ uint32_t scale_lds[];
   const int lane = threadIdx.x & 63;
   const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int tile_id = gw / waves_per_tile;
@@ -63,6 +65,47 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
     aoff[mi] = valid ? row * static_cast<uint32_t>(K) * 2u + (kDeep ? 128u : 64u) * g
                      : kRsrcOutOfRange;
   }
+
+  // Row tiles of at most a_lds_rows rows (decode: mostly one or two): the four
+  // wavefronts share the tile (the host enables this only when the wavefronts per
+  // tile are a multiple of 4), so the workgroup stages its activation rows for all
+  // of K in LDS once and the K loop reads them there.  This drops the activation
+  // loads -- as many 16-byte loads per chunk as the weights, mostly of rows past
+  // the tile -- from the vector-memory queue.
+  const int nvalid = rt.p_end - rt.p_begin;
+  const bool small_a = kDeep && MSUB == 1 && a_lds_rows > 0 && nvalid <= a_lds_rows;
+  unsigned char* a_lds = reinterpret_cast<unsigned char*>(scale_lds + 4 * n_chunks * 64);
+  const int a_row_bytes = K * 2;
+  if (small_a) {   // uniform over the workgroup (one tile)
+    // the tile's rows, then the zero block at row a_lds_rows
+    const int row_pieces = nvalid * (a_row_bytes / 16);
+    for (int i = threadIdx.x; i < row_pieces + 32; i += 256) {
+      const bool is_row = i < row_pieces;
+      const int byte = is_row ? i * 16 : a_lds_rows * a_row_bytes + (i - row_pieces) * 16;
+      const int r = byte / a_row_bytes;
+      uint32_t off = kRsrcOutOfRange;
+      if (is_row) {
+        const int p = rt.p_begin + r;
+        if (kW1) {
+          const int slot = gather[p];
+          if (static_cast<unsigned>(slot) < static_cast<unsigned>(n_slots))
+            off = static_cast<uint32_t>(slot / k_top) * static_cast<uint32_t>(a_row_bytes) +
+                  static_cast<uint32_t>(byte - r * a_row_bytes);
+        } else {
+          off = static_cast<uint32_t>(p) * static_cast<uint32_t>(a_row_bytes) +
+                static_cast<uint32_t>(byte - r * a_row_bytes);
+        }
+      }
+      *reinterpret_cast<uint4*>(a_lds + byte) =
+          __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(arsrc, off, 0, 0));
+    }
+    __syncthreads();
+  }
+  // this lane's activation run in LDS: its row, or the zero block (which does
+  // not advance with the chunk)
+  const unsigned char* a_mine = r16 < nvalid ? a_lds + r16 * a_row_bytes + 128 * g
+                                             : a_lds + a_lds_rows * a_row_bytes + 128 * g;
+  const int a_step = r16 < nvalid ? 512 : 0;
 
   // weight row of fragment f for a lane whose MFMA column is c16
   auto wrow = [&](int f, int c16) {
@@ -173,6 +216,11 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
           a[mi][t] = __builtin_bit_cast(
               bf16x8, __builtin_amdgcn_raw_buffer_load_b128(arsrc, aoff[mi] + c2 * 512 + 16 * t, 0, 0));
     };
+    auto load_a2_lds = [&](bf16x8 (&a)[MSUB][8], int c2) {   // small_a (MSUB == 1)
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        a[0][t] = *reinterpret_cast<const bf16x8*>(a_mine + c2 * a_step + 16 * t);
+    };
     auto compute2 = [&](const uint4 (&q)[4][2], const bf16x8 (&a)[MSUB][8], int c2) {
       const uint4 d0 = *reinterpret_cast<const uint4*>(my_scales + ((c2 * 16 + r16) * 4) * 2);
       const uint4 d1 = *reinterpret_cast<const uint4*>(my_scales + ((c2 * 16 + r16) * 4) * 2 + 4);
@@ -200,6 +248,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
         }
       }
     };
+    auto run = [&](auto&& load_a) __attribute__((always_inline)) {
     uint4 q0[4][2], q1[4][2];
     load_w2(q0, 0);
     __builtin_amdgcn_sched_barrier(0);
@@ -207,7 +256,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
 #define MOE_STREAM_STEP(Q_NEXT, KQ, Q_CUR, KC) \
   {                                           \
     bf16x8 a[MSUB][8];                        \
-    load_a2(a, KC);                           \
+    load_a(a, KC);                              \
     __builtin_amdgcn_sched_barrier(0);        \
     load_w2(Q_NEXT, KQ);                      \
     __builtin_amdgcn_sched_barrier(0);        \
@@ -218,6 +267,11 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(
       MOE_STREAM_STEP(q0, c2 + 2 < n2 ? c2 + 2 : n2 - 1, q1, c2 + 1)
 #undef MOE_STREAM_STEP
     }
+    };
+    if (small_a)
+      run(load_a2_lds);
+    else
+      run(load_a2);
   } else {
     uint4 qa[4], qb[4];
     uint32_t sa[4], sb[4];
@@ -279,14 +333,22 @@ hipError_t launch_stream_t(unsigned grid, hipStream_t stream, const uint16_t* ac
                          int ld_out) {
   const int n_chunks = K / kFfnKChunk;
   const size_t lds = static_cast<size_t>(4) * n_chunks * 64 * sizeof(uint32_t);
+  // activation rows in LDS for row tiles that fit: one tile per workgroup, and
+  // room for three workgroups per CU (W1 at H = 4096: 2 rows; W2 at I = 2048: 9)
+  int a_rows = 0;
+  if (MSUB == 1 && wpt % 4 == 0 && lds + 512 < kStreamMaxLds) {
+    const size_t fit = (kStreamMaxLds - lds - 512) / (static_cast<size_t>(K) * 2);
+    a_rows = static_cast<int>(fit < 16 ? fit : 16);
+  }
+  const size_t a_bytes = a_rows > 0 ? static_cast<size_t>(a_rows) * K * 2 + 512 : 0;
   if (n_chunks % 4 == 0 && lds <= kStreamMaxScaleLds)
-    gemm_stream_kernel<kW1, MSUB, true><<<grid, 256, lds, stream>>>(
+    gemm_stream_kernel<kW1, MSUB, true><<<grid, 256, lds + a_bytes, stream>>>(
         act, act_bytes, gather, k_top, n_slots, wq, wsc, tiles, n_tiles, K, n_rows, half, wpt,
-        limit, clamp, out, ld_out);
+        limit, clamp, out, ld_out, a_rows);
   else
     gemm_stream_kernel<kW1, MSUB, false><<<grid, 256, 0, stream>>>(
         act, act_bytes, gather, k_top, n_slots, wq, wsc, tiles, n_tiles, K, n_rows, half, wpt,
-        limit, clamp, out, ld_out);
+        limit, clamp, out, ld_out, 0);
   return hipGetLastError();
 }
 
