@@ -32,7 +32,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MSUB == 1 ?
     int k_top, int n_slots, const uint8_t* __restrict__ wq, const uint8_t* __restrict__ wsc,
     const RowTile* __restrict__ tiles, const int32_t* __restrict__ n_tiles, int K, int n_rows,
     int half, int waves_per_tile, float limit, int clamp, uint16_t* __restrict__ out,
-    int ld_out, int a_lds_rows) {
+    int ld_out, int a_lds_rows, int a_ring) {
   // kDeep: per wavefront [K/128][16][4] dwords of scales; then, with a_lds_rows > 0,
   // a_lds_rows activation rows of K bf16 and a 512-byte zero block
   extern __shared__ uint32_t scale_lds[];
@@ -74,6 +74,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MSUB == 1 ?
   // the tile -- from the vector-memory queue.
   const int nvalid = rt.p_end - rt.p_begin;
   const bool small_a = kDeep && MSUB == 1 && a_lds_rows > 0 && nvalid <= a_lds_rows;
+  const bool ring = kDeep && MSUB == 1 && a_ring != 0 && !small_a;   // uniform (one tile)
   unsigned char* a_lds = reinterpret_cast<unsigned char*>(scale_lds + 4 * n_chunks * 64);
   const int a_row_bytes = K * 2;
   if (small_a) {   // uniform over the workgroup (one tile)
@@ -268,8 +269,74 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MSUB == 1 ?
 #undef MOE_STREAM_STEP
     }
     };
+    // Larger tiles with a_ring: the workgroup stages each 256-element activation
+    // chunk once (16 rows x 512 bytes, 16 threads per row, contiguous 16-byte
+    // pieces) into a two-slot LDS ring with rows padded to 528 bytes, one barrier
+    // per chunk; the chunk after next is in flight in registers meanwhile.
+    auto run_ring = [&]() __attribute__((always_inline)) {
+      constexpr int kRowPad = 528, kSlot = 16 * kRowPad;
+      const int sr = threadIdx.x >> 4, sp = threadIdx.x & 15;
+      uint32_t srow = kRsrcOutOfRange;
+      {
+        const int p = rt.p_begin + sr;
+        if (p < rt.p_end) {
+          if (kW1) {
+            const int slot = gather[p];
+            if (static_cast<unsigned>(slot) < static_cast<unsigned>(n_slots))
+              srow = static_cast<uint32_t>(slot / k_top) * static_cast<uint32_t>(K) * 2u;
+          } else {
+            srow = static_cast<uint32_t>(p) * static_cast<uint32_t>(K) * 2u;
+          }
+        }
+      }
+      auto stage_load = [&](uint4 (&r)[2], int c2) __attribute__((always_inline)) {
+        r[0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(arsrc, srow + 16 * sp, c2 * 512, 0));
+        r[1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(arsrc, srow + 256 + 16 * sp, c2 * 512, 0));
+      };
+      auto stage_store = [&](const uint4 (&r)[2], int slot) __attribute__((always_inline)) {
+        unsigned char* d = a_lds + slot * kSlot + sr * kRowPad + 16 * sp;
+        *reinterpret_cast<uint4*>(d) = r[0];
+        *reinterpret_cast<uint4*>(d + 256) = r[1];
+      };
+      const unsigned char* a_rd = a_lds + r16 * kRowPad + 128 * g;
+      auto read_a = [&](bf16x8 (&a)[MSUB][8], int c2) __attribute__((always_inline)) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+          a[0][t] = *reinterpret_cast<const bf16x8*>(a_rd + (c2 & 1) * kSlot + 16 * t);
+      };
+      uint4 sa[2];
+      uint4 q0[4][2], q1[4][2];
+      stage_load(sa, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      load_w2(q0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      stage_store(sa, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      stage_load(sa, n2 > 1 ? 1 : 0);
+      __syncthreads();
+      for (int c2 = 0; c2 < n2; c2 += 2) {
+#define MOE_RING_STEP(Q_NEXT, KQ, Q_CUR, KC)                  \
+  {                                                           \
+    load_w2(Q_NEXT, KQ);                                      \
+    __builtin_amdgcn_sched_barrier(0);                        \
+    bf16x8 a[MSUB][8];                                        \
+    read_a(a, KC);                                            \
+    compute2(Q_CUR, a, KC);                                   \
+    __builtin_amdgcn_sched_barrier(0);                        \
+    stage_store(sa, (KC + 1) & 1);                            \
+    __builtin_amdgcn_sched_barrier(0);                        \
+    stage_load(sa, KC + 2 < n2 ? KC + 2 : n2 - 1);            \
+    __syncthreads();                                          \
+  }
+        MOE_RING_STEP(q1, c2 + 1, q0, c2)
+        MOE_RING_STEP(q0, c2 + 2 < n2 ? c2 + 2 : n2 - 1, q1, c2 + 1)
+#undef MOE_RING_STEP
+      }
+    };
     if (small_a)
       run(load_a2_lds);
+    else if (ring)
+      run_ring();
     else
       run(load_a2);
   } else {
@@ -340,15 +407,18 @@ hipError_t launch_stream_t(unsigned grid, hipStream_t stream, const uint16_t* ac
     const size_t fit = (kStreamMaxLds - lds - 512) / (static_cast<size_t>(K) * 2);
     a_rows = static_cast<int>(fit < 16 ? fit : 16);
   }
-  const size_t a_bytes = a_rows > 0 ? static_cast<size_t>(a_rows) * K * 2 + 512 : 0;
+  size_t a_bytes = a_rows > 0 ? static_cast<size_t>(a_rows) * K * 2 + 512 : 0;
+  const size_t ring_bytes = 2 * 16 * 528;
+  const int a_ring = MSUB == 1 && wpt % 4 == 0 && lds + ring_bytes <= kStreamMaxLds ? 1 : 0;
+  if (a_ring && ring_bytes > a_bytes) a_bytes = ring_bytes;
   if (n_chunks % 4 == 0 && lds <= kStreamMaxScaleLds)
     gemm_stream_kernel<kW1, MSUB, true><<<grid, 256, lds + a_bytes, stream>>>(
         act, act_bytes, gather, k_top, n_slots, wq, wsc, tiles, n_tiles, K, n_rows, half, wpt,
-        limit, clamp, out, ld_out, a_rows);
+        limit, clamp, out, ld_out, a_rows, a_ring);
   else
     gemm_stream_kernel<kW1, MSUB, false><<<grid, 256, 0, stream>>>(
         act, act_bytes, gather, k_top, n_slots, wq, wsc, tiles, n_tiles, K, n_rows, half, wpt,
-        limit, clamp, out, ld_out, 0);
+        limit, clamp, out, ld_out, 0, 0);
   return hipGetLastError();
 }
 
