@@ -74,7 +74,9 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(
   const bool store_cols = cg_raw < waves_per_tile;
   const int cg = store_cols ? cg_raw : waves_per_tile - 1;
 
-  // --- activation staging: thread -> (row ar, part aq) of the chunk
+  // --- activation staging: thread -> (row ar, part aq) of the chunk; piece i of a
+  // thread is bytes 16*(aq + kThreadsPerRow*i) of the row's 256, so each load
+  // instruction reads contiguous 16*kThreadsPerRow bytes of every row
   const __amdgpu_buffer_rsrc_t arsrc = make_rsrc(act, act_bytes);
   const int ar = tid / kThreadsPerRow, aq = tid % kThreadsPerRow;
   uint32_t aoff;
@@ -91,20 +93,20 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(
         row = static_cast<uint32_t>(p);
       }
     }
-    aoff = valid ? row * static_cast<uint32_t>(K) * 2u + 16u * kPieces * aq : kRsrcOutOfRange;
+    aoff = valid ? row * static_cast<uint32_t>(K) * 2u + 16u * aq : kRsrcOutOfRange;
   }
   unsigned char* a_lds = tile_lds;                       // [2][kRows][kARowBytes]
-  const int a_store = ar * kARowBytes + aq * 16 * kPieces;
+  const int a_store = ar * kARowBytes + aq * 16;
   auto load_a = [&](uint4 (&ra)[kPieces], int kc) {
 #pragma unroll
     for (int i = 0; i < kPieces; ++i)
       ra[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                            arsrc, aoff + kc * 256 + 16 * i, 0, 0));
+                                            arsrc, aoff + kc * 256 + 16 * kThreadsPerRow * i, 0, 0));
   };
   auto store_a = [&](const uint4 (&ra)[kPieces], int buf) {
 #pragma unroll
     for (int i = 0; i < kPieces; ++i)
-      *reinterpret_cast<uint4*>(a_lds + buf * kABuf + a_store + 16 * i) = ra[i];
+      *reinterpret_cast<uint4*>(a_lds + buf * kABuf + a_store + 16 * kThreadsPerRow * i) = ra[i];
   };
 
   // --- weights: four fragments of 16 rows, this lane's row in each
