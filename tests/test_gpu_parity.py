@@ -187,6 +187,25 @@ def test_streaming_path_32_row_tiles():
     whole_layer_parity(tiny(120, 32, 5, 256, 128, 21), 10.0)
 
 
+@pytest.mark.parametrize("T,E,k,H,I,seed", [
+    # 12 rows per expert on average, skewed: 16-row tiles of 1 to 16 rows.  W1
+    # (K = 3072) keeps tiles of <= 4 rows in LDS for all of K and stages larger
+    # ones chunk by chunk through the LDS ring; W2 (K = 2048) keeps <= 9 rows.
+    (96, 16, 2, 3072, 2048, 22),
+    # W1 at K = 4096 keeps <= 2 rows (the decode setting); W2 at K = 1024 keeps
+    # every 16-row tile
+    (48, 32, 6, 4096, 1024, 23),
+    # H = 1152: 18 W2 wavefronts per tile, so a workgroup straddles tiles and W2
+    # loads its activations per wavefront (no LDS rows, no ring)
+    (64, 8, 2, 1152, 512, 24),
+    # 20 rows per expert on average: 32-row tiles (two 16-row subtiles) with the
+    # deep pipeline on both GEMMs (activations per wavefront)
+    (128, 32, 5, 1024, 512, 25),
+])
+def test_streaming_activation_paths(T, E, k, H, I, seed):
+    whole_layer_parity(tiny(T, E, k, H, I, seed, skew=True), 10.0)
+
+
 def test_single_expert():
     # E = 1, k = 1: every token routes to expert 0 with weight 1
     whole_layer_parity(tiny(50, 1, 1, 128, 128, 18), 10.0)
