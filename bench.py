@@ -70,7 +70,7 @@ class HipEvents:
 
 def ffn_kernel_name(T: int, E: int, k: int) -> str:
     """The W1 kernel the library picks for these sizes (its row-tile rule)."""
-    if T <= 16:
+    if T <= 16 or T * k // E <= 8:
         return "gemm_stream_kernel<true, 1, true>"
     if T * k // E <= 24:
         return "gemm_stream_kernel<true, 2, true>"

@@ -24,6 +24,8 @@ constexpr size_t kStreamMaxScaleLds = 64 * 1024;
 // streaming path: row tiles whose activation rows (all of K) fit beside the
 // staged scales within this much LDS per workgroup (three per CU) keep them in LDS
 constexpr size_t kStreamMaxLds = 53 * 1024;
+// the same with 32-row tiles (two workgroups per CU)
+constexpr size_t kStreamMaxLds2 = 80 * 1024;
 
 // Upper bound on the row tiles of n_slots rows over E experts cut into tiles of
 // tile_rows rows: at most one partial tile per non-empty expert.
@@ -32,14 +34,15 @@ inline int64_t ffn_tile_bound(int64_t n_slots, int E, int tile_rows) {
 }
 
 // Rows per FFN row tile for T tokens, E experts, k experts per token.  A token
-// picks an expert at most once, so no expert has more than T rows.  Up to 16 rows
-// per expert on average: 16-row streaming tiles (an expert past 16 rows takes a
-// second tile, but the 16-row kernel keeps 12 wavefronts per CU against 8 for 32
-// rows: 3 % faster on the 512-token burst); up to 24: 32-row streaming tiles;
-// more: 64-row tiles of the LDS-tiled kernel.
+// picks an expert at most once, so no expert has more than T rows.  Up to 8 rows
+// per expert on average: 16-row streaming tiles (decode: the tiles' rows fit in
+// LDS for all of K); up to 24: 32-row streaming tiles (measured on the 512-token
+// burst, 12 rows per expert: 671 us per layer against 715 with 16-row tiles,
+// whose experts past 16 rows read their weights twice); more: 64-row tiles of the
+// LDS-tiled kernel.
 inline int ffn_tile_rows(int64_t T, int E, int k) {
   const int64_t avg_rows = T * k / E;
-  if (T <= 16 || avg_rows <= 16) return 16;
+  if (T <= 16 || avg_rows <= 8) return 16;
   return avg_rows <= 24 ? 32 : 64;
 }
 

@@ -74,7 +74,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MSUB == 1 ?
   // the tile -- from the vector-memory queue.
   const int nvalid = rt.p_end - rt.p_begin;
   const bool small_a = kDeep && MSUB == 1 && a_lds_rows > 0 && nvalid <= a_lds_rows;
-  const bool ring = kDeep && MSUB == 1 && a_ring != 0 && !small_a;   // uniform (one tile)
+  const bool ring = kDeep && a_ring != 0 && !small_a;   // uniform (one tile)
   unsigned char* a_lds = reinterpret_cast<unsigned char*>(scale_lds + 4 * n_chunks * 64);
   const int a_row_bytes = K * 2;
   if (small_a) {   // uniform over the workgroup (one tile)
@@ -270,12 +270,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MSUB == 1 ?
     }
     };
     // Larger tiles with a_ring: the workgroup stages each 256-element activation
-    // chunk once (16 rows x 512 bytes, 16 threads per row, contiguous 16-byte
-    // pieces) into a two-slot LDS ring with rows padded to 528 bytes, one barrier
-    // per chunk; the chunk after next is in flight in registers meanwhile.
+    // chunk once (16*MSUB rows x 512 bytes; 16/MSUB threads per row, each load
+    // instruction reading 256/MSUB contiguous bytes of every row) into a two-slot
+    // LDS ring with rows padded to 528 bytes, one barrier per chunk; the chunk
+    // after next is in flight in registers meanwhile.
     auto run_ring = [&]() __attribute__((always_inline)) {
-      constexpr int kRowPad = 528, kSlot = 16 * kRowPad;
-      const int sr = threadIdx.x >> 4, sp = threadIdx.x & 15;
+      constexpr int kRowPad = 528, kSlot = 16 * MSUB * kRowPad;
+      constexpr int kTpr = 16 / MSUB, kPc = 2 * MSUB;   // threads per row, pieces per thread
+      const int sr = threadIdx.x / kTpr, sp = threadIdx.x % kTpr;
       uint32_t srow = kRsrcOutOfRange;
       {
         const int p = rt.p_begin + sr;
@@ -289,22 +291,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MSUB == 1 ?
           }
         }
       }
-      auto stage_load = [&](uint4 (&r)[2], int c2) __attribute__((always_inline)) {
-        r[0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(arsrc, srow + 16 * sp, c2 * 512, 0));
-        r[1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(arsrc, srow + 256 + 16 * sp, c2 * 512, 0));
+      auto stage_load = [&](uint4 (&r)[kPc], int c2) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < kPc; ++i)
+          r[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                               arsrc, srow + 16 * (sp + kTpr * i), c2 * 512, 0));
       };
-      auto stage_store = [&](const uint4 (&r)[2], int slot) __attribute__((always_inline)) {
+      auto stage_store = [&](const uint4 (&r)[kPc], int slot) __attribute__((always_inline)) {
         unsigned char* d = a_lds + slot * kSlot + sr * kRowPad + 16 * sp;
-        *reinterpret_cast<uint4*>(d) = r[0];
-        *reinterpret_cast<uint4*>(d + 256) = r[1];
+#pragma unroll
+        for (int i = 0; i < kPc; ++i) *reinterpret_cast<uint4*>(d + 16 * kTpr * i) = r[i];
       };
       const unsigned char* a_rd = a_lds + r16 * kRowPad + 128 * g;
       auto read_a = [&](bf16x8 (&a)[MSUB][8], int c2) __attribute__((always_inline)) {
 #pragma unroll
-        for (int t = 0; t < 8; ++t)
-          a[0][t] = *reinterpret_cast<const bf16x8*>(a_rd + (c2 & 1) * kSlot + 16 * t);
+        for (int mi = 0; mi < MSUB; ++mi)
+#pragma unroll
+          for (int t = 0; t < 8; ++t)
+            a[mi][t] = *reinterpret_cast<const bf16x8*>(a_rd + mi * 16 * kRowPad + (c2 & 1) * kSlot +
+                                                        16 * t);
       };
-      uint4 sa[2];
+      uint4 sa[kPc];
       uint4 q0[4][2], q1[4][2];
       stage_load(sa, 0);
       __builtin_amdgcn_sched_barrier(0);
@@ -408,8 +415,11 @@ hipError_t launch_stream_t(unsigned grid, hipStream_t stream, const uint16_t* ac
     a_rows = static_cast<int>(fit < 16 ? fit : 16);
   }
   size_t a_bytes = a_rows > 0 ? static_cast<size_t>(a_rows) * K * 2 + 512 : 0;
-  const size_t ring_bytes = 2 * 16 * 528;
-  const int a_ring = MSUB == 1 && wpt % 4 == 0 && lds + ring_bytes <= kStreamMaxLds ? 1 : 0;
+  // the ring: two chunks of 16*MSUB padded rows, within the workgroup's share of
+  // LDS (three workgroups per CU with 16-row tiles, two with 32-row tiles)
+  const size_t ring_bytes = 2 * 16 * MSUB * 528;
+  const size_t budget = MSUB == 1 ? kStreamMaxLds : kStreamMaxLds2;
+  const int a_ring = wpt % 4 == 0 && lds + ring_bytes <= budget ? 1 : 0;
   if (a_ring && ring_bytes > a_bytes) a_bytes = ring_bytes;
   if (n_chunks % 4 == 0 && lds <= kStreamMaxScaleLds)
     gemm_stream_kernel<kW1, MSUB, true><<<grid, 256, lds + a_bytes, stream>>>(

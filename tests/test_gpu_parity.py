@@ -188,13 +188,16 @@ def test_streaming_path_32_row_tiles():
 
 
 @pytest.mark.parametrize("T,E,k,H,I,seed", [
-    # 12 rows per expert on average, skewed: 16-row tiles of 1 to 16 rows.  W1
+    # 8 rows per expert on average, skewed: 16-row tiles of 1 to 16 rows.  W1
     # (K = 3072) keeps tiles of <= 4 rows in LDS for all of K and stages larger
     # ones chunk by chunk through the LDS ring; W2 (K = 2048) keeps <= 9 rows.
-    (96, 16, 2, 3072, 2048, 22),
+    (64, 16, 2, 3072, 2048, 22),
     # W1 at K = 4096 keeps <= 2 rows (the decode setting); W2 at K = 1024 keeps
     # every 16-row tile
-    (48, 32, 6, 4096, 1024, 23),
+    (40, 32, 6, 4096, 1024, 23),
+    # 12 rows per expert on average (the burst setting): 32-row tiles through the
+    # LDS ring, W1 at K = 4096
+    (96, 16, 2, 4096, 1024, 26),
     # H = 1152: 18 W2 wavefronts per tile, so a workgroup straddles tiles and W2
     # loads its activations per wavefront (no LDS rows, no ring)
     (64, 8, 2, 1152, 512, 24),
