@@ -129,17 +129,15 @@ __global__ __launch_bounds__(1024) void frontend_small_kernel(
     if (lane == 63) *n_tiles = tincl < tile_bound ? tincl : tile_bound;
   }
   wave_sync_lds();
-  if (lane < T) {
-    const uint64_t below = (1ull << lane) - 1ull;
-    for (int j = 0; j < k; ++j) {
-      const int s = lane * k + j;
-      const int e = ids_lds[s];
-      if (static_cast<unsigned>(e) >= static_cast<unsigned>(E)) continue;
-      const int p = off_lds[e] + __popcll(masks[e] & below);
-      if (p < 0 || p >= n_entries) continue;
-      gather[p] = s;
-      scatter[s] = p;
-    }
+  // one lane per (token, choice) entry: its row is the expert's offset plus the
+  // earlier tokens that chose the same expert (bits below the token in its mask)
+  for (int s = lane; s < n_entries; s += 64) {
+    const int e = ids_lds[s];
+    if (static_cast<unsigned>(e) >= static_cast<unsigned>(E)) continue;
+    const int p = off_lds[e] + __popcll(masks[e] & ((1ull << (s / k)) - 1ull));
+    if (p < 0 || p >= n_entries) continue;
+    gather[p] = s;
+    scatter[s] = p;
   }
 }
 
