@@ -6,35 +6,44 @@ namespace {
 
 // ---------------------------------------------------------------- streaming GEMM (few rows)
 //
-// For row tiles of at most 16*MSUB rows (decode-shaped batches, where each
-// expert has a handful of rows and the weights are read once): one wavefront
-// owns a row tile and 64 weight rows (W1: 32 gate rows and the 32 matching up
-// rows; W2: 64 output rows) and needs no barrier, so many wavefronts stay
-// resident per CU.
+// For row tiles of at most 16*MSUB rows (decode and small batches, where each
+// expert has few rows and the weights are read once): one wavefront owns a row
+// tile and 64 weight rows (W1: 32 gate rows and the 32 matching up rows; W2: 64
+// output rows), so many wavefronts stay resident per CU.
 //
 // Memory pipeline (kDeep, K a multiple of 512).  K advances in chunks of 256
 // elements: each lane takes 32 bytes (two scale blocks) of each of its four rows,
 // so a weight row is visited 128 bytes at a time -- measured on MI355X, 128-byte
 // visits of this many concurrent rows stream about 20% faster than 64-byte ones.
-// Vector-memory loads retire in issue order and a wait is a count of loads still
-// allowed in flight, so the issue order decides what a wait drains: per chunk the
-// loop issues the chunk's activations, then the next chunk's weights, then
-// computes; the wait for the activations leaves the weight prefetch in flight.
+// Two register stages of weights: the next chunk streams in while this one
+// computes.  The E8M0 scales of the wavefront's 64 rows are staged in LDS once,
+// laid out so that two 16-byte LDS reads per chunk give a lane the scales of its
+// four rows; they never enter the vector-memory queue.  Activations take one of
+// three routes (the host enables the first two only when the four wavefronts of
+// a workgroup share one tile):
+//   * rows in LDS: a tile whose rows fit beside the scales is staged once, for
+//     all of K, behind one workgroup barrier (decode: one or two rows);
+//   * ring: larger tiles are staged chunk by chunk, once per workgroup, through
+//     a two-slot LDS ring with one barrier per chunk;
+//   * per wavefront: each wavefront loads its chunk's activations itself, issued
+//     before the weight prefetch, so waiting for them leaves the prefetch in
+//     flight (vector-memory loads retire in issue order).
 // Every load in the loop is unconditional (rows past the tile read zeros through
 // a bounded buffer resource; the last prefetch re-reads the last chunk), which
-// keeps those wait counts exact.  The E8M0 scales of the wavefront's 64 rows are
-// staged in LDS once, laid out so that two 16-byte LDS reads per chunk give a
-// lane the scales of its four rows; they never enter the vector-memory queue.
+// keeps the compiler's wait counts exact.
 // Otherwise (small K): 128-element chunks, one-chunk prefetch, scales from memory.
+// Three wavefronts per SIMD (12 per CU) with 16-row tiles, two with 32-row tiles.
 template <bool kW1, int MSUB, bool kDeep>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MSUB == 1 ? 3 : 2))) void gemm_stream_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MSUB == 1 ? 3 : 2)))
+void gemm_stream_kernel(
     const uint16_t* __restrict__ act, uint32_t act_bytes, const int32_t* __restrict__ gather,
     int k_top, int n_slots, const uint8_t* __restrict__ wq, const uint8_t* __restrict__ wsc,
     const RowTile* __restrict__ tiles, const int32_t* __restrict__ n_tiles, int K, int n_rows,
     int half, int waves_per_tile, float limit, int clamp, uint16_t* __restrict__ out,
     int ld_out, int a_lds_rows, int a_ring) {
-  // kDeep: per wavefront [K/128][16][4] dwords of scales; then, with a_lds_rows > 0,
-  // a_lds_rows activation rows of K bf16 and a 512-byte zero block
+  // kDeep: per wavefront [K/128][16][4] dwords of scales; after the four
+  // wavefronts' scales, either a_lds_rows activation rows of K bf16 and a
+  // 512-byte zero block, or the ring (two slots of 16*MSUB rows of 528 bytes)
   extern __shared__ uint32_t scale_lds[];
   const int lane = threadIdx.x & 63;
   const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -194,12 +203,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MSUB == 1 ?
   };
 
   if constexpr (kDeep) {
-    // 256-element chunks: each lane takes 32 bytes (two scale blocks) of each of its
-    // four rows, so a row is visited 128 bytes at a time (about 20% more HBM
-    // throughput than 64-byte visits for this many concurrent rows).  Weights:
-    // two register stages (the next chunk streams in while this one computes).
-    // Activations: loaded for the current chunk, issued before the weight
-    // prefetch, so waiting for them leaves the prefetch in flight.
+    // 256-element chunks, two weight register stages; `run` is the K loop for the
+    // LDS-held rows and the per-wavefront activation loads, `run_ring` for the ring.
     const int n2 = n_chunks / 2;   // 256-element chunks (even: n_chunks % 4 == 0)
     auto load_w2 = [&](uint4 (&q)[4][2], int c2) {
 #pragma unroll
@@ -250,24 +255,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MSUB == 1 ?
       }
     };
     auto run = [&](auto&& load_a) __attribute__((always_inline)) {
-    uint4 q0[4][2], q1[4][2];
-    load_w2(q0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    for (int c2 = 0; c2 < n2; c2 += 2) {
+      uint4 q0[4][2], q1[4][2];
+      load_w2(q0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      for (int c2 = 0; c2 < n2; c2 += 2) {
 #define MOE_STREAM_STEP(Q_NEXT, KQ, Q_CUR, KC) \
   {                                           \
     bf16x8 a[MSUB][8];                        \
-    load_a(a, KC);                              \
+    load_a(a, KC);                            \
     __builtin_amdgcn_sched_barrier(0);        \
     load_w2(Q_NEXT, KQ);                      \
     __builtin_amdgcn_sched_barrier(0);        \
     compute2(Q_CUR, a, KC);                   \
     __builtin_amdgcn_sched_barrier(0);        \
   }
-      MOE_STREAM_STEP(q1, c2 + 1, q0, c2)
-      MOE_STREAM_STEP(q0, c2 + 2 < n2 ? c2 + 2 : n2 - 1, q1, c2 + 1)
+        MOE_STREAM_STEP(q1, c2 + 1, q0, c2)
+        MOE_STREAM_STEP(q0, c2 + 2 < n2 ? c2 + 2 : n2 - 1, q1, c2 + 1)
 #undef MOE_STREAM_STEP
-    }
+      }
     };
     // Larger tiles with a_ring: the workgroup stages each 256-element activation
     // chunk once (16*MSUB rows x 512 bytes; 16/MSUB threads per row, each load
