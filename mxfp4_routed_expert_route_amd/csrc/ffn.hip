@@ -109,16 +109,15 @@ hipError_t launch_ffn(const uint16_t* x, int64_t T, int H, int I, int E, int k,
     err = launch_stream(false, msub, g2, stream, h, h_bytes, nullptr, k, slots_i, w2, w2s, t,
                         n_tiles, I, H, 0, wpt2, limit, 0, y_sorted, H);
   } else {
-    const int wpt1 = I / 32, wpt2 = H / 64;
-    err = launch_tile(true, tile_bound, stream, x, x_bytes, gather, k, slots_i, w1, w1s, tiles,
-                      n_tiles, H, 2 * I, I, wpt1, limit, clamp_i, h, I);
+    err = launch_tile(true, tile_rows, tile_bound, stream, x, x_bytes, gather, k, slots_i, w1,
+                      w1s, tiles, n_tiles, H, 2 * I, I, limit, clamp_i, h, I);
     if (err != hipSuccess) return err;
     if (events) {
       err = hipEventRecord(events[1], stream);
       if (err != hipSuccess) return err;
     }
-    err = launch_tile(false, tile_bound, stream, h, h_bytes, nullptr, k, slots_i, w2, w2s, tiles,
-                      n_tiles, I, H, 0, wpt2, limit, 0, y_sorted, H);
+    err = launch_tile(false, tile_rows, tile_bound, stream, h, h_bytes, nullptr, k, slots_i, w2,
+                      w2s, tiles, n_tiles, I, H, 0, limit, 0, y_sorted, H);
   }
   if (err != hipSuccess || !events) return err;
   return hipEventRecord(events[2], stream);

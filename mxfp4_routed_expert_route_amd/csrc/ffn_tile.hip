@@ -1,4 +1,6 @@
 // Tiled grouped GEMM for prefill-shaped batches (64-row tiles).
+#include <type_traits>
+
 #include "ffn_common.h"
 
 namespace moe {
@@ -6,18 +8,30 @@ namespace {
 
 // ---------------------------------------------------------------- tiled GEMM (many rows)
 //
-// For row tiles of 64 or 128 rows (prefill-shaped batches).  A workgroup of four
-// wavefronts owns one row tile and 256 weight rows; each wavefront has 64 weight
-// rows (same split as the streaming kernel: W1 32 gate + 32 up rows, W2 64 output
-// rows) and all 16-row MFMA subtiles of the tile (kMSub = 4 or 8), so each
-// dequantised weight fragment feeds kMSub MFMAs.  The activation tile of each K
-// chunk (kMSub*16 rows x 128 bf16) is loaded once per workgroup into LDS
+// For row tiles of 64 or 128 rows (prefill-shaped batches).  A workgroup of kWaves
+// wavefronts owns one row tile and kWaves x 16 x kFrag weight rows.  A wavefront
+// holds kFrag 16-row weight fragments (W1: kFrag/2 gate fragments and the
+// matching up fragments, so each SwiGLU pair meets in one lane; W2: kFrag output
+// fragments) and all kMSub 16-row MFMA subtiles of the tile, so each dequantised
+// weight fragment feeds kMSub MFMAs.  The activation tile of each K chunk
+// (kMSub*16 rows x 128 bf16) is loaded once per workgroup into LDS
 // (double-buffered; rows padded by 16 bytes so that the 16 lanes of a read group
-// hit distinct banks) and read by all four wavefronts.  Weights go straight to
+// hit distinct banks) and read by all its wavefronts.  Weights go straight to
 // registers, issued right after the chunk that frees their registers.  With 64-row
 // tiles the E8M0 scales are staged in LDS as in the streaming kernel; with
 // 128-row tiles the LDS holds only activations and the scales come with the
 // weights.
+//
+// Two shapes are used:
+//  * 64 x 256 (kMSub 4, four wavefronts, two workgroups per CU) for tiles of ~48
+//    rows, where the weights are read from HBM about once per expert and the
+//    batch is bound by HBM;
+//  * 128 x 512 (kMSub 8, eight wavefronts, one workgroup per CU) for experts with
+//    hundreds of rows, where the products bound the batch: per K chunk it moves
+//    half the activation and weight bytes per product of the 64 x 256 shape.  Its
+//    128 accumulator registers leave no room for the compiler to hoist every LDS
+//    read and dequantisation of a chunk; a scheduling barrier between the 32-wide
+//    K steps keeps it within 256 VGPRs without spills.
 //
 // Per chunk c: issue the activation loads of c+1 (128 rows) or c+2 (64 rows),
 // compute c, issue the weights of c+2, store the activations of c+1 to the other
@@ -25,38 +39,48 @@ namespace {
 //
 // Workgroup order.  The hardware deals consecutive workgroups to the 8 XCDs in
 // turn, and each XCD has its own 4 MB L2.  Launch order (row tile major) gives
-// each XCD 2 of the 16 column blocks of every tile: a small weight slice per L2,
-// but every tile's activations fetched into all 8 L2s.  Measured alternatives:
-// whole tiles per XCD (each L2 then cycles an expert's full 8.9 MB W1) was 40%
-// slower; 4 column blocks x half the tiles per XCD is ~1% faster than launch
-// order and is what is used.
+// each XCD 2 of the 16 column blocks of every tile (64 x 256 tiles of W1): a small
+// weight slice per L2, but every tile's activations fetched into all 8 L2s.
+// Measured alternatives: whole tiles per XCD (each L2 then cycles an expert's full
+// 8.9 MB W1) was 40% slower; 4 column blocks x half the tiles per XCD is ~1%
+// faster than launch order and is what is used there.  With 8 column blocks per
+// tile (128 x 512 tiles) the same split gives each XCD 2 column blocks of half
+// the tiles: a 1 MB activation tile goes to 4 L2s instead of 8, and the XCD's
+// slice of a hot expert (2 x 1.1 MB of W1) stays in its L2 across that expert's
+// many row tiles.
 constexpr int kARowBytes = kFfnKChunk * 2 + 16;   // 256 B of bf16 + 16 B pad
 constexpr int kXcds = 8;
 
 template <int kMSub>
 constexpr int a_buf_bytes() { return kMSub * 16 * kARowBytes; }
 
-template <bool kW1, int kMSub>
-__global__ __launch_bounds__(256, 2) void gemm_tile_kernel(
+template <bool kW1, int kMSub, int kFrag, int kWaves>
+__global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
     const uint16_t* __restrict__ act, uint32_t act_bytes, const int32_t* __restrict__ gather,
     int k_top, int n_slots, const uint8_t* __restrict__ wq, const uint8_t* __restrict__ wsc,
     const RowTile* __restrict__ tiles, const int32_t* __restrict__ n_tiles, int K, int n_rows,
     int half, int waves_per_tile, int blocks_per_tile, float limit, int clamp,
     uint16_t* __restrict__ out, int ld_out) {
+  static_assert(kFrag == 4 || kFrag == 8, "four or eight weight fragments per wavefront");
   constexpr bool kLdsScales = kMSub == 4;
   constexpr int kRows = kMSub * 16;
   constexpr int kABuf = a_buf_bytes<kMSub>();
-  constexpr int kThreadsPerRow = 256 / kRows;          // 4 (64 rows) or 2 (128 rows)
-  constexpr int kPieces = kMSub;                       // 16-byte pieces per thread per chunk
+  constexpr int kThreads = 64 * kWaves;
+  constexpr int kThreadsPerRow = kThreads / kRows;     // 4 (64 rows x 4 waves, 128 x 8) or 2
+  constexpr int kPieces = 16 / kThreadsPerRow;         // 16-byte pieces per thread per chunk
+  static_assert(kThreadsPerRow * kRows == kThreads, "activation staging covers each row exactly");
+  constexpr int kGate = kFrag / 2;                     // W1: gate fragments per wavefront
   extern __shared__ __attribute__((aligned(16))) unsigned char tile_lds[];
 
   // work id: with 16 column blocks per tile, XCD x takes column blocks
   // 4(x%4)..4(x%4)+3 of the row tiles of parity x/4 (its weight slice stays in its
   // L2 while each tile's activations go to 4 XCDs, not 8); otherwise launch order
+  // (same with 8 column blocks: XCD x takes column blocks 2(x%4), 2(x%4)+1)
   int work = blockIdx.x;
-  if (blocks_per_tile == 16) {
+  if (blocks_per_tile == 16 || blocks_per_tile == 8) {
     const int x = blockIdx.x % kXcds, l = blockIdx.x / kXcds;
-    work = ((l / 4) * 2 + x / 4) * 16 + (x % 4) * 4 + (l % 4);
+    const int per = blocks_per_tile / 4;   // column blocks per XCD and tile
+    work = ((l / per) * 2 + x / 4) * blocks_per_tile + (x % 4) * per + (l % per);
   }
   const int tile_id = work / blocks_per_tile;
   const int nb = work - tile_id * blocks_per_tile;
@@ -70,7 +94,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(
 
   // column group of this wavefront; a wavefront past the last group repeats the
   // last one (it still stages activations and meets every barrier) and stores nothing
-  const int cg_raw = nb * 4 + wave;
+  const int cg_raw = nb * kWaves + wave;
   const bool store_cols = cg_raw < waves_per_tile;
   const int cg = store_cols ? cg_raw : waves_per_tile - 1;
 
@@ -109,28 +133,36 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(
       *reinterpret_cast<uint4*>(a_lds + buf * kABuf + a_store + 16 * kThreadsPerRow * i) = ra[i];
   };
 
-  // --- weights: four fragments of 16 rows, this lane's row in each
+  // --- weights: kFrag fragments of 16 rows, this lane's row in each
   auto wrow = [&](int f, int c16) {
-    return kW1 ? (f >= 2 ? half : 0) + cg * 32 + (f & 1) * 16 + c16 : cg * 64 + f * 16 + c16;
+    return kW1 ? (f >= kGate ? half : 0) + cg * (16 * kGate) + (f % kGate) * 16 + c16
+               : cg * (16 * kFrag) + f * 16 + c16;
   };
-  int nrow[4];
-#pragma unroll
-  for (int f = 0; f < 4; ++f) nrow[f] = wrow(f, r16);
   const size_t row_q = static_cast<size_t>(K / 2), row_s = static_cast<size_t>(K / 32);
   const size_t e_rows = static_cast<size_t>(rt.expert) * n_rows;
-  const uint8_t* bq[4];
-  const uint32_t* bs[4];   // scale dword of (row, chunk): one byte per lane group
+  // weight and scale addresses: a wave-uniform base (the expert's slab and the
+  // fragment's first row) plus one 32-bit lane offset within the slab, so each
+  // load takes the scalar-base form and costs the wavefront one VGPR of address
+  const uint8_t* wbase = wq + e_rows * row_q;
+  const uint8_t* sbase = wsc + e_rows * row_s;
+  const int row0 = wrow(0, r16);
+  const uint32_t lane_q = static_cast<uint32_t>(row0 * row_q) + 16u * g;
+  const uint32_t lane_s = static_cast<uint32_t>(row0 * row_s);
+  size_t dq[kFrag], ds[kFrag];   // fragment f's rows start wrow(f) - wrow(0) rows further on
 #pragma unroll
-  for (int f = 0; f < 4; ++f) {
-    bq[f] = wq + (e_rows + nrow[f]) * row_q + 16 * g;
-    bs[f] = reinterpret_cast<const uint32_t*>(wsc + (e_rows + nrow[f]) * row_s);
+  for (int f = 0; f < kFrag; ++f) {
+    const int d = __builtin_amdgcn_readfirstlane(wrow(f, 0) - wrow(0, 0));
+    dq[f] = static_cast<size_t>(d) * row_q;
+    ds[f] = static_cast<size_t>(d) * row_s;
   }
-  auto load_w = [&](uint4 (&q)[4], uint32_t (&sd)[4], int kc) {
+  auto load_w = [&](uint4 (&q)[kFrag], uint32_t (&sd)[kFrag], int kc) {
 #pragma unroll
-    for (int f = 0; f < 4; ++f) q[f] = *reinterpret_cast<const uint4*>(bq[f] + kc * 64);
+    for (int f = 0; f < kFrag; ++f)
+      q[f] = *reinterpret_cast<const uint4*>(wbase + (dq[f] + kc * 64) + lane_q);
     if constexpr (!kLdsScales) {
 #pragma unroll
-      for (int f = 0; f < 4; ++f) sd[f] = bs[f][kc];
+      for (int f = 0; f < kFrag; ++f)
+        sd[f] = *reinterpret_cast<const uint32_t*>(sbase + (ds[f] + kc * 4) + lane_s);
     }
   };
 
@@ -138,6 +170,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(
   uint32_t* my_scales =
       reinterpret_cast<uint32_t*>(tile_lds + 2 * kABuf) + wave * (n_chunks * 64);
   if constexpr (kLdsScales) {
+    static_assert(!kLdsScales || kFrag == 4, "LDS scale staging holds four fragments");
     const int f = lane >> 4;
     const uint8_t* srow = wsc + (e_rows + wrow(f, r16)) * row_s;
     int c = 0;
@@ -152,52 +185,56 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(
       my_scales[(c * 16 + r16) * 4 + f] = *reinterpret_cast<const uint32_t*>(srow + c * 4);
   }
 
-  floatx4 acc[kMSub][4];
+  floatx4 acc[kMSub][kFrag];
 #pragma unroll
   for (int mi = 0; mi < kMSub; ++mi)
 #pragma unroll
-    for (int f = 0; f < 4; ++f) acc[mi][f] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int f = 0; f < kFrag; ++f) acc[mi][f] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // one chunk: activations from LDS buffer `buf`, weights in q, scale dwords in sd
-  auto compute = [&](const uint4 (&q)[4], const uint32_t (&sd)[4], int kc, int buf) {
-    uint32_t dw[4];
+  // one chunk: activations from LDS buffer `buf`, weights in q, scale dwords in sd;
+  // subtiles 0 .. NS-1 (NS = kMSub, or fewer when the tile's rows end earlier)
+  auto compute = [&](auto ns_c, const uint4 (&q)[kFrag], const uint32_t (&sd)[kFrag], int kc,
+                     int buf) {
+    constexpr int NS = decltype(ns_c)::value;
+    uint32_t dw[kFrag];
     if constexpr (kLdsScales) {
       const uint4 d = *reinterpret_cast<const uint4*>(my_scales + (kc * 16 + r16) * 4);
       dw[0] = d.x; dw[1] = d.y; dw[2] = d.z; dw[3] = d.w;
     } else {
 #pragma unroll
-      for (int f = 0; f < 4; ++f) dw[f] = sd[f];
+      for (int f = 0; f < kFrag; ++f) dw[f] = sd[f];
     }
-    float scl[4];
+    float scl[kFrag];
 #pragma unroll
-    for (int f = 0; f < 4; ++f) scl[f] = e8m0_as_f32((dw[f] >> (8 * g)) & 0xFFu);
-    const uint32_t w[4][4] = {{q[0].x, q[0].y, q[0].z, q[0].w},
-                              {q[1].x, q[1].y, q[1].z, q[1].w},
-                              {q[2].x, q[2].y, q[2].z, q[2].w},
-                              {q[3].x, q[3].y, q[3].z, q[3].w}};
+    for (int f = 0; f < kFrag; ++f) scl[f] = e8m0_as_f32((dw[f] >> (8 * g)) & 0xFFu);
     const unsigned char* abase = a_lds + buf * kABuf + r16 * kARowBytes + 64 * g;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      bf16x8 b[4];
+      bf16x8 b[kFrag];
 #pragma unroll
-      for (int f = 0; f < 4; ++f) b[f] = dequant8(w[f][s], scl[f]);
-      // every subtile, also those past the tile's rows (they hold zeros): a branch
-      // here would cut the MFMA stream into blocks that each wait on one LDS read
+      for (int f = 0; f < kFrag; ++f) {
+        const uint32_t wd = s == 0 ? q[f].x : s == 1 ? q[f].y : s == 2 ? q[f].z : q[f].w;
+        b[f] = dequant8(wd, scl[f]);
+      }
+      // every subtile up to NS, also those past the tile's rows (they hold zeros): a
+      // branch here would cut the MFMA stream into blocks that each wait on one LDS read
 #pragma unroll
-      for (int mi = 0; mi < kMSub; ++mi) {
+      for (int mi = 0; mi < NS; ++mi) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(abase + mi * 16 * kARowBytes + 16 * s);
 #pragma unroll
-        for (int f = 0; f < 4; ++f)
+        for (int f = 0; f < kFrag; ++f)
           acc[mi][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[f], acc[mi][f], 0, 0, 0);
       }
+      if constexpr (kMSub == 8) __builtin_amdgcn_sched_barrier(0);
     }
   };
 
   const int last = n_chunks - 1;
-  uint4 q0[4], q1[4];
-  uint32_t s0[4], s1[4];
+  uint4 q0[kFrag], q1[kFrag];
+  uint32_t s0[kFrag], s1[kFrag];
   int kc = 0;
   if constexpr (kMSub == 4) {
+    constexpr std::integral_constant<int, 4> all{};
     // activations two chunks ahead in registers (ra0/ra1), one chunk ahead in LDS
     uint4 ra0[kPieces], ra1[kPieces];
     load_a(ra0, 0);
@@ -208,38 +245,52 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(
     __syncthreads();
     for (; kc + 2 <= n_chunks; kc += 2) {
       load_a(ra0, kc + 2 <= last ? kc + 2 : last);
-      compute(q0, s0, kc, 0);
+      compute(all, q0, s0, kc, 0);
       load_w(q0, s0, kc + 2 <= last ? kc + 2 : last);
       store_a(ra1, 1);
       __syncthreads();
       load_a(ra1, kc + 3 <= last ? kc + 3 : last);
-      compute(q1, s1, kc + 1, 1);
+      compute(all, q1, s1, kc + 1, 1);
       load_w(q1, s1, kc + 3 <= last ? kc + 3 : last);
       store_a(ra0, 0);
       __syncthreads();
     }
+    if (kc < n_chunks) compute(all, q0, s0, kc, 0);   // odd chunk count: last chunk in q0
   } else {
-    // activations one chunk ahead (registers ra, then LDS)
-    uint4 ra[kPieces];
-    load_a(ra, 0);
-    load_w(q0, s0, 0);
-    load_w(q1, s1, last >= 1 ? 1 : 0);
-    store_a(ra, 0);
-    __syncthreads();
-    for (; kc + 2 <= n_chunks; kc += 2) {
-      load_a(ra, kc + 1);
-      compute(q0, s0, kc, 0);
-      load_w(q0, s0, kc + 2 <= last ? kc + 2 : last);
-      store_a(ra, 1);
-      __syncthreads();
-      load_a(ra, kc + 2 <= last ? kc + 2 : last);
-      compute(q1, s1, kc + 1, 1);
-      load_w(q1, s1, kc + 3 <= last ? kc + 3 : last);
+    // activations one chunk ahead (registers ra, then LDS).  The K loop is
+    // instantiated for 2, 4 and 8 subtiles and the tile takes the smallest that
+    // covers its rows (a uniform branch outside the loop): the last tile of an
+    // expert, and every tile of an expert with few rows, runs only the MFMAs of
+    // its rows
+    auto run = [&](auto ns_c) {
+      uint4 ra[kPieces];
+      load_a(ra, 0);
+      load_w(q0, s0, 0);
+      load_w(q1, s1, last >= 1 ? 1 : 0);
       store_a(ra, 0);
       __syncthreads();
+      for (; kc + 2 <= n_chunks; kc += 2) {
+        load_a(ra, kc + 1);
+        compute(ns_c, q0, s0, kc, 0);
+        load_w(q0, s0, kc + 2 <= last ? kc + 2 : last);
+        store_a(ra, 1);
+        __syncthreads();
+        load_a(ra, kc + 2 <= last ? kc + 2 : last);
+        compute(ns_c, q1, s1, kc + 1, 1);
+        load_w(q1, s1, kc + 3 <= last ? kc + 3 : last);
+        store_a(ra, 0);
+        __syncthreads();
+      }
+      if (kc < n_chunks) compute(ns_c, q0, s0, kc, 0);   // odd chunk count
+    };
+    if (msub > kMSub / 2) {
+      run(std::integral_constant<int, kMSub>{});
+    } else if (msub > kMSub / 4) {
+      run(std::integral_constant<int, kMSub / 2>{});
+    } else {
+      run(std::integral_constant<int, kMSub / 4>{});
     }
   }
-  if (kc < n_chunks) compute(q0, s0, kc, 0);   // odd chunk count: last chunk in buffer 0 / q0
 
   if (!store_cols) return;
   const bool do_clamp = clamp != 0;
@@ -252,28 +303,34 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(
       if (p >= rt.p_end) continue;
       uint16_t* orow = out + static_cast<int64_t>(p) * ld_out;
       if (kW1) {
-        orow[nrow[0]] = f32_to_bf16_bits(swiglu(acc[mi][0][i], acc[mi][2][i], limit, do_clamp));
-        orow[nrow[1]] = f32_to_bf16_bits(swiglu(acc[mi][1][i], acc[mi][3][i], limit, do_clamp));
+#pragma unroll
+        for (int f = 0; f < kGate; ++f)
+          orow[wrow(f, r16)] =
+              f32_to_bf16_bits(swiglu(acc[mi][f][i], acc[mi][f + kGate][i], limit, do_clamp));
       } else {
 #pragma unroll
-        for (int f = 0; f < 4; ++f) orow[nrow[f]] = f32_to_bf16_bits(acc[mi][f][i]);
+        for (int f = 0; f < kFrag; ++f) orow[wrow(f, r16)] = f32_to_bf16_bits(acc[mi][f][i]);
       }
     }
   }
 }
 
-template <bool kW1, int kMSub>
+template <bool kW1, int kMSub, int kFrag, int kWaves>
 hipError_t launch_tile_t(int64_t tile_bound, hipStream_t stream, const uint16_t* act,
-                       uint32_t act_bytes, const int32_t* gather, int k_top, int n_slots,
-                       const uint8_t* wq, const uint8_t* wsc, const RowTile* tiles,
-                       const int32_t* n_tiles, int K, int n_rows, int half, int wpt, float limit,
-                       int clamp, uint16_t* out, int ld_out) {
-  const int bpt = (wpt + 3) / 4;
+                         uint32_t act_bytes, const int32_t* gather, int k_top, int n_slots,
+                         const uint8_t* wq, const uint8_t* wsc, const RowTile* tiles,
+                         const int32_t* n_tiles, int K, int n_rows, int half, float limit,
+                         int clamp, uint16_t* out, int ld_out) {
+  // wavefronts per row tile: W1 pairs `half` gate rows with as many up rows, 16 *
+  // kFrag/2 of each per wavefront; W2 covers n_rows output rows, 16 * kFrag each
+  const int wpt = kW1 ? half / (8 * kFrag) : n_rows / (16 * kFrag);
+  const int bpt = (wpt + kWaves - 1) / kWaves;
   size_t lds = 2 * static_cast<size_t>(a_buf_bytes<kMSub>());
-  if (kMSub == 4) lds += static_cast<size_t>(4) * (K / kFfnKChunk) * 64 * sizeof(uint32_t);
+  if (kMSub == 4) lds += static_cast<size_t>(kWaves) * (K / kFfnKChunk) * 64 * sizeof(uint32_t);
   // the column-block/XCD split covers row tiles in pairs: round up to whole pairs
-  const int64_t blocks = bpt == 16 ? (tile_bound + 1) / 2 * 2 * bpt : tile_bound * bpt;
-  gemm_tile_kernel<kW1, kMSub><<<static_cast<unsigned>(blocks), 256, lds, stream>>>(
+  const int64_t blocks =
+      (bpt == 16 || bpt == 8) ? (tile_bound + 1) / 2 * 2 * bpt : tile_bound * bpt;
+  gemm_tile_kernel<kW1, kMSub, kFrag, kWaves><<<static_cast<unsigned>(blocks), 64 * kWaves, lds, stream>>>(
       act, act_bytes, gather, k_top, n_slots, wq, wsc, tiles, n_tiles, K, n_rows, half, wpt, bpt,
       limit, clamp, out, ld_out);
   return hipGetLastError();
@@ -281,17 +338,24 @@ hipError_t launch_tile_t(int64_t tile_bound, hipStream_t stream, const uint16_t*
 
 }  // namespace
 
-hipError_t launch_tile(bool w1, int64_t tile_bound, hipStream_t stream, const uint16_t* act,
-                       uint32_t act_bytes, const int32_t* gather, int k_top, int n_slots,
-                       const uint8_t* wq, const uint8_t* wsc, const RowTile* tiles,
-                       const int32_t* n_tiles, int K, int n_rows, int half, int wpt, float limit,
-                       int clamp, uint16_t* out, int ld_out) {
-  return w1 ? launch_tile_t<true, 4>(tile_bound, stream, act, act_bytes, gather, k_top, n_slots, wq,
-                                     wsc, tiles, n_tiles, K, n_rows, half, wpt, limit, clamp, out,
-                                     ld_out)
-            : launch_tile_t<false, 4>(tile_bound, stream, act, act_bytes, gather, k_top, n_slots,
-                                      wq, wsc, tiles, n_tiles, K, n_rows, half, wpt, limit, clamp,
-                                      out, ld_out);
+hipError_t launch_tile(bool w1, int tile_rows, int64_t tile_bound, hipStream_t stream,
+                       const uint16_t* act, uint32_t act_bytes, const int32_t* gather, int k_top,
+                       int n_slots, const uint8_t* wq, const uint8_t* wsc, const RowTile* tiles,
+                       const int32_t* n_tiles, int K, int n_rows, int half, float limit, int clamp,
+                       uint16_t* out, int ld_out) {
+  if (tile_rows == 128)
+    return w1 ? launch_tile_t<true, 8, 4, 8>(tile_bound, stream, act, act_bytes, gather, k_top,
+                                          n_slots, wq, wsc, tiles, n_tiles, K, n_rows, half,
+                                          limit, clamp, out, ld_out)
+              : launch_tile_t<false, 8, 4, 8>(tile_bound, stream, act, act_bytes, gather, k_top,
+                                           n_slots, wq, wsc, tiles, n_tiles, K, n_rows, half,
+                                           limit, clamp, out, ld_out);
+  return w1 ? launch_tile_t<true, 4, 4, 4>(tile_bound, stream, act, act_bytes, gather, k_top, n_slots,
+                                        wq, wsc, tiles, n_tiles, K, n_rows, half, limit, clamp, out,
+                                        ld_out)
+            : launch_tile_t<false, 4, 4, 4>(tile_bound, stream, act, act_bytes, gather, k_top, n_slots,
+                                         wq, wsc, tiles, n_tiles, K, n_rows, half, limit, clamp,
+                                         out, ld_out);
 }
 
 }  // namespace moe

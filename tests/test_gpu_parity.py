@@ -133,9 +133,13 @@ def test_workload0_whole_layer(limit):
     (1030, 48, 8, 128, 128, 6),      # crosses a 1024-token offsets block
     (33, 1024, 8, 128, 128, 7),      # maximum E and k
     (40, 8, 1, 128, 128, 8),         # k = 1
-    (400, 16, 4, 768, 512, 14),      # 256-K tiled GEMM: W1 3 chunks (odd), W2 2 chunks
-    (260, 8, 3, 512, 768, 15),       # 256-K tiled GEMM: W1 2 chunks, W2 3 chunks, ragged tiles
-    (300, 8, 2, 1536, 1024, 16),     # wide tiled GEMM: W1 6 chunks (one loop pass), W2 4 (tail)
+    (400, 16, 4, 768, 512, 14),      # 128-row tiles (100 rows per expert): W1 6 chunks, W2 4
+    (260, 8, 3, 512, 768, 15),       # 128-row tiles (97 rows per expert): W1 4 chunks, W2 6,
+                                     # ragged tiles
+    (300, 8, 2, 1536, 1024, 16),     # 64-row tiles (75 rows per expert): W1 12 chunks, W2 8
+    (300, 8, 3, 384, 640, 17),       # 128-row tiles (112 rows per expert): W1 3 chunks, 20
+                                     # wavefronts per tile (last workgroup part-idle); W2 5
+                                     # chunks, 6 wavefronts per tile
 ])
 def test_ragged_shapes_whole_layer(T, E, k, H, I, seed):
     whole_layer_parity(tiny(T, E, k, H, I, seed), 10.0)
@@ -159,6 +163,12 @@ def test_fused_front_end_ties():
 
 def test_skewed_small_whole_layer():
     whole_layer_parity(tiny(500, 64, 6, 256, 128, 9, skew=True), 10.0)
+
+
+def test_skewed_128_row_tiles():
+    # 131 rows per expert on average -> 128-row tiles; the skew leaves hot experts
+    # with several full tiles and the rest with tails that run 2, 4 or 8 subtiles
+    whole_layer_parity(tiny(700, 32, 6, 384, 256, 27, skew=True), 10.0)
 
 
 def test_all_tied_logits_route_to_lowest_ids():
