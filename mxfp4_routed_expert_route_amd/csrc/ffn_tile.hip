@@ -234,28 +234,38 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
   uint32_t s0[kFrag], s1[kFrag];
   int kc = 0;
   if constexpr (kMSub == 4) {
-    constexpr std::integral_constant<int, 4> all{};
-    // activations two chunks ahead in registers (ra0/ra1), one chunk ahead in LDS
-    uint4 ra0[kPieces], ra1[kPieces];
-    load_a(ra0, 0);
-    load_w(q0, s0, 0);
-    load_w(q1, s1, last >= 1 ? 1 : 0);
-    load_a(ra1, last >= 1 ? 1 : 0);
-    store_a(ra0, 0);
-    __syncthreads();
-    for (; kc + 2 <= n_chunks; kc += 2) {
-      load_a(ra0, kc + 2 <= last ? kc + 2 : last);
-      compute(all, q0, s0, kc, 0);
-      load_w(q0, s0, kc + 2 <= last ? kc + 2 : last);
-      store_a(ra1, 1);
-      __syncthreads();
-      load_a(ra1, kc + 3 <= last ? kc + 3 : last);
-      compute(all, q1, s1, kc + 1, 1);
-      load_w(q1, s1, kc + 3 <= last ? kc + 3 : last);
+    // activations two chunks ahead in registers (ra0/ra1), one chunk ahead in LDS.
+    // The K loop is instantiated for 2, 3 and 4 subtiles; the tile takes the
+    // smallest that covers its rows (a uniform branch outside the loop)
+    auto run = [&](auto ns_c) {
+      uint4 ra0[kPieces], ra1[kPieces];
+      load_a(ra0, 0);
+      load_w(q0, s0, 0);
+      load_w(q1, s1, last >= 1 ? 1 : 0);
+      load_a(ra1, last >= 1 ? 1 : 0);
       store_a(ra0, 0);
       __syncthreads();
+      for (; kc + 2 <= n_chunks; kc += 2) {
+        load_a(ra0, kc + 2 <= last ? kc + 2 : last);
+        compute(ns_c, q0, s0, kc, 0);
+        load_w(q0, s0, kc + 2 <= last ? kc + 2 : last);
+        store_a(ra1, 1);
+        __syncthreads();
+        load_a(ra1, kc + 3 <= last ? kc + 3 : last);
+        compute(ns_c, q1, s1, kc + 1, 1);
+        load_w(q1, s1, kc + 3 <= last ? kc + 3 : last);
+        store_a(ra0, 0);
+        __syncthreads();
+      }
+      if (kc < n_chunks) compute(ns_c, q0, s0, kc, 0);   // odd chunk count: last chunk in q0
+    };
+    if (msub > 3) {
+      run(std::integral_constant<int, 4>{});
+    } else if (msub > 2) {
+      run(std::integral_constant<int, 3>{});
+    } else {
+      run(std::integral_constant<int, 2>{});
     }
-    if (kc < n_chunks) compute(all, q0, s0, kc, 0);   // odd chunk count: last chunk in q0
   } else {
     // activations one chunk ahead (registers ra, then LDS).  The K loop is
     // instantiated for 2, 4 and 8 subtiles and the tile takes the smallest that
