@@ -111,10 +111,18 @@ def cpu_baseline(inp, n_tokens):
     dt = time.perf_counter() - t0
     if limiter is not None:
         limiter.restore_original_limits()
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f
+                              if ln.startswith("model name")), None)
+    except OSError:
+        pass
     return dict(value=n_tokens / dt, unit="tokens/s", cores=1, kind="oracle",
                 sample=f"first {n_tokens} of {inp['logits'].shape[0]} tokens, whole layer "
                        f"(route..combine, dequantisation included), numpy with 1 BLAS thread, "
-                       f"{dt:.1f} s")
+                       f"{dt:.1f} s",
+                host_cpu=cpu_model, host_cpu_count=os.cpu_count(), numpy=np.__version__)
 
 
 def main():
@@ -319,11 +327,12 @@ def main():
     avg_ms = per.mean(axis=0)
     layer_ev_us = np.array([hip.ms(events[i * n_ev], events[i * n_ev + 7]) for i in range(n_bd)]) * 1e3
 
-    # Achievable-HBM marker of the same run: a plain device copy (read + write).
-    copy_gbs = None
+    # Achievable-HBM markers of the same run: a plain device copy (read + write
+    # bytes over its time) and a plain streaming read (moe_read_probe).
+    copy_gbs = read_gbs = None
     if args.copy_marker_mib > 0:
         n = args.copy_marker_mib << 20
-        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        src = torch.zeros(n, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
@@ -332,7 +341,17 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         copy_gbs = 2 * n * 10 / (time.perf_counter() - c0) / 1e9
-        del src, dst
+        del dst
+        # and a plain streaming read of the same bytes (the library's read probe)
+        sink = torch.empty(binding.READ_PROBE_SINK_WORDS, dtype=torch.int32, device="cuda")
+        binding.moe_read_probe(src, sink)
+        torch.cuda.synchronize()
+        c0 = time.perf_counter()
+        for _ in range(10):
+            binding.moe_read_probe(src, sink)
+        torch.cuda.synchronize()
+        read_gbs = n * 10 / (time.perf_counter() - c0) / 1e9
+        del src, sink
 
     counts = b.counts.cpu().numpy()
     touched = int((counts > 0).sum())
@@ -390,6 +409,7 @@ def main():
         "graph_us_per_layer": graph_us,
         "layer_us_with_events_p10_p50_p90": [float(np.percentile(layer_ev_us, q)) for q in (10, 50, 90)],
         "hbm_copy_marker_gbs": copy_gbs,
+        "hbm_read_marker_gbs": read_gbs,
         "ffn_w1_us_timed": w1_ms * 1e3,
         "ffn_w2_us_timed": w2_ms * 1e3,
         "touched_experts": touched,

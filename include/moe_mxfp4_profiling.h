@@ -12,6 +12,17 @@
  * Each entry is a hipEvent_t created by the caller (passed as void*); all three
  * must be non-NULL when T > 0.  Elapsed time between consecutive events is the
  * duration of one kernel.  T = 0 records nothing.
+ *
+ * moe_read_probe is the "achievable read bandwidth" marker measured beside the
+ * FFN kernels: a plain streaming read of `bytes` bytes of device memory at `buf`
+ * (16-byte loads, four in flight per lane, grid-stride), enqueued on `stream`.
+ * Workgroup b writes the XOR of the 32-bit words it read to sink[b], so the XOR
+ * of all MOE_READ_PROBE_SINK_WORDS sink words is the XOR of every 32-bit word of
+ * the buffer (a check that every byte was read).  `buf` and `sink` are device
+ * pointers owned by the caller; sink holds MOE_READ_PROBE_SINK_WORDS uint32.
+ * Errors: NULL buf (bytes > 0) or NULL sink -> MOE_ERR_INVALID_ARGUMENT; buf not
+ * 16-byte aligned or bytes not a multiple of 16 -> MOE_ERR_MISALIGNED; a failed
+ * launch -> MOE_ERR_HIP.  bytes = 0 enqueues nothing.
  */
 #ifndef MOE_MXFP4_PROFILING_H
 #define MOE_MXFP4_PROFILING_H
@@ -22,6 +33,8 @@
 extern "C" {
 #endif
 
+#define MOE_READ_PROBE_SINK_WORDS 2048
+
 moe_status moe_grouped_ffn_mxfp4_timed(const uint16_t* x, int64_t T, int32_t H, int32_t I,
                                        int32_t E, int32_t k, const uint8_t* w1,
                                        const uint8_t* w1_scale, const uint8_t* w2,
@@ -29,6 +42,8 @@ moe_status moe_grouped_ffn_mxfp4_timed(const uint16_t* x, int64_t T, int32_t H, 
                                        const int32_t* offsets, const int32_t* gather,
                                        float swiglu_limit, uint16_t* y_sorted, void* ws,
                                        size_t ws_bytes, void* const* events, void* stream);
+
+moe_status moe_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

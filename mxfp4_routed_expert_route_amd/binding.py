@@ -50,6 +50,7 @@ _SIG = {
     "moe_combine": [_P, _P, _P, _I64, _I32, _I32, _P, _P],
     "moe_forward_mxfp4": [_P, _P, _I64, _I32, _I32, _I32, _I32, _P, _P, _P, _P, ctypes.c_float,
                           _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "moe_read_probe": [_P, ctypes.c_size_t, _P, _P],
     "moe_workspace_bytes": [_I64, _I32, _I32, _I32, _I32],
     "moe_status_string": [ctypes.c_int],
 }
@@ -179,4 +180,20 @@ def moe_forward_mxfp4(logits, x, k: int, w1, w1_scale, w2, w2_scale, swiglu_limi
         _ptr(offsets, torch.int32, "offsets"), _ptr(gather, torch.int32, "gather"),
         _ptr(scatter, torch.int32, "scatter"), _ptr(y_sorted, BF16, "y_sorted"),
         _ptr(y, BF16, "y"), _ptr(ws, torch.uint8, "ws"), ws.numel() if ws is not None else 0,
+        _stream(stream)))
+
+
+READ_PROBE_SINK_WORDS = 2048
+
+
+def moe_read_probe(buf, sink, stream=None):
+    """Streaming read of every byte of `buf` (a contiguous device tensor, 16-byte
+    aligned, size a multiple of 16); `sink` is an int32 device tensor of
+    READ_PROBE_SINK_WORDS entries that receives the per-workgroup XORs."""
+    if not buf.is_contiguous():
+        raise ValueError("buf must be contiguous")
+    if sink.dtype != torch.int32 or sink.numel() < READ_PROBE_SINK_WORDS:
+        raise ValueError(f"sink must be int32 with >= {READ_PROBE_SINK_WORDS} entries")
+    _check("moe_read_probe", load().moe_read_probe(
+        _ptr(buf, None, "buf"), buf.numel() * buf.element_size(), _ptr(sink, torch.int32, "sink"),
         _stream(stream)))

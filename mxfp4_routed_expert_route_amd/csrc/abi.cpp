@@ -142,6 +142,14 @@ moe_status moe_grouped_ffn_mxfp4_timed(const uint16_t* x, int64_t T, int32_t H, 
                                   L.ffn_plan_offset, L.tile_bound, as_stream(stream), ev));
 }
 
+moe_status moe_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  static_assert(moe::kReadProbeBlocks == MOE_READ_PROBE_SINK_WORDS, "one sink word per workgroup");
+  if (sink == nullptr || (bytes > 0 && buf == nullptr)) return MOE_ERR_INVALID_ARGUMENT;
+  if (bytes % 16 != 0 || reinterpret_cast<uintptr_t>(buf) % 16 != 0) return MOE_ERR_MISALIGNED;
+  if (bytes == 0) return MOE_OK;
+  return from_hip(moe::launch_read_probe(buf, bytes, sink, as_stream(stream)));
+}
+
 moe_status moe_combine(const uint16_t* y_sorted, const float* topk_weights,
                        const int32_t* scatter, int64_t T, int32_t H, int32_t k, uint16_t* y,
                        void* stream) {

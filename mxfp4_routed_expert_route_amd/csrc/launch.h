@@ -41,6 +41,10 @@ hipError_t launch_route_and_group(const float* logits, int64_t T, int E, int k, 
                                   int32_t* gather, int32_t* scatter, void* ws, hipStream_t stream,
                                   const PlanOut* plan = nullptr, bool* plan_written = nullptr);
 
+// Streaming-read marker: kReadProbeBlocks workgroups, one sink word each.
+constexpr int kReadProbeBlocks = 2048;
+hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
+
 hipError_t launch_combine(const uint16_t* ys, const float* w, const int32_t* scatter, int64_t T,
                           int H, int k, uint16_t* y, hipStream_t stream);
 

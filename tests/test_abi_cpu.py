@@ -34,7 +34,7 @@ def test_header_declares_the_five_calls():
     names = declared_functions()
     for n in ("moe_route", "moe_build_bitmatrix", "moe_expert_offsets", "moe_route_and_group",
               "moe_grouped_ffn_mxfp4", "moe_combine", "moe_workspace_bytes", "moe_status_string",
-              "moe_grouped_ffn_mxfp4_timed", "moe_forward_mxfp4"):
+              "moe_grouped_ffn_mxfp4_timed", "moe_forward_mxfp4", "moe_read_probe"):
         assert n in names
 
 
@@ -76,6 +76,12 @@ def test_error_codes_through_the_abi(lib):
     assert lib.moe_workspace_bytes(8191, 256, 6, 4096, 2048) >= 49146 * 2048 * 2
     assert lib.moe_workspace_bytes(-1, 256, 6, 4096, 2048) == 0
     assert lib.moe_status_string(WS_SMALL) == b"MOE_ERR_WORKSPACE_TOO_SMALL"
+    lib.moe_read_probe.argtypes = [P, ctypes.c_size_t, P, P]
+    assert lib.moe_read_probe(None, 0, 256, None) == OK        # nothing to read: nothing enqueued
+    assert lib.moe_read_probe(256, 1 << 20, None, None) == INVALID   # no sink
+    assert lib.moe_read_probe(None, 1 << 20, 256, None) == INVALID   # no buffer
+    assert lib.moe_read_probe(256, 1000, 256, None) == MISALIGNED    # not a multiple of 16
+    assert lib.moe_read_probe(264, 1 << 20, 256, None) == MISALIGNED  # buffer not 16-B aligned
     lib.moe_forward_mxfp4.argtypes = [P, P, I64, I32, I32, I32, I32, P, P, P, P, ctypes.c_float] + \
         [P] * 10 + [ctypes.c_size_t, P]
     fwd = lambda T, H, I, E, k, ptrs, ws_bytes: lib.moe_forward_mxfp4(
