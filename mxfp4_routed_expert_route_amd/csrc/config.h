@@ -14,7 +14,7 @@ constexpr int64_t kMaxActivationBytes = 3758096384LL;   // 3.5 GiB: 32-bit buffe
 // moe_expert_offsets: tokens per workgroup (8 wavefronts of 64 tokens)
 constexpr int kOffsBlockTokens = 512;
 
-// grouped FFN: the smallest row tile of any path (16, 32, 64 or 128 rows are
+// grouped FFN: the smallest row tile of any path (16, 32, 80 or 128 rows are
 // used), and the K chunk per step
 constexpr int kFfnMinTileRows = 16;
 constexpr int kFfnKChunk = 128;
@@ -38,15 +38,15 @@ inline int64_t ffn_tile_bound(int64_t n_slots, int E, int tile_rows) {
 // per expert on average: 16-row streaming tiles (decode: the tiles' rows fit in
 // LDS for all of K); up to 24: 32-row streaming tiles (measured on the 512-token
 // burst, 12 rows per expert: 671 us per layer against 715 with 16-row tiles,
-// whose experts past 16 rows read their weights twice); up to 95: 64-row tiles of
-// the LDS-tiled kernel (HBM-bound: each expert's weights read about once); from
-// 96 on, 128-row tiles of the 128 x 512 tiled kernel (the products bound the
-// batch).
+// whose experts past 16 rows read their weights twice); up to 95: 80-row tiles of
+// the LDS-tiled kernel (HBM-bound: each expert's weights read about once; at 48
+// rows per expert on average the largest experts stay within one tile); from 96
+// on, 128-row tiles of the 128 x 512 tiled kernel (the products bound the batch).
 inline int ffn_tile_rows(int64_t T, int E, int k) {
   const int64_t avg_rows = T * k / E;
   if (T <= 16 || avg_rows <= 8) return 16;
   if (avg_rows <= 24) return 32;
-  return avg_rows < 96 ? 64 : 128;
+  return avg_rows < 96 ? 80 : 128;
 }
 
 struct RowTile {

@@ -2,7 +2,7 @@
 // W1 (gate|up with the clamped SwiGLU epilogue) and W2.
 //
 // A plan kernel cuts each expert's rows [offsets[e], offsets[e+1]) into row tiles
-// (16, 32 or 64 rows, chosen from T and the mean rows per expert); only experts
+// (16, 32, 80 or 128 rows, chosen from T and the mean rows per expert); only experts
 // with rows get tiles.  Few rows per expert (decode shapes): the streaming kernel
 // (ffn_stream.hip), one independent wavefront per (tile, 64 weight rows), bound
 // by HBM.  Many rows: the tiled kernel (ffn_tile.hip), four wavefronts sharing an
@@ -75,7 +75,7 @@ hipError_t launch_ffn(const uint16_t* x, int64_t T, int H, int I, int E, int k,
   const uint32_t x_bytes = static_cast<uint32_t>(T * H * 2);         // < 2^32 - 2^20 (host check)
   const uint32_t h_bytes = static_cast<uint32_t>(n_slots * I * 2);
 
-  // Few rows per expert -> weight streaming with 16- or 32-row tiles; else 64-row
+  // Few rows per expert -> weight streaming with 16- or 32-row tiles; else 80- or 128-row
   // tiles (ffn_tile_rows).  The plan may already be in the workspace (written by
   // the one-launch front-end of moe_forward_mxfp4 under the same rule).
   const int tile_rows = ffn_tile_rows(T, E, k);

@@ -51,7 +51,7 @@ hipError_t launch_stream(bool w1, int msub, unsigned grid, hipStream_t stream, c
                          const uint8_t* wq, const uint8_t* wsc, const RowTile* tiles,
                          const int32_t* n_tiles, int K, int n_rows, int half, int wpt, float limit,
                          int clamp, uint16_t* out, int ld_out);
-// tile_rows: 64 (64 x 256 workgroups) or 128 (128 x 512 workgroups)
+// tile_rows: 80 (80 x 256 workgroups) or 128 (128 x 512 workgroups)
 hipError_t launch_tile(bool w1, int tile_rows, int64_t tile_bound, hipStream_t stream,
                        const uint16_t* act, uint32_t act_bytes, const int32_t* gather, int k_top,
                        int n_slots, const uint8_t* wq, const uint8_t* wsc, const RowTile* tiles,

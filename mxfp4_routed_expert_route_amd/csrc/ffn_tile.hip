@@ -1,4 +1,4 @@
-// Tiled grouped GEMM for prefill-shaped batches (64-row tiles).
+// Tiled grouped GEMM for prefill-shaped batches (80- and 128-row tiles).
 #include <type_traits>
 
 #include "ffn_common.h"
@@ -8,7 +8,7 @@ namespace {
 
 // ---------------------------------------------------------------- tiled GEMM (many rows)
 //
-// For row tiles of 64 or 128 rows (prefill-shaped batches).  A workgroup of kWaves
+// For row tiles of 80 or 128 rows (prefill-shaped batches).  A workgroup of kWaves
 // wavefronts owns one row tile and kWaves x 16 x kFrag weight rows.  A wavefront
 // holds kFrag 16-row weight fragments (W1: kFrag/2 gate fragments and the
 // matching up fragments, so each SwiGLU pair meets in one lane; W2: kFrag output
@@ -17,15 +17,20 @@ namespace {
 // (kMSub*16 rows x 128 bf16) is loaded once per workgroup into LDS
 // (double-buffered; rows padded by 16 bytes so that the 16 lanes of a read group
 // hit distinct banks) and read by all its wavefronts.  Weights go straight to
-// registers, issued right after the chunk that frees their registers.  With 64-row
-// tiles the E8M0 scales are staged in LDS as in the streaming kernel; with
-// 128-row tiles the LDS holds only activations and the scales come with the
-// weights.
+// registers, issued right after the chunk that frees their registers.  With
+// 80-row tiles the E8M0 scales are staged in LDS as in the streaming kernel
+// while they fit beside the activation buffers (K <= 4096);
+// with 128-row tiles the LDS holds only activations and the scales come with the
+// weights.  Each tile runs only the 16-row subtiles that hold rows (the K loop is
+// instantiated per subtile count).
 //
 // Two shapes are used:
-//  * 64 x 256 (kMSub 4, four wavefronts, two workgroups per CU) for tiles of ~48
-//    rows, where the weights are read from HBM about once per expert and the
-//    batch is bound by HBM;
+//  * 80 x 256 (kMSub 5, four wavefronts, two workgroups per CU) for experts of
+//    ~25-95 rows, where the weights are read from HBM about once per expert and
+//    the batch is bound by HBM.  80 rather than 64 rows: with uniform routing at
+//    48 rows per expert the largest experts reach the high 60s, and each one past
+//    the tile size would re-read its 13.4 MB of weights for a few rows -- and
+//    its extra workgroups run as a near-empty last round of the grid;
 //  * 128 x 512 (kMSub 8, eight wavefronts, one workgroup per CU) for experts with
 //    hundreds of rows, where the products bound the batch: per K chunk it moves
 //    half the activation and weight bytes per product of the 64 x 256 shape.  Its
@@ -33,14 +38,14 @@ namespace {
 //    read and dequantisation of a chunk; a scheduling barrier between the 32-wide
 //    K steps keeps it within 256 VGPRs without spills.
 //
-// Per chunk c: issue the activation loads of c+1 (128 rows) or c+2 (64 rows),
+// Per chunk c: issue the activation loads of c+1 (128 rows) or c+2 (80 rows),
 // compute c, issue the weights of c+2, store the activations of c+1 to the other
 // LDS buffer, barrier.
 //
 // Workgroup order.  The hardware deals consecutive workgroups to the 8 XCDs in
 // turn, and each XCD has its own 4 MB L2.  Launch order (row tile major) gives
-// each XCD 2 of the 16 column blocks of every tile (64 x 256 tiles of W1): a small
-// weight slice per L2, but every tile's activations fetched into all 8 L2s.
+// each XCD 2 of the 16 column blocks of every tile (256-column blocks of W1): a
+// small weight slice per L2, but every tile's activations fetched into all 8 L2s.
 // Measured alternatives: whole tiles per XCD (each L2 then cycles an expert's full
 // 8.9 MB W1) was 40% slower; 4 column blocks x half the tiles per XCD is ~1%
 // faster than launch order and is what is used there.  With 8 column blocks per
@@ -53,8 +58,14 @@ constexpr int kXcds = 8;
 
 template <int kMSub>
 constexpr int a_buf_bytes() { return kMSub * 16 * kARowBytes; }
+// LDS of the staged E8M0 scales: per wavefront, one dword per (128-element chunk,
+// weight row) of its 64 rows
+inline size_t tile_scale_lds_bytes(int K, int waves) {
+  return static_cast<size_t>(waves) * (K / kFfnKChunk) * 64 * sizeof(uint32_t);
+}
+constexpr size_t kTileLdsPerWorkgroup = 80 * 1024;   // two workgroups per CU
 
-template <bool kW1, int kMSub, int kFrag, int kWaves>
+template <bool kW1, int kMSub, int kFrag, int kWaves, bool kLdsScales>
 __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
     const uint16_t* __restrict__ act, uint32_t act_bytes, const int32_t* __restrict__ gather,
     int k_top, int n_slots, const uint8_t* __restrict__ wq, const uint8_t* __restrict__ wsc,
@@ -62,13 +73,13 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
     int half, int waves_per_tile, int blocks_per_tile, float limit, int clamp,
     uint16_t* __restrict__ out, int ld_out) {
   static_assert(kFrag == 4 || kFrag == 8, "four or eight weight fragments per wavefront");
-  constexpr bool kLdsScales = kMSub == 4;
+  static_assert(!kLdsScales || kFrag == 4, "LDS scale staging holds four fragments");
   constexpr int kRows = kMSub * 16;
   constexpr int kABuf = a_buf_bytes<kMSub>();
   constexpr int kThreads = 64 * kWaves;
-  constexpr int kThreadsPerRow = kThreads / kRows;     // 4 (64 rows x 4 waves, 128 x 8) or 2
-  constexpr int kPieces = 16 / kThreadsPerRow;         // 16-byte pieces per thread per chunk
-  static_assert(kThreadsPerRow * kRows == kThreads, "activation staging covers each row exactly");
+  constexpr int kRowStride = kThreads / 16;            // rows apart of a thread's pieces
+  constexpr int kPieces = kRows / kRowStride;          // 16-byte pieces per thread per chunk
+  static_assert(kPieces * kRowStride == kRows, "activation staging covers each row exactly");
   constexpr int kGate = kFrag / 2;                     // W1: gate fragments per wavefront
   extern __shared__ __attribute__((aligned(16))) unsigned char tile_lds[];
 
@@ -98,14 +109,16 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
   const bool store_cols = cg_raw < waves_per_tile;
   const int cg = store_cols ? cg_raw : waves_per_tile - 1;
 
-  // --- activation staging: thread -> (row ar, part aq) of the chunk; piece i of a
-  // thread is bytes 16*(aq + kThreadsPerRow*i) of the row's 256, so each load
-  // instruction reads contiguous 16*kThreadsPerRow bytes of every row
+  // --- activation staging: thread t stages the 16-byte part t % 16 of rows
+  // t / 16 + kRowStride * i of the chunk: sixteen consecutive lanes cover one
+  // row's 256 contiguous bytes, so each load instruction reads whole 256-byte row
+  // pieces, and any multiple of 16 rows maps onto the workgroup
   const __amdgpu_buffer_rsrc_t arsrc = make_rsrc(act, act_bytes);
-  const int ar = tid / kThreadsPerRow, aq = tid % kThreadsPerRow;
-  uint32_t aoff;
-  {
-    const int p = rt.p_begin + ar;
+  const int ar = tid >> 4, aq = tid & 15;
+  uint32_t aoff[kPieces];
+#pragma unroll
+  for (int i = 0; i < kPieces; ++i) {
+    const int p = rt.p_begin + ar + kRowStride * i;
     bool valid = p < rt.p_end;
     uint32_t row = 0;
     if (valid) {
@@ -117,20 +130,21 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
         row = static_cast<uint32_t>(p);
       }
     }
-    aoff = valid ? row * static_cast<uint32_t>(K) * 2u + 16u * aq : kRsrcOutOfRange;
+    aoff[i] = valid ? row * static_cast<uint32_t>(K) * 2u + 16u * aq : kRsrcOutOfRange;
   }
   unsigned char* a_lds = tile_lds;                       // [2][kRows][kARowBytes]
   const int a_store = ar * kARowBytes + aq * 16;
   auto load_a = [&](uint4 (&ra)[kPieces], int kc) {
 #pragma unroll
     for (int i = 0; i < kPieces; ++i)
-      ra[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                            arsrc, aoff + kc * 256 + 16 * kThreadsPerRow * i, 0, 0));
+      ra[i] = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(arsrc, aoff[i] + kc * 256, 0, 0));
   };
   auto store_a = [&](const uint4 (&ra)[kPieces], int buf) {
 #pragma unroll
     for (int i = 0; i < kPieces; ++i)
-      *reinterpret_cast<uint4*>(a_lds + buf * kABuf + a_store + 16 * kThreadsPerRow * i) = ra[i];
+      *reinterpret_cast<uint4*>(a_lds + buf * kABuf + a_store + kRowStride * i * kARowBytes) =
+          ra[i];
   };
 
   // --- weights: kFrag fragments of 16 rows, this lane's row in each
@@ -166,11 +180,11 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
     }
   };
 
-  // --- 64-row tiles: scales of the wavefront's 64 rows, staged as [chunk][16][4] dwords
+  // --- 80-row tiles: scales of the wavefront's 64 weight rows, staged as
+  // [chunk][16][4] dwords
   uint32_t* my_scales =
       reinterpret_cast<uint32_t*>(tile_lds + 2 * kABuf) + wave * (n_chunks * 64);
   if constexpr (kLdsScales) {
-    static_assert(!kLdsScales || kFrag == 4, "LDS scale staging holds four fragments");
     const int f = lane >> 4;
     const uint8_t* srow = wsc + (e_rows + wrow(f, r16)) * row_s;
     int c = 0;
@@ -233,10 +247,10 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
   uint4 q0[kFrag], q1[kFrag];
   uint32_t s0[kFrag], s1[kFrag];
   int kc = 0;
-  if constexpr (kMSub == 4) {
+  if constexpr (kWaves == 4) {
     // activations two chunks ahead in registers (ra0/ra1), one chunk ahead in LDS.
-    // The K loop is instantiated for 2, 3 and 4 subtiles; the tile takes the
-    // smallest that covers its rows (a uniform branch outside the loop)
+    // The K loop is instantiated for 2 .. 5 subtiles; the tile takes the smallest
+    // that covers its rows (a uniform branch outside the loop)
     auto run = [&](auto ns_c) {
       uint4 ra0[kPieces], ra1[kPieces];
       load_a(ra0, 0);
@@ -259,7 +273,9 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
       }
       if (kc < n_chunks) compute(ns_c, q0, s0, kc, 0);   // odd chunk count: last chunk in q0
     };
-    if (msub > 3) {
+    if (msub > 4) {
+      run(std::integral_constant<int, 5>{});
+    } else if (msub > 3) {
       run(std::integral_constant<int, 4>{});
     } else if (msub > 2) {
       run(std::integral_constant<int, 3>{});
@@ -325,7 +341,7 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
   }
 }
 
-template <bool kW1, int kMSub, int kFrag, int kWaves>
+template <bool kW1, int kMSub, int kFrag, int kWaves, bool kLdsScales>
 hipError_t launch_tile_t(int64_t tile_bound, hipStream_t stream, const uint16_t* act,
                          uint32_t act_bytes, const int32_t* gather, int k_top, int n_slots,
                          const uint8_t* wq, const uint8_t* wsc, const RowTile* tiles,
@@ -336,11 +352,11 @@ hipError_t launch_tile_t(int64_t tile_bound, hipStream_t stream, const uint16_t*
   const int wpt = kW1 ? half / (8 * kFrag) : n_rows / (16 * kFrag);
   const int bpt = (wpt + kWaves - 1) / kWaves;
   size_t lds = 2 * static_cast<size_t>(a_buf_bytes<kMSub>());
-  if (kMSub == 4) lds += static_cast<size_t>(kWaves) * (K / kFfnKChunk) * 64 * sizeof(uint32_t);
+  if (kLdsScales) lds += tile_scale_lds_bytes(K, kWaves);
   // the column-block/XCD split covers row tiles in pairs: round up to whole pairs
   const int64_t blocks =
       (bpt == 16 || bpt == 8) ? (tile_bound + 1) / 2 * 2 * bpt : tile_bound * bpt;
-  gemm_tile_kernel<kW1, kMSub, kFrag, kWaves><<<static_cast<unsigned>(blocks), 64 * kWaves, lds, stream>>>(
+  gemm_tile_kernel<kW1, kMSub, kFrag, kWaves, kLdsScales><<<static_cast<unsigned>(blocks), 64 * kWaves, lds, stream>>>(
       act, act_bytes, gather, k_top, n_slots, wq, wsc, tiles, n_tiles, K, n_rows, half, wpt, bpt,
       limit, clamp, out, ld_out);
   return hipGetLastError();
@@ -354,18 +370,28 @@ hipError_t launch_tile(bool w1, int tile_rows, int64_t tile_bound, hipStream_t s
                        const int32_t* n_tiles, int K, int n_rows, int half, float limit, int clamp,
                        uint16_t* out, int ld_out) {
   if (tile_rows == 128)
-    return w1 ? launch_tile_t<true, 8, 4, 8>(tile_bound, stream, act, act_bytes, gather, k_top,
+    return w1 ? launch_tile_t<true, 8, 4, 8, false>(tile_bound, stream, act, act_bytes, gather, k_top,
                                           n_slots, wq, wsc, tiles, n_tiles, K, n_rows, half,
                                           limit, clamp, out, ld_out)
-              : launch_tile_t<false, 8, 4, 8>(tile_bound, stream, act, act_bytes, gather, k_top,
+              : launch_tile_t<false, 8, 4, 8, false>(tile_bound, stream, act, act_bytes, gather, k_top,
                                            n_slots, wq, wsc, tiles, n_tiles, K, n_rows, half,
                                            limit, clamp, out, ld_out);
-  return w1 ? launch_tile_t<true, 4, 4, 4>(tile_bound, stream, act, act_bytes, gather, k_top, n_slots,
-                                        wq, wsc, tiles, n_tiles, K, n_rows, half, limit, clamp, out,
-                                        ld_out)
-            : launch_tile_t<false, 4, 4, 4>(tile_bound, stream, act, act_bytes, gather, k_top, n_slots,
-                                         wq, wsc, tiles, n_tiles, K, n_rows, half, limit, clamp,
-                                         out, ld_out);
+  // 80-row tiles keep two workgroups per CU: the E8M0 scales are staged in LDS
+  // while they fit beside the activation buffers in half the CU's LDS (K <= 4096
+  // for 256-element rows of scales per wavefront), else they come with the weights
+  if (2 * static_cast<size_t>(a_buf_bytes<5>()) + tile_scale_lds_bytes(K, 4) <= kTileLdsPerWorkgroup)
+    return w1 ? launch_tile_t<true, 5, 4, 4, true>(tile_bound, stream, act, act_bytes, gather,
+                                                   k_top, n_slots, wq, wsc, tiles, n_tiles, K,
+                                                   n_rows, half, limit, clamp, out, ld_out)
+              : launch_tile_t<false, 5, 4, 4, true>(tile_bound, stream, act, act_bytes, gather,
+                                                    k_top, n_slots, wq, wsc, tiles, n_tiles, K,
+                                                    n_rows, half, limit, clamp, out, ld_out);
+  return w1 ? launch_tile_t<true, 5, 4, 4, false>(tile_bound, stream, act, act_bytes, gather,
+                                                  k_top, n_slots, wq, wsc, tiles, n_tiles, K,
+                                                  n_rows, half, limit, clamp, out, ld_out)
+            : launch_tile_t<false, 5, 4, 4, false>(tile_bound, stream, act, act_bytes, gather,
+                                                   k_top, n_slots, wq, wsc, tiles, n_tiles, K,
+                                                   n_rows, half, limit, clamp, out, ld_out);
 }
 
 }  // namespace moe

@@ -4,7 +4,7 @@ Every output must match the separate-call chain (moe_route_and_group,
 moe_grouped_ffn_mxfp4, moe_combine) bit for bit: the same kernels run, except
 that for T <= 64 the one-launch front-end also writes the FFN's row-tile plan in
 place of the FFN's plan kernel.  The cases cover each tile kind the plan can
-hold (16- and 32-row streaming tiles, 64-row LDS tiles; 128-row tiles, which
+hold (16- and 32-row streaming tiles, 80-row LDS tiles; 128-row tiles, which
 need more than 64 tokens) on both sides of the T = 64 front-end limit, and T = 0.
 """
 from __future__ import annotations
@@ -60,7 +60,7 @@ def test_forward_matches_separate_calls_workloads(index):
     (1, 256, 6, 256, 128, 41),       # one token, 16-row tiles
     (40, 8, 1, 128, 128, 42),        # 5 rows per expert: 16-row tiles, several per expert
     (64, 24, 7, 256, 128, 43),       # 18.7 rows per expert: 32-row tiles, front-end plan
-    (64, 16, 8, 256, 256, 44),       # 32 rows per expert: 64-row LDS tiles, front-end plan
+    (64, 16, 8, 256, 256, 44),       # 32 rows per expert: 80-row LDS tiles, front-end plan
     (65, 16, 8, 256, 256, 45),       # past the one-launch limit: plan kernel
     (300, 8, 3, 256, 256, 48),       # 112 rows per expert: 128-row tiles, plan kernel
     (33, 1024, 8, 128, 128, 46),     # maximum E and k

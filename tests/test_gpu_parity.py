@@ -129,14 +129,18 @@ def test_workload0_whole_layer(limit):
     (7, 256, 6, 256, 128, 2),
     (11, 64, 6, 128, 256, 3),        # rows span two bitmatrix wavefronts
     (70, 32, 6, 384, 128, 4),        # ragged row tiles (>64 rows for some experts)
-    (300, 16, 2, 256, 384, 5),       # many rows per expert: several 64-row tiles + tail
+    (300, 16, 2, 256, 384, 5),       # many rows per expert: 80-row tiles
     (1030, 48, 8, 128, 128, 6),      # crosses a 1024-token offsets block
     (33, 1024, 8, 128, 128, 7),      # maximum E and k
     (40, 8, 1, 128, 128, 8),         # k = 1
     (400, 16, 4, 768, 512, 14),      # 128-row tiles (100 rows per expert): W1 6 chunks, W2 4
     (260, 8, 3, 512, 768, 15),       # 128-row tiles (97 rows per expert): W1 4 chunks, W2 6,
                                      # ragged tiles
-    (300, 8, 2, 1536, 1024, 16),     # 64-row tiles (75 rows per expert): W1 12 chunks, W2 8
+    (300, 8, 2, 1536, 1024, 16),     # 80-row tiles (75 rows per expert, some experts in two
+                                     # tiles): W1 12 chunks, W2 8
+    (290, 8, 2, 256, 256, 19),       # 80-row tiles, experts of ~60-85 rows: 4 and 5 subtiles
+    (100, 8, 2, 8192, 256, 18),      # 80-row tiles, W1 K = 8192: E8M0 scales come with the
+                                     # weights (they do not fit in LDS beside the activations)
     (300, 8, 3, 384, 640, 17),       # 128-row tiles (112 rows per expert): W1 3 chunks, 20
                                      # wavefronts per tile (last workgroup part-idle); W2 5
                                      # chunks, 6 wavefronts per tile
