@@ -68,15 +68,18 @@ class HipEvents:
         return f.value
 
 
-def ffn_kernel_name(T: int, E: int, k: int) -> str:
-    """The W1 kernel the library picks for these sizes (its row-tile rule)."""
+def ffn_kernel_name(T: int, E: int, k: int, H: int) -> str:
+    """The W1 kernel the library picks for these sizes (its row-tile rule; the
+    80-row kernel stages E8M0 scales in LDS while they fit beside the activations
+    in 80 KB)."""
     if T <= 16 or T * k // E <= 8:
         return "gemm_stream_kernel<true, 1, true>"
     if T * k // E <= 24:
         return "gemm_stream_kernel<true, 2, true>"
     if T * k // E < 96:
-        return "gemm_tile_kernel<true, 4, 4>"
-    return "gemm_tile_kernel<true, 8, 8>"
+        lds_scales = 2 * 80 * 272 + 4 * (H // 128) * 64 * 4 <= 80 * 1024
+        return f"gemm_tile_kernel<true, 5, 4, 4, {'true' if lds_scales else 'false'}>"
+    return "gemm_tile_kernel<true, 8, 4, 8, false>"
 
 
 def measured_traffic(profile_name: str, kernel_source: str):
@@ -366,7 +369,7 @@ def main():
     # the two peaks (bf16 ridge: 312.5 FLOP/B).  Decode and the 48-row prefill sit
     # below it (HBM); experts with hundreds of rows sit above it (MFMA).
     w1_flops = 2.0 * T * k * 2 * I * H
-    kname = "W1 gate|up + clamped SwiGLU (" + ffn_kernel_name(T, E, k) + ")"
+    kname = "W1 gate|up + clamped SwiGLU (" + ffn_kernel_name(T, E, k, H) + ")"
     if w1_flops / w1_alg > BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
         tflops = w1_flops / (w1_ms * 1e-3) / 1e12
         roofline = {"bound": "mfma", "kernel": kname, "achieved": tflops,
