@@ -64,6 +64,7 @@ inline size_t tile_scale_lds_bytes(int K, int waves) {
   return static_cast<size_t>(waves) * (K / kFfnKChunk) * 64 * sizeof(uint32_t);
 }
 constexpr size_t kTileLdsPerWorkgroup = 80 * 1024;   // two workgroups per CU
+constexpr size_t kCuLds = 160 * 1024;                 // one workgroup per CU
 
 template <bool kW1, int kMSub, int kFrag, int kWaves, bool kLdsScales>
 __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
@@ -369,13 +370,23 @@ hipError_t launch_tile(bool w1, int tile_rows, int64_t tile_bound, hipStream_t s
                        int n_slots, const uint8_t* wq, const uint8_t* wsc, const RowTile* tiles,
                        const int32_t* n_tiles, int K, int n_rows, int half, float limit, int clamp,
                        uint16_t* out, int ld_out) {
-  if (tile_rows == 128)
-    return w1 ? launch_tile_t<true, 8, 4, 8, false>(tile_bound, stream, act, act_bytes, gather, k_top,
-                                          n_slots, wq, wsc, tiles, n_tiles, K, n_rows, half,
-                                          limit, clamp, out, ld_out)
-              : launch_tile_t<false, 8, 4, 8, false>(tile_bound, stream, act, act_bytes, gather, k_top,
-                                           n_slots, wq, wsc, tiles, n_tiles, K, n_rows, half,
-                                           limit, clamp, out, ld_out);
+  // 128-row tiles (one workgroup per CU) stage the scales in LDS while they fit
+  // beside the activation buffers in the CU's 160 KB (K <= 4096)
+  if (tile_rows == 128) {
+    if (2 * static_cast<size_t>(a_buf_bytes<8>()) + tile_scale_lds_bytes(K, 8) <= kCuLds)
+      return w1 ? launch_tile_t<true, 8, 4, 8, true>(tile_bound, stream, act, act_bytes, gather,
+                                                     k_top, n_slots, wq, wsc, tiles, n_tiles, K,
+                                                     n_rows, half, limit, clamp, out, ld_out)
+                : launch_tile_t<false, 8, 4, 8, true>(tile_bound, stream, act, act_bytes, gather,
+                                                      k_top, n_slots, wq, wsc, tiles, n_tiles, K,
+                                                      n_rows, half, limit, clamp, out, ld_out);
+    return w1 ? launch_tile_t<true, 8, 4, 8, false>(tile_bound, stream, act, act_bytes, gather,
+                                                    k_top, n_slots, wq, wsc, tiles, n_tiles, K,
+                                                    n_rows, half, limit, clamp, out, ld_out)
+              : launch_tile_t<false, 8, 4, 8, false>(tile_bound, stream, act, act_bytes, gather,
+                                                     k_top, n_slots, wq, wsc, tiles, n_tiles, K,
+                                                     n_rows, half, limit, clamp, out, ld_out);
+  }
   // 80-row tiles keep two workgroups per CU: the E8M0 scales are staged in LDS
   // while they fit beside the activation buffers in half the CU's LDS (K <= 4096
   // for 256-element rows of scales per wavefront), else they come with the weights
