@@ -135,17 +135,21 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
   }
   unsigned char* a_lds = tile_lds;                       // [2][kRows][kARowBytes]
   const int a_store = ar * kARowBytes + aq * 16;
-  auto load_a = [&](uint4 (&ra)[kPieces], int kc) {
+  // np: the pieces that hold rows of the subtiles a tile runs (a constant at each
+  // call site); pieces past them are neither loaded nor stored
+  auto load_a = [&](uint4 (&ra)[kPieces], int kc, int np) {
 #pragma unroll
     for (int i = 0; i < kPieces; ++i)
-      ra[i] = __builtin_bit_cast(
-          uint4, __builtin_amdgcn_raw_buffer_load_b128(arsrc, aoff[i] + kc * 256, 0, 0));
+      if (i < np)
+        ra[i] = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(arsrc, aoff[i] + kc * 256, 0, 0));
   };
-  auto store_a = [&](const uint4 (&ra)[kPieces], int buf) {
+  auto store_a = [&](const uint4 (&ra)[kPieces], int buf, int np) {
 #pragma unroll
     for (int i = 0; i < kPieces; ++i)
-      *reinterpret_cast<uint4*>(a_lds + buf * kABuf + a_store + kRowStride * i * kARowBytes) =
-          ra[i];
+      if (i < np)
+        *reinterpret_cast<uint4*>(a_lds + buf * kABuf + a_store + kRowStride * i * kARowBytes) =
+            ra[i];
   };
 
   // --- weights: kFrag fragments of 16 rows, this lane's row in each
@@ -253,23 +257,25 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
     // The K loop is instantiated for 2 .. 5 subtiles; the tile takes the smallest
     // that covers its rows (a uniform branch outside the loop)
     auto run = [&](auto ns_c) {
+      constexpr int NS = decltype(ns_c)::value;
+      constexpr int NP = (NS * 16 + kRowStride - 1) / kRowStride;   // pieces in use
       uint4 ra0[kPieces], ra1[kPieces];
-      load_a(ra0, 0);
+      load_a(ra0, 0, NP);
       load_w(q0, s0, 0);
       load_w(q1, s1, last >= 1 ? 1 : 0);
-      load_a(ra1, last >= 1 ? 1 : 0);
-      store_a(ra0, 0);
+      load_a(ra1, last >= 1 ? 1 : 0, NP);
+      store_a(ra0, 0, NP);
       __syncthreads();
       for (; kc + 2 <= n_chunks; kc += 2) {
-        load_a(ra0, kc + 2 <= last ? kc + 2 : last);
+        load_a(ra0, kc + 2 <= last ? kc + 2 : last, NP);
         compute(ns_c, q0, s0, kc, 0);
         load_w(q0, s0, kc + 2 <= last ? kc + 2 : last);
-        store_a(ra1, 1);
+        store_a(ra1, 1, NP);
         __syncthreads();
-        load_a(ra1, kc + 3 <= last ? kc + 3 : last);
+        load_a(ra1, kc + 3 <= last ? kc + 3 : last, NP);
         compute(ns_c, q1, s1, kc + 1, 1);
         load_w(q1, s1, kc + 3 <= last ? kc + 3 : last);
-        store_a(ra0, 0);
+        store_a(ra0, 0, NP);
         __syncthreads();
       }
       if (kc < n_chunks) compute(ns_c, q0, s0, kc, 0);   // odd chunk count: last chunk in q0
@@ -290,22 +296,24 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
     // expert, and every tile of an expert with few rows, runs only the MFMAs of
     // its rows
     auto run = [&](auto ns_c) {
+      constexpr int NS = decltype(ns_c)::value;
+      constexpr int NP = (NS * 16 + kRowStride - 1) / kRowStride;   // pieces in use
       uint4 ra[kPieces];
-      load_a(ra, 0);
+      load_a(ra, 0, NP);
       load_w(q0, s0, 0);
       load_w(q1, s1, last >= 1 ? 1 : 0);
-      store_a(ra, 0);
+      store_a(ra, 0, NP);
       __syncthreads();
       for (; kc + 2 <= n_chunks; kc += 2) {
-        load_a(ra, kc + 1);
+        load_a(ra, kc + 1, NP);
         compute(ns_c, q0, s0, kc, 0);
         load_w(q0, s0, kc + 2 <= last ? kc + 2 : last);
-        store_a(ra, 1);
+        store_a(ra, 1, NP);
         __syncthreads();
-        load_a(ra, kc + 2 <= last ? kc + 2 : last);
+        load_a(ra, kc + 2 <= last ? kc + 2 : last, NP);
         compute(ns_c, q1, s1, kc + 1, 1);
         load_w(q1, s1, kc + 3 <= last ? kc + 3 : last);
-        store_a(ra, 0);
+        store_a(ra, 0, NP);
         __syncthreads();
       }
       if (kc < n_chunks) compute(ns_c, q0, s0, kc, 0);   // odd chunk count
