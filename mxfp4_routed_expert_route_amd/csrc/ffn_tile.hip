@@ -192,14 +192,23 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
   if constexpr (kLdsScales) {
     const int f = lane >> 4;
     const uint8_t* srow = wsc + (e_rows + wrow(f, r16)) * row_s;
-    int c = 0;
-    for (; c + 4 <= n_chunks; c += 4) {
-      const uint4 d = *reinterpret_cast<const uint4*>(srow + c * 4);
+    // eight 16-byte loads in flight before their stores: a load-then-store loop
+    // would wait one memory latency per iteration
+    auto put = [&](int c, const uint4& d) {
       my_scales[((c + 0) * 16 + r16) * 4 + f] = d.x;
       my_scales[((c + 1) * 16 + r16) * 4 + f] = d.y;
       my_scales[((c + 2) * 16 + r16) * 4 + f] = d.z;
       my_scales[((c + 3) * 16 + r16) * 4 + f] = d.w;
+    };
+    int c = 0;
+    for (; c + 32 <= n_chunks; c += 32) {
+      uint4 d[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) d[j] = *reinterpret_cast<const uint4*>(srow + (c + 4 * j) * 4);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) put(c + 4 * j, d[j]);
     }
+    for (; c + 4 <= n_chunks; c += 4) put(c, *reinterpret_cast<const uint4*>(srow + c * 4));
     for (; c < n_chunks; ++c)
       my_scales[(c * 16 + r16) * 4 + f] = *reinterpret_cast<const uint32_t*>(srow + c * 4);
   }
