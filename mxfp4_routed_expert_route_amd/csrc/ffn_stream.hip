@@ -138,14 +138,25 @@ void gemm_stream_kernel(
     // my_scales[((c2*16 + L%16)*4 + f)*2 + {0,1}]
     const int f = lane >> 4;
     const uint8_t* srow = wsc + (e_rows + wrow(f, r16)) * row_s;
-    for (int c = 0; c < n_chunks; c += 4) {   // c counts 128-element chunks
-      const uint4 d = *reinterpret_cast<const uint4*>(srow + c * 4);
+    auto put = [&](int c, const uint4& d) {   // c counts 128-element chunks
       const int c2 = c / 2;
       my_scales[(((c2 + 0) * 16 + r16) * 4 + f) * 2 + 0] = d.x;
       my_scales[(((c2 + 0) * 16 + r16) * 4 + f) * 2 + 1] = d.y;
       my_scales[(((c2 + 1) * 16 + r16) * 4 + f) * 2 + 0] = d.z;
       my_scales[(((c2 + 1) * 16 + r16) * 4 + f) * 2 + 1] = d.w;
+    };
+    // four 16-byte loads in flight before their stores (a load-then-store loop
+    // waits one memory latency per iteration, with every wavefront of the grid
+    // in this prologue at once; eight would exceed the register budget)
+    int c = 0;
+    for (; c + 16 <= n_chunks; c += 16) {
+      uint4 d[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) d[j] = *reinterpret_cast<const uint4*>(srow + (c + 4 * j) * 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) put(c + 4 * j, d[j]);
     }
+    for (; c < n_chunks; c += 4) put(c, *reinterpret_cast<const uint4*>(srow + c * 4));
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
