@@ -17,12 +17,13 @@ namespace {
 // (kMSub*16 rows x 128 bf16) is loaded once per workgroup into LDS
 // (double-buffered; rows padded by 16 bytes so that the 16 lanes of a read group
 // hit distinct banks) and read by all its wavefronts.  Weights go straight to
-// registers, issued right after the chunk that frees their registers.  With
-// 80-row tiles the E8M0 scales are staged in LDS as in the streaming kernel
-// while they fit beside the activation buffers (K <= 4096);
-// with 128-row tiles the LDS holds only activations and the scales come with the
-// weights.  Each tile runs only the 16-row subtiles that hold rows (the K loop is
-// instantiated per subtile count).
+// registers, issued right after the chunk that frees their registers.  The E8M0
+// scales of the wavefronts' weight rows are staged in LDS for all of K while they
+// fit beside the activation buffers (K <= 4096 for both shapes; staging them
+// took the 128-row kernel's loop off four scale loads per chunk, 11% of the
+// skewed layer); beyond that they come with the weights.  Each tile runs only
+// the 16-row subtiles that hold rows and stages only their activation rows (the
+// K loop is instantiated per subtile count).
 //
 // Two shapes are used:
 //  * 80 x 256 (kMSub 5, four wavefronts, two workgroups per CU) for experts of
