@@ -74,8 +74,9 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
     const RowTile* __restrict__ tiles, const int32_t* __restrict__ n_tiles, int K, int n_rows,
     int half, int waves_per_tile, int blocks_per_tile, float limit, int clamp,
     uint16_t* __restrict__ out, int ld_out) {
-  static_assert(kFrag == 4 || kFrag == 8, "four or eight weight fragments per wavefront");
-  static_assert(!kLdsScales || kFrag == 4, "LDS scale staging holds four fragments");
+  // the fragment count is a parameter of the indexing below, but only four
+  // fragments per wavefront (64 weight rows) are instantiated and tested
+  static_assert(kFrag == 4, "four weight fragments per wavefront");
   constexpr int kRows = kMSub * 16;
   constexpr int kABuf = a_buf_bytes<kMSub>();
   constexpr int kThreads = 64 * kWaves;
@@ -375,7 +376,8 @@ hipError_t launch_tile_t(int64_t tile_bound, hipStream_t stream, const uint16_t*
   // the column-block/XCD split covers row tiles in pairs: round up to whole pairs
   const int64_t blocks =
       (bpt == 16 || bpt == 8) ? (tile_bound + 1) / 2 * 2 * bpt : tile_bound * bpt;
-  gemm_tile_kernel<kW1, kMSub, kFrag, kWaves, kLdsScales><<<static_cast<unsigned>(blocks), 64 * kWaves, lds, stream>>>(
+  gemm_tile_kernel<kW1, kMSub, kFrag, kWaves, kLdsScales>
+      <<<static_cast<unsigned>(blocks), 64 * kWaves, lds, stream>>>(
       act, act_bytes, gather, k_top, n_slots, wq, wsc, tiles, n_tiles, K, n_rows, half, wpt, bpt,
       limit, clamp, out, ld_out);
   return hipGetLastError();
