@@ -141,6 +141,7 @@ def test_workload0_whole_layer(limit):
     (290, 8, 2, 256, 256, 19),       # 80-row tiles, experts of ~60-85 rows: 4 and 5 subtiles
     (100, 8, 2, 8192, 256, 18),      # 80-row tiles, W1 K = 8192: E8M0 scales come with the
                                      # weights (they do not fit in LDS beside the activations)
+    (200, 4, 2, 8192, 256, 20),      # 128-row tiles, W1 K = 8192: the same fallback there
     (300, 8, 3, 384, 640, 17),       # 128-row tiles (112 rows per expert): W1 3 chunks, 20
                                      # wavefronts per tile (last workgroup part-idle); W2 5
                                      # chunks, 6 wavefronts per tile
