@@ -196,8 +196,9 @@ moe_status moe_route_and_group(const float* logits, int64_t T, int32_t E, int32_
  * moe_forward_mxfp4 -- the whole layer in one call: exactly the outputs of
  * moe_route_and_group, moe_grouped_ffn_mxfp4 and moe_combine on the same
  * arguments (see those calls for each output's definition, layout, alignment
- * and citation).  For T <= 64 the one-launch front-end also writes the FFN's
- * row-tile plan, so the layer is four kernel launches instead of five.  ws is
+ * and citation).  The FFN's row-tile plan is written by the routing side where
+ * it holds the counts in one workgroup -- the one-launch front-end for T <= 64,
+ * the expert-offsets scan for T > 512 -- which saves the FFN its plan launch.  ws is
  * the workspace of those calls (moe_workspace_bytes).  T = 0 writes zeros to
  * counts and offsets and nothing else.
  */

@@ -9,6 +9,7 @@
 // LDS activation tile.
 #include "ffn_common.h"
 #include "launch.h"
+#include "plan.h"
 
 namespace moe {
 namespace {
@@ -21,7 +22,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
                                                     int32_t* __restrict__ n_tiles,
                                                     RowTile* __restrict__ tiles) {
   __shared__ int wave_tot[16];
-  const int e = threadIdx.x, lane = e & 63, wave = e >> 6;
+  const int e = threadIdx.x;
   int c = 0, begin = 0;
   if (e < E) {
     c = counts[e];
@@ -29,32 +30,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
     if (c < 0 || begin < 0 || begin > n_slots) c = 0;
     if (static_cast<int64_t>(begin) + c > n_slots) c = static_cast<int>(n_slots - begin);
   }
-  const int nt = (c + tile_rows - 1) / tile_rows;
-  int incl = nt;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int o = __shfl_up(incl, d, 64);
-    if (lane >= d) incl += o;
-  }
-  if (lane == 63) wave_tot[wave] = incl;
-  __syncthreads();
-  int base = 0;
-  for (int w = 0; w < wave; ++w) base += wave_tot[w];
-  const int first = base + incl - nt;
-  for (int i = 0; i < nt; ++i) {
-    const int64_t slot = static_cast<int64_t>(first) + i;
-    if (slot >= tile_bound) break;
-    RowTile rt;
-    rt.expert = e;
-    rt.p_begin = begin + i * tile_rows;
-    rt.p_end = (i + 1) * tile_rows < c ? begin + (i + 1) * tile_rows : begin + c;
-    rt.pad = 0;
-    tiles[slot] = rt;
-  }
-  if (e == blockDim.x - 1) {
-    const int64_t total = base + incl;
-    *n_tiles = static_cast<int32_t>(total < tile_bound ? total : tile_bound);
-  }
+  write_tile_plan(e, E, c, begin, tile_rows, tile_bound, n_tiles, tiles, wave_tot);
 }
 
 }  // namespace

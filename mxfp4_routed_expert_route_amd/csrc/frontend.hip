@@ -153,7 +153,8 @@ hipError_t launch_route_and_group(const float* logits, int64_t T, int E, int k, 
     if (err != hipSuccess) return err;
     err = launch_bitmatrix(ids, T, E, k, bm, stream);
     if (err != hipSuccess) return err;
-    return launch_offsets(bm, ids, T, E, k, counts, offsets, gather, scatter, ws, stream);
+    return launch_offsets(bm, ids, T, E, k, counts, offsets, gather, scatter, ws, stream, plan,
+                          plan_written);
   }
   const int words = (E + 31) / 32;
   const int epl = (E + 63) / 64;

@@ -13,9 +13,14 @@ hipError_t launch_route(const float* logits, int64_t T, int E, int k, int32_t* i
 hipError_t launch_bitmatrix(const int32_t* ids, int64_t T, int E, int k, uint32_t* bm,
                             hipStream_t stream);
 
+struct PlanOut;
+
+// With plan != nullptr and T above one offsets block (512 tokens), the scan step
+// also writes the FFN's row-tile plan and sets *plan_written.
 hipError_t launch_offsets(const uint32_t* bm, const int32_t* ids, int64_t T, int E, int k,
                           int32_t* counts, int32_t* offsets, int32_t* gather, int32_t* scatter,
-                          void* ws, hipStream_t stream);
+                          void* ws, hipStream_t stream, const PlanOut* plan = nullptr,
+                          bool* plan_written = nullptr);
 
 hipError_t launch_ffn(const uint16_t* x, int64_t T, int H, int I, int E, int k,
                       const uint8_t* w1, const uint8_t* w1s, const uint8_t* w2,
@@ -35,7 +40,8 @@ struct PlanOut {
 };
 
 // With plan != nullptr the one-launch path (T <= 64) also writes the FFN plan and
-// sets *plan_written; larger T runs the separate kernels and writes no plan.
+// sets *plan_written; larger T runs the separate kernels, whose scan step writes
+// the plan above 512 tokens.
 hipError_t launch_route_and_group(const float* logits, int64_t T, int E, int k, int32_t* ids,
                                   float* weights, uint32_t* bm, int32_t* counts, int32_t* offsets,
                                   int32_t* gather, int32_t* scatter, void* ws, hipStream_t stream,

@@ -16,6 +16,7 @@
 // offsets, and ranks writes the permutations.
 #include "config.h"
 #include "launch.h"
+#include "plan.h"
 #include "routing_core.h"
 
 namespace moe {
@@ -106,9 +107,13 @@ __global__ __launch_bounds__(kOffsBlockTokens) void block_counts_kernel(
 
 // One workgroup of 1024 threads: thread e turns expert e's per-block counts into
 // exclusive per-block bases (in place) and its total; a scan over e gives offsets.
+// With tiles != nullptr (the one-call layer) it also writes the FFN's row-tile
+// plan from the counts and offsets it holds, which saves the FFN its plan launch.
 __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ blk, int64_t n_blocks,
                                                     int E, int32_t* __restrict__ counts,
-                                                    int32_t* __restrict__ offsets) {
+                                                    int32_t* __restrict__ offsets, int tile_rows,
+                                                    int64_t tile_bound, int32_t* __restrict__ n_tiles,
+                                                    RowTile* __restrict__ tiles) {
   __shared__ int wave_tot[16];
   const int e = threadIdx.x;
   int run = 0;
@@ -134,6 +139,10 @@ __global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ blk, i
   const int first = block_exclusive_scan(run, wave_tot, &total);
   if (e < E) offsets[e] = first;
   if (e == 0) offsets[E] = total;
+  if (tiles != nullptr) {   // uniform
+    __syncthreads();        // wave_tot is reused
+    write_tile_plan(e, E, run, first, tile_rows, tile_bound, n_tiles, tiles, wave_tot);
+  }
 }
 
 __global__ __launch_bounds__(kOffsBlockTokens) void ranks_kernel(
@@ -170,7 +179,8 @@ __global__ void zero_counts_kernel(int32_t* counts, int32_t* offsets, int E) {
 
 hipError_t launch_offsets(const uint32_t* bm, const int32_t* ids, int64_t T, int E, int k,
                           int32_t* counts, int32_t* offsets, int32_t* gather, int32_t* scatter,
-                          void* ws, hipStream_t stream) {
+                          void* ws, hipStream_t stream, const PlanOut* plan, bool* plan_written) {
+  if (plan_written) *plan_written = false;
   if (T == 0) {
     zero_counts_kernel<<<1, 256, 0, stream>>>(counts, offsets, E);
     return hipGetLastError();
@@ -189,9 +199,13 @@ hipError_t launch_offsets(const uint32_t* bm, const int32_t* ids, int64_t T, int
   block_counts_kernel<<<grid, block, lds_masks, stream>>>(bm, T, E, words, blk);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  scan_kernel<<<1, 1024, 0, stream>>>(blk, n_blocks, E, counts, offsets);
+  RowTile* tiles = plan ? static_cast<RowTile*>(plan->tiles) : nullptr;
+  scan_kernel<<<1, 1024, 0, stream>>>(blk, n_blocks, E, counts, offsets,
+                                      plan ? plan->tile_rows : 1, plan ? plan->tile_bound : 0,
+                                      plan ? plan->n_tiles : nullptr, tiles);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
+  if (plan_written) *plan_written = tiles != nullptr;
   ranks_kernel<<<grid, block, lds_masks + lds_base, stream>>>(bm, ids, T, E, k, words, blk,
                                                               offsets, gather, scatter);
   return hipGetLastError();

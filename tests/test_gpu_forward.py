@@ -3,7 +3,8 @@
 Every output must match the separate-call chain (moe_route_and_group,
 moe_grouped_ffn_mxfp4, moe_combine) bit for bit: the same kernels run, except
 that for T <= 64 the one-launch front-end also writes the FFN's row-tile plan in
-place of the FFN's plan kernel.  The cases cover each tile kind the plan can
+place of the FFN's plan kernel, and above 512 tokens the expert-offsets scan
+does.  The cases cover each tile kind the plan can
 hold (16- and 32-row streaming tiles, 80-row LDS tiles; 128-row tiles, which
 need more than 64 tokens) on both sides of the T = 64 front-end limit, and T = 0.
 """
@@ -49,7 +50,7 @@ def _compare(inp, limit=10.0):
         assert torch.equal(_bits(getattr(a, name)), _bits(getattr(b, name))), name
 
 
-@pytest.mark.parametrize("index", [0, 1])
+@pytest.mark.parametrize("index", [0, 1, 3, 4])   # 3, 4: the scan writes the plan
 def test_forward_matches_separate_calls_workloads(index):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
@@ -63,6 +64,9 @@ def test_forward_matches_separate_calls_workloads(index):
     (64, 16, 8, 256, 256, 44),       # 32 rows per expert: 80-row LDS tiles, front-end plan
     (65, 16, 8, 256, 256, 45),       # past the one-launch limit: plan kernel
     (300, 8, 3, 256, 256, 48),       # 112 rows per expert: 128-row tiles, plan kernel
+    (600, 16, 2, 256, 256, 49),      # past one offsets block (512 tokens): the scan writes
+                                     # the plan (80-row tiles)
+    (1100, 8, 3, 256, 256, 50),      # three offsets blocks, 128-row tiles from the scan's plan
     (33, 1024, 8, 128, 128, 46),     # maximum E and k
 ])
 def test_forward_matches_separate_calls(T, E, k, H, I, seed):
