@@ -70,7 +70,9 @@ hipError_t launch_ffn(const uint16_t* x, int64_t T, int H, int I, int E, int k,
   }
 
   if (tile_rows <= 32) {
-    const int wpt1 = I / 32, wpt2 = H / 64;
+    // W1: 8 * frags gate rows (and as many up rows) per wavefront; W2: 16 * frags rows
+    const int frags = stream_frags(tile_rows / 16);
+    const int wpt1 = I / (8 * frags), wpt2 = H / (16 * frags);
     const unsigned g1 = static_cast<unsigned>((tile_bound * wpt1 + 3) / 4);
     const unsigned g2 = static_cast<unsigned>((tile_bound * wpt2 + 3) / 4);
     const RowTile* t = tiles;

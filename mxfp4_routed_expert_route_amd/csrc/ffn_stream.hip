@@ -8,8 +8,10 @@ namespace {
 //
 // For row tiles of at most 16*MSUB rows (decode and small batches, where each
 // expert has few rows and the weights are read once): one wavefront owns a row
-// tile and 64 weight rows (W1: 32 gate rows and the 32 matching up rows; W2: 64
-// output rows), so many wavefronts stay resident per CU.
+// tile and 16*kFrag weight rows (W1: 8*kFrag gate rows and the matching up rows;
+// W2: 16*kFrag output rows), so many wavefronts stay resident per CU.  16-row
+// tiles use two fragments per wavefront: finer work units balance the CUs
+// better (5,888 wavefronts instead of 2,944 for the verify step's W1).
 //
 // Memory pipeline (kDeep, K a multiple of 512).  K advances in chunks of 256
 // elements: each lane takes 32 bytes (two scale blocks) of each of its four rows,
@@ -33,7 +35,7 @@ namespace {
 // keeps the compiler's wait counts exact.
 // Otherwise (small K): 128-element chunks, one-chunk prefetch, scales from memory.
 // Three wavefronts per SIMD (12 per CU) with 16-row tiles, two with 32-row tiles.
-template <bool kW1, int MSUB, bool kDeep>
+template <bool kW1, int MSUB, bool kDeep, int kFrag>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MSUB == 1 ? 3 : 2)))
 void gemm_stream_kernel(
     const uint16_t* __restrict__ act, uint32_t act_bytes, const int32_t* __restrict__ gather,
@@ -53,6 +55,8 @@ void gemm_stream_kernel(
   const RowTile rt = tiles[tile_id];
   const int r16 = lane & 15, g = lane >> 4;
   const int n_chunks = K / kFfnKChunk;
+  static_assert(kFrag == 2 || kFrag == 4, "two or four 16-row weight fragments per wavefront");
+  constexpr int kGate = kFrag / 2;   // W1: gate fragments (the up fragments follow)
 
   const __amdgpu_buffer_rsrc_t arsrc = make_rsrc(act, act_bytes);
   uint32_t aoff[MSUB];   // byte offset of this lane's activation run in chunk 0
@@ -118,23 +122,24 @@ void gemm_stream_kernel(
   const int a_step = r16 < nvalid ? 512 : 0;
 
   // weight row of fragment f for a lane whose MFMA column is c16
-  auto wrow = [&](int f, int c16) {
-    return kW1 ? (f >= 2 ? half : 0) + cg * 32 + (f & 1) * 16 + c16   // gate, gate, up, up
-               : cg * 64 + f * 16 + c16;
+  auto wrow = [&](int f, int c16) {   // W1: gate fragments, then the matching up fragments
+    return kW1 ? (f >= kGate ? half : 0) + cg * (16 * kGate) + (f % kGate) * 16 + c16
+               : cg * (16 * kFrag) + f * 16 + c16;
   };
-  int nrow[4];
+  int nrow[kFrag];
 #pragma unroll
-  for (int f = 0; f < 4; ++f) nrow[f] = wrow(f, r16);
+  for (int f = 0; f < kFrag; ++f) nrow[f] = wrow(f, r16);
   const size_t row_q = static_cast<size_t>(K / 2), row_s = static_cast<size_t>(K / 32);
   const size_t e_rows = static_cast<size_t>(rt.expert) * n_rows;
-  const uint8_t* bq[4];
+  const uint8_t* bq[kFrag];
 #pragma unroll
-  for (int f = 0; f < 4; ++f) bq[f] = wq + (e_rows + nrow[f]) * row_q + (kDeep ? 0 : 16 * g);
+  for (int f = 0; f < kFrag; ++f) bq[f] = wq + (e_rows + nrow[f]) * row_q + (kDeep ? 0 : 16 * g);
 
   uint32_t* my_scales = scale_lds + (threadIdx.x >> 6) * (n_chunks * 64);
-  if (kDeep) {
-    // lane L stages the scales of row (f = L/16, column L%16).  The 8 scale bytes
-    // of a 256-element chunk c2 (2 per lane group) go to the two dwords
+  if (kDeep && (lane >> 4) < kFrag) {
+    // lane L stages the scales of row (f = L/16, column L%16); with two fragments
+    // per wavefront lanes 32..63 have no row.  The 8 scale bytes of a 256-element
+    // chunk c2 (2 per lane group) go to the two dwords
     // my_scales[((c2*16 + L%16)*4 + f)*2 + {0,1}]
     const int f = lane >> 4;
     const uint8_t* srow = wsc + (e_rows + wrow(f, r16)) * row_s;
@@ -157,33 +162,35 @@ void gemm_stream_kernel(
       for (int j = 0; j < 4; ++j) put(c + 4 * j, d[j]);
     }
     for (; c < n_chunks; c += 4) put(c, *reinterpret_cast<const uint4*>(srow + c * 4));
+  }
+  if (kDeep) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
-  const uint8_t* bs[4];
+  const uint8_t* bs[kFrag];
 #pragma unroll
-  for (int f = 0; f < 4; ++f) bs[f] = wsc + (e_rows + nrow[f]) * row_s + g;
+  for (int f = 0; f < kFrag; ++f) bs[f] = wsc + (e_rows + nrow[f]) * row_s + g;
 
-  floatx4 acc[MSUB][4];
+  floatx4 acc[MSUB][kFrag];
 #pragma unroll
   for (int mi = 0; mi < MSUB; ++mi)
 #pragma unroll
-    for (int f = 0; f < 4; ++f) acc[mi][f] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int f = 0; f < kFrag; ++f) acc[mi][f] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  auto load_w = [&](uint4 (&q)[4], int kc) {
+  auto load_w = [&](uint4 (&q)[kFrag], int kc) {
 #pragma unroll
-    for (int f = 0; f < 4; ++f) q[f] = *reinterpret_cast<const uint4*>(bq[f] + kc * 64);
+    for (int f = 0; f < kFrag; ++f) q[f] = *reinterpret_cast<const uint4*>(bq[f] + kc * 64);
   };
-  auto load_s = [&](uint32_t (&sc)[4], int kc) {   // from memory (shallow pipeline)
+  auto load_s = [&](uint32_t (&sc)[kFrag], int kc) {   // from memory (shallow pipeline)
 #pragma unroll
-    for (int f = 0; f < 4; ++f) sc[f] = bs[f][kc * 4];
+    for (int f = 0; f < kFrag; ++f) sc[f] = bs[f][kc * 4];
   };
-  auto lds_s = [&](uint32_t (&sc)[4], int kc) {    // from the staged copy
+  auto lds_s = [&](uint32_t (&sc)[kFrag], int kc) {    // from the staged copy
     const uint4 d = *reinterpret_cast<const uint4*>(my_scales + (kc * 16 + r16) * 4);
     const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
 #pragma unroll
-    for (int f = 0; f < 4; ++f) sc[f] = (dw[f] >> (8 * g)) & 0xFFu;
+    for (int f = 0; f < kFrag; ++f) sc[f] = (dw[f] >> (8 * g)) & 0xFFu;
   };
   auto load_a = [&](bf16x8 (&a)[MSUB][4], int kc) {
 #pragma unroll
@@ -193,18 +200,20 @@ void gemm_stream_kernel(
         a[mi][s] = __builtin_bit_cast(
             bf16x8, __builtin_amdgcn_raw_buffer_load_b128(arsrc, aoff[mi] + kc * 256 + 16 * s, 0, 0));
   };
-  auto compute = [&](const uint4 (&q)[4], const uint32_t (&sc)[4], const bf16x8 (&a)[MSUB][4]) {
-    const uint32_t w[4][4] = {{q[0].x, q[0].y, q[0].z, q[0].w},
-                              {q[1].x, q[1].y, q[1].z, q[1].w},
-                              {q[2].x, q[2].y, q[2].z, q[2].w},
-                              {q[3].x, q[3].y, q[3].z, q[3].w}};
-    float scl[4];
+  auto compute = [&](const uint4 (&q)[kFrag], const uint32_t (&sc)[kFrag],
+                     const bf16x8 (&a)[MSUB][4]) {
+    uint32_t w[kFrag][4];
 #pragma unroll
-    for (int f = 0; f < 4; ++f) scl[f] = e8m0_as_f32(sc[f]);
+    for (int f = 0; f < kFrag; ++f) {
+      w[f][0] = q[f].x; w[f][1] = q[f].y; w[f][2] = q[f].z; w[f][3] = q[f].w;
+    }
+    float scl[kFrag];
+#pragma unroll
+    for (int f = 0; f < kFrag; ++f) scl[f] = e8m0_as_f32(sc[f]);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
-      for (int f = 0; f < 4; ++f) {
+      for (int f = 0; f < kFrag; ++f) {
         const bf16x8 b = dequant8(w[f][s], scl[f]);
 #pragma unroll
         for (int mi = 0; mi < MSUB; ++mi)
@@ -217,9 +226,9 @@ void gemm_stream_kernel(
     // 256-element chunks, two weight register stages; `run` is the K loop for the
     // LDS-held rows and the per-wavefront activation loads, `run_ring` for the ring.
     const int n2 = n_chunks / 2;   // 256-element chunks (even: n_chunks % 4 == 0)
-    auto load_w2 = [&](uint4 (&q)[4][2], int c2) {
+    auto load_w2 = [&](uint4 (&q)[kFrag][2], int c2) {
 #pragma unroll
-      for (int f = 0; f < 4; ++f) {
+      for (int f = 0; f < kFrag; ++f) {
         const uint8_t* src = bq[f] + c2 * 128 + 32 * g;   // lane group g: bytes 32g..32g+31
         q[f][0] = *reinterpret_cast<const uint4*>(src);
         q[f][1] = *reinterpret_cast<const uint4*>(src + 16);
@@ -238,24 +247,29 @@ void gemm_stream_kernel(
       for (int t = 0; t < 8; ++t)
         a[0][t] = *reinterpret_cast<const bf16x8*>(a_mine + c2 * a_step + 16 * t);
     };
-    auto compute2 = [&](const uint4 (&q)[4][2], const bf16x8 (&a)[MSUB][8], int c2) {
+    auto compute2 = [&](const uint4 (&q)[kFrag][2], const bf16x8 (&a)[MSUB][8], int c2) {
+      // the staged layout keeps four fragments per row slot; with two fragments
+      // per wavefront only the first half of each slot is read
       const uint4 d0 = *reinterpret_cast<const uint4*>(my_scales + ((c2 * 16 + r16) * 4) * 2);
-      const uint4 d1 = *reinterpret_cast<const uint4*>(my_scales + ((c2 * 16 + r16) * 4) * 2 + 4);
+      uint4 d1 = d0;
+      if constexpr (kFrag == 4)
+        d1 = *reinterpret_cast<const uint4*>(my_scales + ((c2 * 16 + r16) * 4) * 2 + 4);
       const uint32_t sd[4][2] = {{d0.x, d0.y}, {d0.z, d0.w}, {d1.x, d1.y}, {d1.z, d1.w}};
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        float scl[4];
+        float scl[kFrag];
 #pragma unroll
-        for (int f = 0; f < 4; ++f)   // block 2g + j of the chunk: byte (2g+j)%4 of dword (2g+j)/4
+        for (int f = 0; f < kFrag; ++f)   // block 2g + j of the chunk: byte (2g+j)%4 of dword (2g+j)/4
           scl[f] = e8m0_as_f32((sd[f][(2 * g + j) >> 2] >> (8 * ((2 * g + j) & 3))) & 0xFFu);
-        const uint32_t w[4][4] = {{q[0][j].x, q[0][j].y, q[0][j].z, q[0][j].w},
-                                  {q[1][j].x, q[1][j].y, q[1][j].z, q[1][j].w},
-                                  {q[2][j].x, q[2][j].y, q[2][j].z, q[2][j].w},
-                                  {q[3][j].x, q[3][j].y, q[3][j].z, q[3][j].w}};
+        uint32_t w[kFrag][4];
+#pragma unroll
+        for (int f = 0; f < kFrag; ++f) {
+          w[f][0] = q[f][j].x; w[f][1] = q[f][j].y; w[f][2] = q[f][j].z; w[f][3] = q[f][j].w;
+        }
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
 #pragma unroll
-          for (int f = 0; f < 4; ++f) {
+          for (int f = 0; f < kFrag; ++f) {
             const bf16x8 b = dequant8(w[f][s], scl[f]);
 #pragma unroll
             for (int mi = 0; mi < MSUB; ++mi)
@@ -266,7 +280,7 @@ void gemm_stream_kernel(
       }
     };
     auto run = [&](auto&& load_a) __attribute__((always_inline)) {
-      uint4 q0[4][2], q1[4][2];
+      uint4 q0[kFrag][2], q1[kFrag][2];
       load_w2(q0, 0);
       __builtin_amdgcn_sched_barrier(0);
       for (int c2 = 0; c2 < n2; c2 += 2) {
@@ -328,7 +342,7 @@ void gemm_stream_kernel(
                                                         16 * t);
       };
       uint4 sa[kPc];
-      uint4 q0[4][2], q1[4][2];
+      uint4 q0[kFrag][2], q1[kFrag][2];
       stage_load(sa, 0);
       __builtin_amdgcn_sched_barrier(0);
       load_w2(q0, 0);
@@ -363,8 +377,8 @@ void gemm_stream_kernel(
     else
       run(load_a2);
   } else {
-    uint4 qa[4], qb[4];
-    uint32_t sa[4], sb[4];
+    uint4 qa[kFrag], qb[kFrag];
+    uint32_t sa[kFrag], sb[kFrag];
     load_w(qa, 0);
     load_s(sa, 0);
     int kc = 0;
@@ -404,18 +418,20 @@ void gemm_stream_kernel(
       if (p >= rt.p_end) continue;
       uint16_t* orow = out + static_cast<int64_t>(p) * ld_out;
       if (kW1) {
-        orow[nrow[0]] = f32_to_bf16_bits(swiglu(acc[mi][0][i], acc[mi][2][i], limit, do_clamp));
-        orow[nrow[1]] = f32_to_bf16_bits(swiglu(acc[mi][1][i], acc[mi][3][i], limit, do_clamp));
+#pragma unroll
+        for (int f = 0; f < kGate; ++f)
+          orow[nrow[f]] =
+              f32_to_bf16_bits(swiglu(acc[mi][f][i], acc[mi][f + kGate][i], limit, do_clamp));
       } else {
 #pragma unroll
-        for (int f = 0; f < 4; ++f) orow[nrow[f]] = f32_to_bf16_bits(acc[mi][f][i]);
+        for (int f = 0; f < kFrag; ++f) orow[nrow[f]] = f32_to_bf16_bits(acc[mi][f][i]);
       }
     }
   }
 }
 
 // Launch one streaming GEMM; picks the deep pipeline when K allows it.
-template <bool kW1, int MSUB>
+template <bool kW1, int MSUB, int kFrag>
 hipError_t launch_stream_t(unsigned grid, hipStream_t stream, const uint16_t* act, uint32_t act_bytes,
                          const int32_t* gather, int k_top, int n_slots, const uint8_t* wq,
                          const uint8_t* wsc, const RowTile* tiles, const int32_t* n_tiles, int K,
@@ -438,11 +454,11 @@ hipError_t launch_stream_t(unsigned grid, hipStream_t stream, const uint16_t* ac
   const int a_ring = wpt % 4 == 0 && lds + ring_bytes <= budget ? 1 : 0;
   if (a_ring && ring_bytes > a_bytes) a_bytes = ring_bytes;
   if (n_chunks % 4 == 0 && lds <= kStreamMaxScaleLds)
-    gemm_stream_kernel<kW1, MSUB, true><<<grid, 256, lds + a_bytes, stream>>>(
+    gemm_stream_kernel<kW1, MSUB, true, kFrag><<<grid, 256, lds + a_bytes, stream>>>(
         act, act_bytes, gather, k_top, n_slots, wq, wsc, tiles, n_tiles, K, n_rows, half, wpt,
         limit, clamp, out, ld_out, a_rows, a_ring);
   else
-    gemm_stream_kernel<kW1, MSUB, false><<<grid, 256, 0, stream>>>(
+    gemm_stream_kernel<kW1, MSUB, false, kFrag><<<grid, 256, 0, stream>>>(
         act, act_bytes, gather, k_top, n_slots, wq, wsc, tiles, n_tiles, K, n_rows, half, wpt,
         limit, clamp, out, ld_out, 0, 0);
   return hipGetLastError();
@@ -456,18 +472,22 @@ hipError_t launch_stream(bool w1, int msub, unsigned grid, hipStream_t stream, c
                          const int32_t* n_tiles, int K, int n_rows, int half, int wpt, float limit,
                          int clamp, uint16_t* out, int ld_out) {
   if (w1)
-    return msub == 1 ? launch_stream_t<true, 1>(grid, stream, act, act_bytes, gather, k_top,
-                                                n_slots, wq, wsc, tiles, n_tiles, K, n_rows, half,
-                                                wpt, limit, clamp, out, ld_out)
-                     : launch_stream_t<true, 2>(grid, stream, act, act_bytes, gather, k_top,
-                                                n_slots, wq, wsc, tiles, n_tiles, K, n_rows, half,
-                                                wpt, limit, clamp, out, ld_out);
-  return msub == 1 ? launch_stream_t<false, 1>(grid, stream, act, act_bytes, gather, k_top,
-                                               n_slots, wq, wsc, tiles, n_tiles, K, n_rows, half,
-                                               wpt, limit, clamp, out, ld_out)
-                   : launch_stream_t<false, 2>(grid, stream, act, act_bytes, gather, k_top,
-                                               n_slots, wq, wsc, tiles, n_tiles, K, n_rows, half,
-                                               wpt, limit, clamp, out, ld_out);
+    return msub == 1
+               ? launch_stream_t<true, 1, kStreamFrags16>(grid, stream, act, act_bytes, gather,
+                                                          k_top, n_slots, wq, wsc, tiles, n_tiles,
+                                                          K, n_rows, half, wpt, limit, clamp, out,
+                                                          ld_out)
+               : launch_stream_t<true, 2, 4>(grid, stream, act, act_bytes, gather, k_top, n_slots,
+                                             wq, wsc, tiles, n_tiles, K, n_rows, half, wpt, limit,
+                                             clamp, out, ld_out);
+  return msub == 1
+             ? launch_stream_t<false, 1, kStreamFrags16>(grid, stream, act, act_bytes, gather,
+                                                         k_top, n_slots, wq, wsc, tiles, n_tiles,
+                                                         K, n_rows, half, wpt, limit, clamp, out,
+                                                         ld_out)
+             : launch_stream_t<false, 2, 4>(grid, stream, act, act_bytes, gather, k_top, n_slots,
+                                            wq, wsc, tiles, n_tiles, K, n_rows, half, wpt, limit,
+                                            clamp, out, ld_out);
 }
 
 }  // namespace moe
