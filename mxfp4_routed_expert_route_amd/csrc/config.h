@@ -22,10 +22,13 @@ constexpr int kFfnKChunk = 128;
 // 64 rows x K/32 bytes); above this the scales are read from memory
 constexpr size_t kStreamMaxScaleLds = 64 * 1024;
 // streaming path: row tiles whose activation rows (all of K) fit beside the
-// staged scales within this much LDS per workgroup (three per CU) keep them in LDS
+// staged scales within this much LDS per workgroup (three per CU: 16-row tiles
+// with four fragments per wavefront) keep them in LDS
 constexpr size_t kStreamMaxLds = 53 * 1024;
 // the same with 32-row tiles (two workgroups per CU)
 constexpr size_t kStreamMaxLds2 = 80 * 1024;
+// 16-row tiles with two weight fragments per wavefront (four workgroups per CU)
+constexpr size_t kStreamMaxLds4 = 40 * 1024;
 
 // Upper bound on the row tiles of n_slots rows over E experts cut into tiles of
 // tile_rows rows: at most one partial tile per non-empty expert.

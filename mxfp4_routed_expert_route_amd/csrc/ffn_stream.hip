@@ -34,7 +34,8 @@ namespace {
 // a bounded buffer resource; the last prefetch re-reads the last chunk), which
 // keeps the compiler's wait counts exact.
 // Otherwise (small K): 128-element chunks, one-chunk prefetch, scales from memory.
-// Three wavefronts per SIMD (12 per CU) with 16-row tiles, two with 32-row tiles.
+// Four wavefronts per SIMD (16 per CU) with 16-row tiles (two fragments per
+// wavefront, 113 VGPRs, workgroups within 40 KB of LDS), two with 32-row tiles.
 template <bool kW1, int MSUB, bool kDeep, int kFrag>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MSUB == 1 ? 3 : 2)))
 void gemm_stream_kernel(
@@ -88,7 +89,7 @@ void gemm_stream_kernel(
   const int nvalid = rt.p_end - rt.p_begin;
   const bool small_a = kDeep && MSUB == 1 && a_lds_rows > 0 && nvalid <= a_lds_rows;
   const bool ring = kDeep && a_ring != 0 && !small_a;   // uniform (one tile)
-  unsigned char* a_lds = reinterpret_cast<unsigned char*>(scale_lds + 4 * n_chunks * 64);
+  unsigned char* a_lds = reinterpret_cast<unsigned char*>(scale_lds + 4 * n_chunks * 16 * kFrag);
   const int a_row_bytes = K * 2;
   if (small_a) {   // uniform over the workgroup (one tile)
     // the tile's rows, then the zero block at row a_lds_rows
@@ -135,20 +136,20 @@ void gemm_stream_kernel(
 #pragma unroll
   for (int f = 0; f < kFrag; ++f) bq[f] = wq + (e_rows + nrow[f]) * row_q + (kDeep ? 0 : 16 * g);
 
-  uint32_t* my_scales = scale_lds + (threadIdx.x >> 6) * (n_chunks * 64);
+  uint32_t* my_scales = scale_lds + (threadIdx.x >> 6) * (n_chunks * 16 * kFrag);
   if (kDeep && (lane >> 4) < kFrag) {
     // lane L stages the scales of row (f = L/16, column L%16); with two fragments
     // per wavefront lanes 32..63 have no row.  The 8 scale bytes of a 256-element
     // chunk c2 (2 per lane group) go to the two dwords
-    // my_scales[((c2*16 + L%16)*4 + f)*2 + {0,1}]
+    // my_scales[((c2*16 + L%16)*kFrag + f)*2 + {0,1}]
     const int f = lane >> 4;
     const uint8_t* srow = wsc + (e_rows + wrow(f, r16)) * row_s;
     auto put = [&](int c, const uint4& d) {   // c counts 128-element chunks
       const int c2 = c / 2;
-      my_scales[(((c2 + 0) * 16 + r16) * 4 + f) * 2 + 0] = d.x;
-      my_scales[(((c2 + 0) * 16 + r16) * 4 + f) * 2 + 1] = d.y;
-      my_scales[(((c2 + 1) * 16 + r16) * 4 + f) * 2 + 0] = d.z;
-      my_scales[(((c2 + 1) * 16 + r16) * 4 + f) * 2 + 1] = d.w;
+      my_scales[(((c2 + 0) * 16 + r16) * kFrag + f) * 2 + 0] = d.x;
+      my_scales[(((c2 + 0) * 16 + r16) * kFrag + f) * 2 + 1] = d.y;
+      my_scales[(((c2 + 1) * 16 + r16) * kFrag + f) * 2 + 0] = d.z;
+      my_scales[(((c2 + 1) * 16 + r16) * kFrag + f) * 2 + 1] = d.w;
     };
     // four 16-byte loads in flight before their stores (a load-then-store loop
     // waits one memory latency per iteration, with every wavefront of the grid
@@ -185,12 +186,6 @@ void gemm_stream_kernel(
   auto load_s = [&](uint32_t (&sc)[kFrag], int kc) {   // from memory (shallow pipeline)
 #pragma unroll
     for (int f = 0; f < kFrag; ++f) sc[f] = bs[f][kc * 4];
-  };
-  auto lds_s = [&](uint32_t (&sc)[kFrag], int kc) {    // from the staged copy
-    const uint4 d = *reinterpret_cast<const uint4*>(my_scales + (kc * 16 + r16) * 4);
-    const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
-#pragma unroll
-    for (int f = 0; f < kFrag; ++f) sc[f] = (dw[f] >> (8 * g)) & 0xFFu;
   };
   auto load_a = [&](bf16x8 (&a)[MSUB][4], int kc) {
 #pragma unroll
@@ -248,12 +243,11 @@ void gemm_stream_kernel(
         a[0][t] = *reinterpret_cast<const bf16x8*>(a_mine + c2 * a_step + 16 * t);
     };
     auto compute2 = [&](const uint4 (&q)[kFrag][2], const bf16x8 (&a)[MSUB][8], int c2) {
-      // the staged layout keeps four fragments per row slot; with two fragments
-      // per wavefront only the first half of each slot is read
-      const uint4 d0 = *reinterpret_cast<const uint4*>(my_scales + ((c2 * 16 + r16) * 4) * 2);
+      // a row slot holds kFrag fragments x 2 dwords: one 16-byte read per two
+      const uint4 d0 = *reinterpret_cast<const uint4*>(my_scales + ((c2 * 16 + r16) * kFrag) * 2);
       uint4 d1 = d0;
       if constexpr (kFrag == 4)
-        d1 = *reinterpret_cast<const uint4*>(my_scales + ((c2 * 16 + r16) * 4) * 2 + 4);
+        d1 = *reinterpret_cast<const uint4*>(my_scales + ((c2 * 16 + r16) * kFrag) * 2 + 4);
       const uint32_t sd[4][2] = {{d0.x, d0.y}, {d0.z, d0.w}, {d1.x, d1.y}, {d1.z, d1.w}};
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
@@ -438,19 +432,22 @@ hipError_t launch_stream_t(unsigned grid, hipStream_t stream, const uint16_t* ac
                          int n_rows, int half, int wpt, float limit, int clamp, uint16_t* out,
                          int ld_out) {
   const int n_chunks = K / kFfnKChunk;
-  const size_t lds = static_cast<size_t>(4) * n_chunks * 64 * sizeof(uint32_t);
+  const size_t lds = static_cast<size_t>(4) * n_chunks * 16 * kFrag * sizeof(uint32_t);
+  // 16-row tiles with two fragments per wavefront fit four workgroups per CU
+  const size_t max_lds = MSUB == 1 ? (kFrag == 2 ? kStreamMaxLds4 : kStreamMaxLds) : kStreamMaxLds2;
   // activation rows in LDS for row tiles that fit: one tile per workgroup, and
-  // room for three workgroups per CU (W1 at H = 4096: 2 rows; W2 at I = 2048: 9)
+  // room for four workgroups per CU with 16-row tiles (W1 at H = 4096: 2 rows; W2
+  // at I = 2048: 7), two with 32-row tiles
   int a_rows = 0;
-  if (MSUB == 1 && wpt % 4 == 0 && lds + 512 < kStreamMaxLds) {
-    const size_t fit = (kStreamMaxLds - lds - 512) / (static_cast<size_t>(K) * 2);
+  if (MSUB == 1 && wpt % 4 == 0 && lds + 512 < max_lds) {
+    const size_t fit = (max_lds - lds - 512) / (static_cast<size_t>(K) * 2);
     a_rows = static_cast<int>(fit < 16 ? fit : 16);
   }
   size_t a_bytes = a_rows > 0 ? static_cast<size_t>(a_rows) * K * 2 + 512 : 0;
   // the ring: two chunks of 16*MSUB padded rows, within the workgroup's share of
-  // LDS (three workgroups per CU with 16-row tiles, two with 32-row tiles)
+  // LDS
   const size_t ring_bytes = 2 * 16 * MSUB * 528;
-  const size_t budget = MSUB == 1 ? kStreamMaxLds : kStreamMaxLds2;
+  const size_t budget = max_lds;
   const int a_ring = wpt % 4 == 0 && lds + ring_bytes <= budget ? 1 : 0;
   if (a_ring && ring_bytes > a_bytes) a_bytes = ring_bytes;
   if (n_chunks % 4 == 0 && lds <= kStreamMaxScaleLds)
