@@ -73,9 +73,9 @@ def ffn_kernel_name(T: int, E: int, k: int, H: int) -> str:
     80-row kernel stages E8M0 scales in LDS while they fit beside the activations
     in 80 KB)."""
     if T <= 16 or T * k // E <= 8:
-        return "gemm_stream_kernel<true, 1, true>"
+        return "gemm_stream_kernel<true, 1, true, 2>"
     if T * k // E <= 24:
-        return "gemm_stream_kernel<true, 2, true>"
+        return "gemm_stream_kernel<true, 2, true, 4>"
     if T * k // E < 96:
         lds_scales = 2 * 80 * 272 + 4 * (H // 128) * 64 * 4 <= 80 * 1024
         return f"gemm_tile_kernel<true, 5, 4, 4, {'true' if lds_scales else 'false'}>"
