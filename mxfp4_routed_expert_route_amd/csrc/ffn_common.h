@@ -5,9 +5,10 @@
 // clamp (txtmix.com article, §9): gate capped at +limit, up clamped to
 // [-limit, +limit], both before the SwiGLU product.
 //
-// Every GEMM wavefront owns 64 weight rows of one row tile's expert -- for W1 32
-// gate rows and the 32 matching up rows, so each SwiGLU pair meets in one lane;
-// for W2 64 output rows -- as four 16-column MFMA fragments.  Codes are
+// Every GEMM wavefront owns weight rows of one row tile's expert as 16-column MFMA
+// fragments -- four (64 rows) in the tiled kernel and the 32-row streaming tiles,
+// two (32 rows) in the 16-row streaming tiles; for W1 half of them gate rows and
+// half the matching up rows, so each SwiGLU pair meets in one lane.  Codes are
 // dequantised in registers with the gfx950 scaled FP4->BF16 convert (scale passed
 // as an fp32 whose exponent field is the E8M0 byte; 0xFF maps to a NaN scale) and
 // fed to v_mfma_f32_16x16x32_bf16 as the B operand; activations are the A

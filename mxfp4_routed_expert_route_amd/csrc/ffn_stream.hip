@@ -14,13 +14,14 @@ namespace {
 // better (5,888 wavefronts instead of 2,944 for the verify step's W1).
 //
 // Memory pipeline (kDeep, K a multiple of 512).  K advances in chunks of 256
-// elements: each lane takes 32 bytes (two scale blocks) of each of its four rows,
-// so a weight row is visited 128 bytes at a time -- measured on MI355X, 128-byte
-// visits of this many concurrent rows stream about 20% faster than 64-byte ones.
-// Two register stages of weights: the next chunk streams in while this one
-// computes.  The E8M0 scales of the wavefront's 64 rows are staged in LDS once,
-// laid out so that two 16-byte LDS reads per chunk give a lane the scales of its
-// four rows; they never enter the vector-memory queue.  Activations take one of
+// elements: each lane takes 32 bytes (two scale blocks) of each of its kFrag
+// rows, so a weight row is visited 128 bytes at a time -- measured on MI355X,
+// 128-byte visits of this many concurrent rows stream about 20% faster than
+// 64-byte ones.  Two register stages of weights: the next chunk streams in while
+// this one computes.  The E8M0 scales of the wavefront's 16*kFrag rows are staged
+// in LDS once, laid out so that one (two fragments) or two (four) 16-byte LDS
+// reads per chunk give a lane the scales of its rows; they never enter the
+// vector-memory queue.  Activations take one of
 // three routes (the host enables the first two only when the four wavefronts of
 // a workgroup share one tile):
 //   * rows in LDS: a tile whose rows fit beside the scales is staged once, for
