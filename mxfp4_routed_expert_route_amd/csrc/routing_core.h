@@ -11,11 +11,11 @@ namespace moe {
 // descending then expert index ascending; -0.0 ranks equal to +0.0.  Weights:
 // softmax over the k chosen logits.
 //
-// Each lane holds EPL logits (expert e = i*64 + lane, coalesced loads) as 64-bit
-// keys (order-preserving logit bits << 32 | ~e), so one unsigned max picks the
-// larger logit and, on a tie, the lower index.  k rounds of a wave-wide max
-// (wave_max_u64) take the winners in order; the winner's key is retired in the
-// lane that holds it.  Lane j < k returns slot j's id and weight.
+// Each lane holds EPL logits (expert e = i*64 + lane, coalesced loads) as
+// order-preserving 32-bit keys.  k rounds of a wave-wide maximum take the
+// winners in order, a tie going to the lower index (the first set lane of the
+// first non-empty ballot); the winner's key is retired in the lane that holds
+// it.  Lane j < k returns slot j's id and weight.
 
 __device__ __forceinline__ uint32_t order_bits(float f) {
   uint32_t u = __float_as_uint(f);
@@ -49,38 +49,40 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return __builtin_amdgcn_readlane(v, 63);
 }
 
-// 64-bit maximum: the largest high word, then the largest low word among the lanes
-// that hold it.
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  const uint32_t hi = wave_max_u32(static_cast<uint32_t>(v >> 32));
-  const uint32_t lo = wave_max_u32(static_cast<uint32_t>(v >> 32) == hi ? static_cast<uint32_t>(v) : 0u);
-  return (static_cast<uint64_t>(hi) << 32) | lo;
-}
-
 template <int EPL>
 __device__ __forceinline__ void route_token(const float* __restrict__ row, int E, int k, int lane,
                                             int& my_id, float& my_weight) {
-  uint64_t key[EPL];
+  // key[i]: order-preserving bits of expert i*64 + lane's logit, 0 (below every
+  // real key) past E or once taken.  Each round takes the wave-wide maximum key,
+  // then the lowest expert index holding it: expert e = i*64 + lane, so that is
+  // the first set lane of the first non-empty ballot over i -- the same order as
+  // a maximum over (key << 32 | ~e), with one 32-bit reduction instead of two.
+  uint32_t key[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
     const int e = i * 64 + lane;
-    key[i] = (e < E) ? ((static_cast<uint64_t>(order_bits(row[e])) << 32) | static_cast<uint32_t>(~e))
-                     : 0ull;   // below every real key
+    key[i] = e < E ? order_bits(row[e]) : 0u;
   }
   my_id = 0;
   float my_logit = 0.f, top = 0.f;
   for (int j = 0; j < k; ++j) {
-    uint64_t mine = key[0];
+    uint32_t mine = key[0];
 #pragma unroll
     for (int i = 1; i < EPL; ++i) mine = key[i] > mine ? key[i] : mine;
-    const uint64_t best = wave_max_u64(mine);   // wave-uniform
+    const uint32_t best = wave_max_u32(mine);   // wave-uniform
+    int e_best = 0;
+#pragma unroll
+    for (int i = EPL - 1; i >= 0; --i) {   // the lowest i with a holder wins
+      const uint64_t m = __builtin_amdgcn_ballot_w64(key[i] == best);
+      if (m != 0ull) e_best = i * 64 + static_cast<int>(__builtin_ctzll(m));
+    }
 #pragma unroll
     for (int i = 0; i < EPL; ++i)
-      if (key[i] == best) key[i] = 0ull;
-    const float l = order_bits_to_f32(static_cast<uint32_t>(best >> 32));
+      if (i * 64 + lane == e_best) key[i] = 0u;
+    const float l = order_bits_to_f32(best);
     if (j == 0) top = l;
     if (lane == j) {
-      my_id = static_cast<int>(~static_cast<uint32_t>(best));
+      my_id = e_best;
       my_logit = l;
     }
   }
