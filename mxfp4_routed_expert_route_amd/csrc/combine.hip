@@ -2,6 +2,7 @@
 //   y[t][n] = sum_j w[t][j] * y_sorted[scatter[t*k+j]][n],  fp32 in j order, one bf16 rounding.
 // A thread owns 8 consecutive columns (one 16-byte load per expert row); a
 // workgroup of 256 threads covers 2048 columns of one token.
+#include "config.h"
 #include "device.h"
 #include "launch.h"
 
@@ -21,16 +22,32 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-  for (int j = 0; j < k; ++j) {
-    const int64_t p = scatter[t * k + j];
-    const float wj = w[t * k + j];
-    if (p < 0 || p >= n_slots) continue;
-    const uint4 v = *reinterpret_cast<const uint4*>(ys + p * H + col);
-    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+  // all k rows' positions and weights, then all k row loads, then the sum in j
+  // order: one dependent pair of memory latencies instead of k (k <= kMaxK)
+  int64_t p[kMaxK];
+  float wj[kMaxK];
+  bool ok[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    ok[j] = false;
+    if (j < k) {
+      p[j] = scatter[t * k + j];
+      wj[j] = w[t * k + j];
+      ok[j] = p[j] >= 0 && p[j] < n_slots;
+    }
+  }
+  uint4 v[kMaxK];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j)
+    if (ok[j]) v[j] = *reinterpret_cast<const uint4*>(ys + p[j] * H + col);
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    if (!ok[j]) continue;
+    const uint32_t u[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      acc[2 * i] = fmaf(wj, bf16_bits_to_f32(u[i] & 0xFFFFu), acc[2 * i]);
-      acc[2 * i + 1] = fmaf(wj, bf16_bits_to_f32(u[i] >> 16), acc[2 * i + 1]);
+      acc[2 * i] = fmaf(wj[j], bf16_bits_to_f32(u[i] & 0xFFFFu), acc[2 * i]);
+      acc[2 * i + 1] = fmaf(wj[j], bf16_bits_to_f32(u[i] >> 16), acc[2 * i + 1]);
     }
   }
   uint4 o;
