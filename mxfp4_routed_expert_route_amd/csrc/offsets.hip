@@ -34,9 +34,15 @@ __device__ __forceinline__ void write_permutations(const int32_t* __restrict__ i
   if (t >= T) return;
   const uint64_t below = (1ull << lane) - 1ull;
   const int64_t n_slots = T * k;
-  for (int j = 0; j < k; ++j) {
+  int ej[kMaxK];   // the token's k expert ids, loaded together (k <= kMaxK)
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j)
+    if (j < k) ej[j] = ids[t * k + j];
+#pragma unroll
+  for (int j = 0; j < kMaxK; ++j) {
+    if (j >= k) break;
     const int64_t s = t * k + j;
-    const int e = ids[s];
+    const int e = ej[j];
     if (static_cast<unsigned>(e) >= static_cast<unsigned>(E)) continue;
     const int64_t p = static_cast<int64_t>(base[e]) + __popcll(masks[e] & below);
     if (p < 0 || p >= n_slots) continue;
