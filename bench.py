@@ -71,7 +71,7 @@ class HipEvents:
 def ffn_kernel_name(T: int, E: int, k: int, H: int) -> str:
     """The W1 kernel the library picks for these sizes (its row-tile rule; the
     80-row kernel stages E8M0 scales in LDS while they fit beside the activations
-    in 80 KB)."""
+    in 80 KB, the 128-row kernel while they fit in the CU's 160 KB)."""
     if T <= 16 or T * k // E <= 8:
         return "gemm_stream_kernel<true, 1, true, 2>"
     if T * k // E <= 24:
@@ -79,7 +79,8 @@ def ffn_kernel_name(T: int, E: int, k: int, H: int) -> str:
     if T * k // E < 96:
         lds_scales = 2 * 80 * 272 + 4 * (H // 128) * 64 * 4 <= 80 * 1024
         return f"gemm_tile_kernel<true, 5, 4, 4, {'true' if lds_scales else 'false'}>"
-    return "gemm_tile_kernel<true, 8, 4, 8, false>"
+    lds_scales = 2 * 128 * 272 + 8 * (H // 128) * 64 * 4 <= 160 * 1024
+    return f"gemm_tile_kernel<true, 8, 4, 8, {'true' if lds_scales else 'false'}>"
 
 
 def measured_traffic(profile_name: str, kernel_source: str):
