@@ -198,7 +198,8 @@ moe_status moe_route_and_group(const float* logits, int64_t T, int32_t E, int32_
  * arguments (see those calls for each output's definition, layout, alignment
  * and citation).  The FFN's row-tile plan is written by the routing side where
  * it holds the counts in one workgroup -- the one-launch front-end for T <= 64,
- * the expert-offsets scan for T > 512 -- which saves the FFN its plan launch.  ws is
+ * the expert-offsets kernel for 64 < T <= 512, the expert-offsets scan above --
+ * which saves the FFN its plan launch.  ws is
  * the workspace of those calls (moe_workspace_bytes).  T = 0 writes zeros to
  * counts and offsets and nothing else.
  */

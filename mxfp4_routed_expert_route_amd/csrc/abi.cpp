@@ -103,8 +103,8 @@ moe_status moe_forward_mxfp4(const float* logits, const uint16_t* x, int64_t T, 
   moe::WsLayout L;
   s = moe::workspace_layout(T, E, k, H, I, &L);
   if (s != MOE_OK) return s;
-  // the routing side writes the FFN's row-tile plan where it can: the one-launch
-  // front-end (T <= 64) and the expert-offsets scan (T > 512)
+  // the routing side writes the FFN's row-tile plan: the one-launch front-end
+  // (T <= 64), else the expert-offsets kernel (T <= 512) or its scan step
   const int tile_rows = moe::ffn_tile_rows(T, E, k);
   char* wsb = static_cast<char*>(ws);
   const moe::PlanOut plan{tile_rows, moe::ffn_tile_bound(T * k, E, tile_rows),

@@ -15,8 +15,8 @@ hipError_t launch_bitmatrix(const int32_t* ids, int64_t T, int E, int k, uint32_
 
 struct PlanOut;
 
-// With plan != nullptr and T above one offsets block (512 tokens), the scan step
-// also writes the FFN's row-tile plan and sets *plan_written.
+// With plan != nullptr (and T > 0) the one-workgroup kernel (T <= 512) or the
+// scan step (larger T) also writes the FFN's row-tile plan and sets *plan_written.
 hipError_t launch_offsets(const uint32_t* bm, const int32_t* ids, int64_t T, int E, int k,
                           int32_t* counts, int32_t* offsets, int32_t* gather, int32_t* scatter,
                           void* ws, hipStream_t stream, const PlanOut* plan = nullptr,
@@ -40,8 +40,8 @@ struct PlanOut {
 };
 
 // With plan != nullptr the one-launch path (T <= 64) also writes the FFN plan and
-// sets *plan_written; larger T runs the separate kernels, whose scan step writes
-// the plan above 512 tokens.
+// sets *plan_written; larger T runs the separate kernels, whose offsets step
+// writes the plan.
 hipError_t launch_route_and_group(const float* logits, int64_t T, int E, int k, int32_t* ids,
                                   float* weights, uint32_t* bm, int32_t* counts, int32_t* offsets,
                                   int32_t* gather, int32_t* scatter, void* ws, hipStream_t stream,

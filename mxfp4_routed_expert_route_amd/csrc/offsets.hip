@@ -51,11 +51,45 @@ __device__ __forceinline__ void write_permutations(const int32_t* __restrict__ i
   }
 }
 
-// T <= 512: everything in one workgroup.
+// The FFN's row-tile plan from a workgroup whose thread t holds experts 2t and
+// 2t+1 (counts c, first rows off): the same tiles, in the same expert order, as
+// write_tile_plan.  Every thread calls it; wave_tot may be reused on entry only
+// after a barrier.
+__device__ __forceinline__ void write_tile_plan_pairs(int e0, int E, const int (&c)[2],
+                                                      const int (&off)[2], int tile_rows,
+                                                      int64_t tile_bound,
+                                                      int32_t* __restrict__ n_tiles,
+                                                      RowTile* __restrict__ tiles,
+                                                      int* wave_tot) {
+  int nt[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) nt[q] = e0 + q < E ? (c[q] + tile_rows - 1) / tile_rows : 0;
+  int total;
+  int slot0 = block_exclusive_scan(nt[0] + nt[1], wave_tot, &total);
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    for (int i = 0; i < nt[q]; ++i) {
+      const int64_t slot = static_cast<int64_t>(slot0) + i;
+      if (slot >= tile_bound) break;
+      RowTile rt;
+      rt.expert = e0 + q;
+      rt.p_begin = off[q] + i * tile_rows;
+      rt.p_end = (i + 1) * tile_rows < c[q] ? off[q] + (i + 1) * tile_rows : off[q] + c[q];
+      rt.pad = 0;
+      tiles[slot] = rt;
+    }
+    slot0 += nt[q];
+  }
+  if (threadIdx.x == 0) *n_tiles = static_cast<int32_t>(total < tile_bound ? total : tile_bound);
+}
+
+// T <= 512: everything in one workgroup; with tiles != nullptr (the one-call
+// layer) it also writes the FFN's row-tile plan.
 __global__ __launch_bounds__(kOffsBlockTokens) void offsets_small_kernel(
     const uint32_t* __restrict__ bm, const int32_t* __restrict__ ids, int64_t T, int E, int k,
     int words, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ gather, int32_t* __restrict__ scatter) {
+    int32_t* __restrict__ gather, int32_t* __restrict__ scatter, int tile_rows,
+    int64_t tile_bound, int32_t* __restrict__ n_tiles, RowTile* __restrict__ tiles) {
   extern __shared__ uint64_t lds[];
   uint64_t* masks = lds;                                                   // [kWaves][E]
   int32_t* base = reinterpret_cast<int32_t*>(masks + kWaves * E);          // [kWaves][E]
@@ -81,18 +115,20 @@ __global__ __launch_bounds__(kOffsBlockTokens) void offsets_small_kernel(
   }
   int total;
   const int first = block_exclusive_scan(c[0] + c[1], wave_tot, &total);
+  const int off[2] = {first, first + c[0]};
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int e = e0 + q;
     if (e < E) {
-      const int off = first + (q ? c[0] : 0);
       counts[e] = c[q];
-      offsets[e] = off;
-      for (int w = 0; w < kWaves; ++w) base[w * E + e] += off;
+      offsets[e] = off[q];
+      for (int w = 0; w < kWaves; ++w) base[w * E + e] += off[q];
     }
   }
   if (threadIdx.x == 0) offsets[E] = total;
-  __syncthreads();
+  __syncthreads();   // base complete; every thread has read wave_tot
+  if (tiles != nullptr)   // uniform
+    write_tile_plan_pairs(e0, E, c, off, tile_rows, tile_bound, n_tiles, tiles, wave_tot);
   write_permutations(ids, static_cast<int64_t>(threadIdx.x), T, k, lane, masks + wave * E,
                      base + wave * E, E, gather, scatter);
 }
@@ -194,10 +230,14 @@ hipError_t launch_offsets(const uint32_t* bm, const int32_t* ids, int64_t T, int
   const int words = (E + 31) / 32;
   const size_t lds_masks = static_cast<size_t>(kWaves) * E * sizeof(uint64_t);
   const size_t lds_base = static_cast<size_t>(kWaves) * E * sizeof(int32_t);
+  RowTile* tiles = plan ? static_cast<RowTile*>(plan->tiles) : nullptr;
   if (T <= kOffsBlockTokens) {
     offsets_small_kernel<<<1, kOffsBlockTokens, lds_masks + lds_base, stream>>>(
-        bm, ids, T, E, k, words, counts, offsets, gather, scatter);
-    return hipGetLastError();
+        bm, ids, T, E, k, words, counts, offsets, gather, scatter, plan ? plan->tile_rows : 1,
+        plan ? plan->tile_bound : 0, plan ? plan->n_tiles : nullptr, tiles);
+    const hipError_t err = hipGetLastError();
+    if (err == hipSuccess && plan_written) *plan_written = tiles != nullptr;
+    return err;
   }
   const int64_t n_blocks = (T + kOffsBlockTokens - 1) / kOffsBlockTokens;
   int32_t* blk = static_cast<int32_t*>(ws);
@@ -205,7 +245,6 @@ hipError_t launch_offsets(const uint32_t* bm, const int32_t* ids, int64_t T, int
   block_counts_kernel<<<grid, block, lds_masks, stream>>>(bm, T, E, words, blk);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  RowTile* tiles = plan ? static_cast<RowTile*>(plan->tiles) : nullptr;
   scan_kernel<<<1, 1024, 0, stream>>>(blk, n_blocks, E, counts, offsets,
                                       plan ? plan->tile_rows : 1, plan ? plan->tile_bound : 0,
                                       plan ? plan->n_tiles : nullptr, tiles);

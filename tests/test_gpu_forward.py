@@ -2,9 +2,10 @@
 
 Every output must match the separate-call chain (moe_route_and_group,
 moe_grouped_ffn_mxfp4, moe_combine) bit for bit: the same kernels run, except
-that for T <= 64 the one-launch front-end also writes the FFN's row-tile plan in
-place of the FFN's plan kernel, and above 512 tokens the expert-offsets scan
-does.  The cases cover each tile kind the plan can
+that the routing side also writes the FFN's row-tile plan in place of the FFN's
+plan kernel: the one-launch front-end for T <= 64, the one-workgroup
+expert-offsets kernel up to 512 tokens (two experts per thread), the
+expert-offsets scan above.  The cases cover each tile kind the plan can
 hold (16- and 32-row streaming tiles, 80-row LDS tiles; 128-row tiles, which
 need more than 64 tokens) on both sides of the T = 64 front-end limit, and T = 0.
 """
@@ -50,7 +51,8 @@ def _compare(inp, limit=10.0):
         assert torch.equal(_bits(getattr(a, name)), _bits(getattr(b, name))), name
 
 
-@pytest.mark.parametrize("index", [0, 1, 3, 4])   # 3, 4: the scan writes the plan
+@pytest.mark.parametrize("index", [0, 1, 2, 3, 4])   # 2: the offsets kernel writes the
+                                                     # plan; 3, 4: the scan
 def test_forward_matches_separate_calls_workloads(index):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
@@ -62,8 +64,13 @@ def test_forward_matches_separate_calls_workloads(index):
     (40, 8, 1, 128, 128, 42),        # 5 rows per expert: 16-row tiles, several per expert
     (64, 24, 7, 256, 128, 43),       # 18.7 rows per expert: 32-row tiles, front-end plan
     (64, 16, 8, 256, 256, 44),       # 32 rows per expert: 80-row LDS tiles, front-end plan
-    (65, 16, 8, 256, 256, 45),       # past the one-launch limit: plan kernel
-    (300, 8, 3, 256, 256, 48),       # 112 rows per expert: 128-row tiles, plan kernel
+    (65, 16, 8, 256, 256, 45),       # past the one-launch limit: the offsets kernel's plan
+    (300, 8, 3, 256, 256, 48),       # 112 rows per expert: 128-row tiles, offsets kernel
+    (100, 256, 6, 256, 128, 51),     # 16-row tiles for 2.3 rows per expert, offsets kernel
+    (200, 64, 6, 256, 128, 52),      # 18.75 rows per expert: 32-row tiles, offsets kernel
+    (300, 32, 6, 256, 256, 53),      # 56 rows per expert: 80-row tiles, offsets kernel
+    (500, 1024, 8, 128, 128, 54),    # maximum E: every thread holds two experts
+    (130, 40, 5, 128, 128, 55),      # E not a multiple of 64 (odd expert count per wave)
     (600, 16, 2, 256, 256, 49),      # past one offsets block (512 tokens): the scan writes
                                      # the plan (80-row tiles)
     (1100, 8, 3, 256, 256, 50),      # three offsets blocks, 128-row tiles from the scan's plan
