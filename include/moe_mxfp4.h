@@ -184,7 +184,9 @@ moe_status moe_combine(const uint16_t* y_sorted, const float* topk_weights,
  *
  * For T <= 64 the three steps run as one kernel launch (one workgroup; the
  * bit matrix is built in LDS under the same logical-block mask); for larger T
- * the three kernels of the separate calls run back to back.  ws is the
+ * the routing kernel also writes each token's bit-matrix row (one wavefront
+ * per token: lane w writes word w), then the expert-offsets kernels of the
+ * separate call run.  ws is the
  * workspace of moe_expert_offsets.  T = 0 writes zeros to counts and offsets.
  */
 moe_status moe_route_and_group(const float* logits, int64_t T, int32_t E, int32_t k,

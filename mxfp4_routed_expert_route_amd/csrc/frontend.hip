@@ -12,7 +12,8 @@
 //      and writes each slot's row p = offsets[e] + rank of the token within e.
 // With a plan buffer, wavefront 0 also writes the grouped FFN's row-tile plan
 // (moe_forward_mxfp4), which saves the FFN its plan launch.  Larger batches run
-// the three separate kernels.
+// the routing kernel, which then also writes the bit matrix, and the offsets
+// kernels of the separate call.
 #include "config.h"
 #include "launch.h"
 #include "routing_core.h"
@@ -149,9 +150,7 @@ hipError_t launch_route_and_group(const float* logits, int64_t T, int E, int k, 
                                   const PlanOut* plan, bool* plan_written) {
   if (plan_written) *plan_written = false;
   if (T > kFrontMaxTokens) {
-    hipError_t err = launch_route(logits, T, E, k, ids, weights, stream);
-    if (err != hipSuccess) return err;
-    err = launch_bitmatrix(ids, T, E, k, bm, stream);
+    hipError_t err = launch_route(logits, T, E, k, ids, weights, stream, bm);
     if (err != hipSuccess) return err;
     return launch_offsets(bm, ids, T, E, k, counts, offsets, gather, scatter, ws, stream, plan,
                           plan_written);

@@ -7,8 +7,10 @@
 
 namespace moe {
 
+// With bm != nullptr, also the bit matrix ([T][ceil(E/32)] words, every word of
+// each row written).
 hipError_t launch_route(const float* logits, int64_t T, int E, int k, int32_t* ids,
-                        float* weights, hipStream_t stream);
+                        float* weights, hipStream_t stream, uint32_t* bm = nullptr);
 
 hipError_t launch_bitmatrix(const int32_t* ids, int64_t T, int E, int k, uint32_t* bm,
                             hipStream_t stream);
@@ -40,8 +42,8 @@ struct PlanOut {
 };
 
 // With plan != nullptr the one-launch path (T <= 64) also writes the FFN plan and
-// sets *plan_written; larger T runs the separate kernels, whose offsets step
-// writes the plan.
+// sets *plan_written; larger T runs the routing kernel (writing the bit matrix
+// too) and the offsets kernels, whose last step writes the plan.
 hipError_t launch_route_and_group(const float* logits, int64_t T, int E, int k, int32_t* ids,
                                   float* weights, uint32_t* bm, int32_t* counts, int32_t* offsets,
                                   int32_t* gather, int32_t* scatter, void* ws, hipStream_t stream,

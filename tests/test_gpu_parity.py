@@ -152,7 +152,11 @@ def test_ragged_shapes_whole_layer(T, E, k, H, I, seed):
 
 @pytest.mark.parametrize("T,E,k,seed", [
     (1, 256, 6, 31), (8, 256, 6, 32), (16, 256, 6, 33), (63, 256, 6, 34), (64, 256, 6, 35),
-    (65, 256, 6, 36),                # past the one-launch limit: the separate kernels
+    (65, 256, 6, 36),                # past the one-launch limit: the routing kernel writes
+                                     # the bit matrix, then the offsets kernels
+    (300, 40, 5, 56),                # E = 40: a partial last bit-matrix word
+    (130, 1024, 8, 57),              # 32 bit-matrix words per row
+    (513, 96, 3, 58),                # past one offsets block
     (64, 1024, 8, 37), (20, 40, 3, 38), (10, 64, 1, 39),
 ])
 def test_fused_front_end(T, E, k, seed):
