@@ -73,8 +73,13 @@ hipError_t launch_ffn(const uint16_t* x, int64_t T, int H, int I, int E, int k,
     // W1: 8 * frags gate rows (and as many up rows) per wavefront; W2: 16 * frags rows
     const int frags = stream_frags(tile_rows / 16);
     const int wpt1 = I / (8 * frags), wpt2 = H / (16 * frags);
-    const unsigned g1 = static_cast<unsigned>((tile_bound * wpt1 + 3) / 4);
-    const unsigned g2 = static_cast<unsigned>((tile_bound * wpt2 + 3) / 4);
+    unsigned g1 = static_cast<unsigned>((tile_bound * wpt1 + 3) / 4);
+    unsigned g2 = static_cast<unsigned>((tile_bound * wpt2 + 3) / 4);
+    if (tile_rows == 32) {   // whole tiles per XCD: grids in steps of 8 tiles
+      const unsigned s1 = 8u * (wpt1 / 4), s2 = 8u * (wpt2 / 4);
+      if (wpt1 % 4 == 0) g1 = (g1 + s1 - 1) / s1 * s1;
+      if (wpt2 % 4 == 0) g2 = (g2 + s2 - 1) / s2 * s2;
+    }
     const RowTile* t = tiles;
     const int msub = tile_rows / 16;
     err = launch_stream(true, msub, g1, stream, x, x_bytes, gather, k, slots_i, w1, w1s, t,

@@ -50,7 +50,18 @@ void gemm_stream_kernel(
   // 512-byte zero block, or the ring (two slots of 16*MSUB rows of 528 bytes)
   extern __shared__ uint32_t scale_lds[];
   const int lane = threadIdx.x & 63;
-  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);
+  // 32-row tiles: each XCD takes whole tiles (tile x, x+8, ... for XCD x, the
+  // hardware dealing consecutive workgroups to the 8 XCDs in turn), so the tile's
+  // activation chunks, staged by each of its workgroups, are fetched into one L2
+  int blk = blockIdx.x;
+  if constexpr (MSUB == 2) {
+    const int bpt = waves_per_tile >> 2;
+    if ((waves_per_tile & 3) == 0 && gridDim.x % (8 * bpt) == 0) {   // uniform
+      const int x = blockIdx.x % 8, l = blockIdx.x / 8;
+      blk = ((l / bpt) * 8 + x) * bpt + l % bpt;
+    }
+  }
+  const int gw = blk * 4 + (threadIdx.x >> 6);
   const int tile_id = gw / waves_per_tile;
   const int cg = gw - tile_id * waves_per_tile;
   if (tile_id >= *n_tiles) return;   // per wavefront: no workgroup barrier in this kernel
