@@ -92,15 +92,19 @@ hipError_t launch_ffn(const uint16_t* x, int64_t T, int H, int I, int E, int k,
     err = launch_stream(false, msub, g2, stream, h, h_bytes, nullptr, k, slots_i, w2, w2s, t,
                         n_tiles, I, H, 0, wpt2, limit, 0, y_sorted, H);
   } else {
+    // 80-row tiles with at most 64 rows per expert on average (most experts one
+    // tile, so no weight slice to share between an expert's tiles): each XCD takes
+    // whole tiles, and a tile's activation chunks are fetched into one L2
+    const bool whole = tile_rows == 80 && T * k / E <= 64;
     err = launch_tile(true, tile_rows, tile_bound, stream, x, x_bytes, gather, k, slots_i, w1,
-                      w1s, tiles, n_tiles, H, 2 * I, I, limit, clamp_i, h, I);
+                      w1s, tiles, n_tiles, H, 2 * I, I, limit, clamp_i, h, I, whole);
     if (err != hipSuccess) return err;
     if (events) {
       err = hipEventRecord(events[1], stream);
       if (err != hipSuccess) return err;
     }
     err = launch_tile(false, tile_rows, tile_bound, stream, h, h_bytes, nullptr, k, slots_i, w2,
-                      w2s, tiles, n_tiles, I, H, 0, limit, 0, y_sorted, H);
+                      w2s, tiles, n_tiles, I, H, 0, limit, 0, y_sorted, H, whole);
   }
   if (err != hipSuccess || !events) return err;
   return hipEventRecord(events[2], stream);

@@ -65,6 +65,6 @@ hipError_t launch_tile(bool w1, int tile_rows, int64_t tile_bound, hipStream_t s
                        const uint16_t* act, uint32_t act_bytes, const int32_t* gather, int k_top,
                        int n_slots, const uint8_t* wq, const uint8_t* wsc, const RowTile* tiles,
                        const int32_t* n_tiles, int K, int n_rows, int half, float limit, int clamp,
-                       uint16_t* out, int ld_out);
+                       uint16_t* out, int ld_out, bool whole_tiles);
 
 }  // namespace moe

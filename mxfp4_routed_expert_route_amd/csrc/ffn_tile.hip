@@ -53,7 +53,10 @@ namespace {
 // tile (128 x 512 tiles) the same split gives each XCD 2 column blocks of half
 // the tiles: a 1 MB activation tile goes to 4 L2s instead of 8, and the XCD's
 // slice of a hot expert (2 x 1.1 MB of W1) stays in its L2 across that expert's
-// many row tiles.
+// many row tiles.  With 80-row tiles and at most 64 rows per expert on average
+// (prefill batches: most experts are one tile, so there is no slice to share)
+// each XCD takes whole tiles instead: all 16 column blocks of a tile read its
+// activation chunks from one L2 (prefill-2048 W1 ~566 -> ~549 us).
 constexpr int kARowBytes = kFfnKChunk * 2 + 16;   // 256 B of bf16 + 16 B pad
 constexpr int kXcds = 8;
 
@@ -73,7 +76,7 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
     int k_top, int n_slots, const uint8_t* __restrict__ wq, const uint8_t* __restrict__ wsc,
     const RowTile* __restrict__ tiles, const int32_t* __restrict__ n_tiles, int K, int n_rows,
     int half, int waves_per_tile, int blocks_per_tile, float limit, int clamp,
-    uint16_t* __restrict__ out, int ld_out) {
+    uint16_t* __restrict__ out, int ld_out, int whole_tiles) {
   // the fragment count is a parameter of the indexing below, but only four
   // fragments per wavefront (64 weight rows) are instantiated and tested
   static_assert(kFrag == 4, "four weight fragments per wavefront");
@@ -91,7 +94,10 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
   // L2 while each tile's activations go to 4 XCDs, not 8); otherwise launch order
   // (same with 8 column blocks: XCD x takes column blocks 2(x%4), 2(x%4)+1)
   int work = blockIdx.x;
-  if (blocks_per_tile == 16 || blocks_per_tile == 8) {
+  if (whole_tiles) {   // XCD x takes row tiles x, x+8, ... (grid: whole 8-tile groups)
+    const int x = blockIdx.x % kXcds, l = blockIdx.x / kXcds;
+    work = ((l / blocks_per_tile) * kXcds + x) * blocks_per_tile + l % blocks_per_tile;
+  } else if (blocks_per_tile == 16 || blocks_per_tile == 8) {
     const int x = blockIdx.x % kXcds, l = blockIdx.x / kXcds;
     const int per = blocks_per_tile / 4;   // column blocks per XCD and tile
     work = ((l / per) * 2 + x / 4) * blocks_per_tile + (x % 4) * per + (l % per);
@@ -366,20 +372,22 @@ hipError_t launch_tile_t(int64_t tile_bound, hipStream_t stream, const uint16_t*
                          uint32_t act_bytes, const int32_t* gather, int k_top, int n_slots,
                          const uint8_t* wq, const uint8_t* wsc, const RowTile* tiles,
                          const int32_t* n_tiles, int K, int n_rows, int half, float limit,
-                         int clamp, uint16_t* out, int ld_out) {
+                         int clamp, uint16_t* out, int ld_out, bool whole_tiles) {
   // wavefronts per row tile: W1 pairs `half` gate rows with as many up rows, 16 *
   // kFrag/2 of each per wavefront; W2 covers n_rows output rows, 16 * kFrag each
   const int wpt = kW1 ? half / (8 * kFrag) : n_rows / (16 * kFrag);
   const int bpt = (wpt + kWaves - 1) / kWaves;
   size_t lds = 2 * static_cast<size_t>(a_buf_bytes<kMSub>());
   if (kLdsScales) lds += tile_scale_lds_bytes(K, kWaves);
-  // the column-block/XCD split covers row tiles in pairs: round up to whole pairs
-  const int64_t blocks =
-      (bpt == 16 || bpt == 8) ? (tile_bound + 1) / 2 * 2 * bpt : tile_bound * bpt;
+  // whole tiles per XCD cover row tiles in groups of 8, the column-block/XCD split
+  // in pairs: round up to whole groups
+  const int64_t blocks = whole_tiles               ? (tile_bound + 7) / 8 * 8 * bpt
+                         : (bpt == 16 || bpt == 8) ? (tile_bound + 1) / 2 * 2 * bpt
+                                                   : tile_bound * bpt;
   gemm_tile_kernel<kW1, kMSub, kFrag, kWaves, kLdsScales>
       <<<static_cast<unsigned>(blocks), 64 * kWaves, lds, stream>>>(
       act, act_bytes, gather, k_top, n_slots, wq, wsc, tiles, n_tiles, K, n_rows, half, wpt, bpt,
-      limit, clamp, out, ld_out);
+      limit, clamp, out, ld_out, whole_tiles ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -389,23 +397,23 @@ hipError_t launch_tile(bool w1, int tile_rows, int64_t tile_bound, hipStream_t s
                        const uint16_t* act, uint32_t act_bytes, const int32_t* gather, int k_top,
                        int n_slots, const uint8_t* wq, const uint8_t* wsc, const RowTile* tiles,
                        const int32_t* n_tiles, int K, int n_rows, int half, float limit, int clamp,
-                       uint16_t* out, int ld_out) {
+                       uint16_t* out, int ld_out, bool whole_tiles) {
   // 128-row tiles (one workgroup per CU) stage the scales in LDS while they fit
   // beside the activation buffers in the CU's 160 KB (K <= 4096)
   if (tile_rows == 128) {
     if (2 * static_cast<size_t>(a_buf_bytes<8>()) + tile_scale_lds_bytes(K, 8) <= kCuLds)
       return w1 ? launch_tile_t<true, 8, 4, 8, true>(tile_bound, stream, act, act_bytes, gather,
                                                      k_top, n_slots, wq, wsc, tiles, n_tiles, K,
-                                                     n_rows, half, limit, clamp, out, ld_out)
+                                                     n_rows, half, limit, clamp, out, ld_out, false)
                 : launch_tile_t<false, 8, 4, 8, true>(tile_bound, stream, act, act_bytes, gather,
                                                       k_top, n_slots, wq, wsc, tiles, n_tiles, K,
-                                                      n_rows, half, limit, clamp, out, ld_out);
+                                                      n_rows, half, limit, clamp, out, ld_out, false);
     return w1 ? launch_tile_t<true, 8, 4, 8, false>(tile_bound, stream, act, act_bytes, gather,
                                                     k_top, n_slots, wq, wsc, tiles, n_tiles, K,
-                                                    n_rows, half, limit, clamp, out, ld_out)
+                                                    n_rows, half, limit, clamp, out, ld_out, false)
               : launch_tile_t<false, 8, 4, 8, false>(tile_bound, stream, act, act_bytes, gather,
                                                      k_top, n_slots, wq, wsc, tiles, n_tiles, K,
-                                                     n_rows, half, limit, clamp, out, ld_out);
+                                                     n_rows, half, limit, clamp, out, ld_out, false);
   }
   // 80-row tiles keep two workgroups per CU: the E8M0 scales are staged in LDS
   // while they fit beside the activation buffers in half the CU's LDS (K <= 4096
@@ -413,16 +421,16 @@ hipError_t launch_tile(bool w1, int tile_rows, int64_t tile_bound, hipStream_t s
   if (2 * static_cast<size_t>(a_buf_bytes<5>()) + tile_scale_lds_bytes(K, 4) <= kTileLdsPerWorkgroup)
     return w1 ? launch_tile_t<true, 5, 4, 4, true>(tile_bound, stream, act, act_bytes, gather,
                                                    k_top, n_slots, wq, wsc, tiles, n_tiles, K,
-                                                   n_rows, half, limit, clamp, out, ld_out)
+                                                   n_rows, half, limit, clamp, out, ld_out, whole_tiles)
               : launch_tile_t<false, 5, 4, 4, true>(tile_bound, stream, act, act_bytes, gather,
                                                     k_top, n_slots, wq, wsc, tiles, n_tiles, K,
-                                                    n_rows, half, limit, clamp, out, ld_out);
+                                                    n_rows, half, limit, clamp, out, ld_out, whole_tiles);
   return w1 ? launch_tile_t<true, 5, 4, 4, false>(tile_bound, stream, act, act_bytes, gather,
                                                   k_top, n_slots, wq, wsc, tiles, n_tiles, K,
-                                                  n_rows, half, limit, clamp, out, ld_out)
+                                                  n_rows, half, limit, clamp, out, ld_out, whole_tiles)
             : launch_tile_t<false, 5, 4, 4, false>(tile_bound, stream, act, act_bytes, gather,
                                                    k_top, n_slots, wq, wsc, tiles, n_tiles, K,
-                                                   n_rows, half, limit, clamp, out, ld_out);
+                                                   n_rows, half, limit, clamp, out, ld_out, whole_tiles);
 }
 
 }  // namespace moe
