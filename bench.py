@@ -157,8 +157,9 @@ def main():
                          "MiB (--steps times): the reference for HBM traffic counters")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer is "
-              "built and measured per GPU, see DESIGN.md for how it would shard", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the layer is "
+              "built and measured on a single GPU; sharding it by expert across GPUs is not "
+              "implemented", file=sys.stderr)
         sys.exit(2)
 
     import torch
