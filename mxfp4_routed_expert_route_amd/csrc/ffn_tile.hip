@@ -48,8 +48,10 @@ namespace {
 // each XCD 2 of the 16 column blocks of every tile (256-column blocks of W1): a
 // small weight slice per L2, but every tile's activations fetched into all 8 L2s.
 // Measured alternatives: whole tiles per XCD (each L2 then cycles an expert's full
-// 8.9 MB W1) was 40% slower; 4 column blocks x half the tiles per XCD is ~1%
-// faster than launch order and is what is used there.  With 8 column blocks per
+// 8.9 MB W1) was 40% slower on an earlier version of this kernel and is neutral on
+// the present 128-row kernel (skewed-8191: 2,514-2,532 against 2,524-2,528 us per
+// layer); 4 column blocks x half the tiles per XCD is ~1% faster than launch order
+// and is what is used there.  With 8 column blocks per
 // tile (128 x 512 tiles) the same split gives each XCD 2 column blocks of half
 // the tiles: a 1 MB activation tile goes to 4 L2s instead of 8, and the XCD's
 // slice of a hot expert (2 x 1.1 MB of W1) stays in its L2 across that expert's
