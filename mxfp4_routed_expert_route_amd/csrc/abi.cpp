@@ -14,6 +14,60 @@ hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
 }  // namespace
 
+namespace moe {
+
+moe_status check_forward(const float* logits, const uint16_t* x, int64_t T, int32_t H, int32_t I,
+                         int32_t E, int32_t k, const uint8_t* w1, const uint8_t* w1_scale,
+                         const uint8_t* w2, const uint8_t* w2_scale, const int32_t* topk_ids,
+                         const float* topk_weights, const uint32_t* bitmatrix,
+                         const int32_t* counts, const int32_t* offsets, const int32_t* gather,
+                         const int32_t* scatter, const uint16_t* y_sorted, const uint16_t* y,
+                         const void* ws, size_t ws_bytes) {
+  moe_status s = check_route(logits, T, E, k, topk_ids, topk_weights);
+  if (s != MOE_OK) return s;
+  s = check_bitmatrix(topk_ids, T, E, k, bitmatrix);
+  if (s != MOE_OK) return s;
+  s = check_offsets(bitmatrix, topk_ids, T, E, k, counts, offsets, gather, scatter, ws, ws_bytes);
+  if (s != MOE_OK) return s;
+  s = check_ffn(x, T, H, I, E, k, w1, w1_scale, w2, w2_scale, counts, offsets, gather, y_sorted,
+                ws, ws_bytes);
+  if (s != MOE_OK) return s;
+  return check_combine(y_sorted, topk_weights, scatter, T, H, k, y);
+}
+
+moe_status forward_layer(const float* logits, const uint16_t* x, int64_t T, int32_t H, int32_t I,
+                         int32_t E, int32_t k, const uint8_t* w1, const uint8_t* w1_scale,
+                         const uint8_t* w2, const uint8_t* w2_scale, float swiglu_limit,
+                         int32_t* topk_ids, float* topk_weights, uint32_t* bitmatrix,
+                         int32_t* counts, int32_t* offsets, int32_t* gather, int32_t* scatter,
+                         uint16_t* y_sorted, uint16_t* y, void* ws, hipStream_t st) {
+  if (T == 0)
+    return from_hip(launch_offsets(nullptr, nullptr, 0, E, k, counts, offsets, nullptr, nullptr,
+                                   nullptr, st));
+  WsLayout L;
+  moe_status s = workspace_layout(T, E, k, H, I, &L);
+  if (s != MOE_OK) return s;
+  // the routing side writes the FFN's row-tile plan: the one-launch front-end
+  // (T <= 64), else the expert-offsets kernel (T <= 512) or its scan step
+  const int tile_rows = ffn_tile_rows(T, E, k);
+  char* wsb = static_cast<char*>(ws);
+  const PlanOut plan{tile_rows, ffn_tile_bound(T * k, E, tile_rows),
+                     reinterpret_cast<int32_t*>(wsb + L.ffn_plan_offset),
+                     wsb + L.ffn_plan_offset + 256};
+  bool plan_written = false;
+  hipError_t e = launch_route_and_group(logits, T, E, k, topk_ids, topk_weights, bitmatrix,
+                                        counts, offsets, gather, scatter, ws, st, &plan,
+                                        &plan_written);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  e = launch_ffn(x, T, H, I, E, k, w1, w1_scale, w2, w2_scale, counts, offsets, gather,
+                 swiglu_limit, y_sorted, ws, L.ffn_h_offset, L.ffn_plan_offset, L.tile_bound, st,
+                 nullptr, plan_written);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  return from_hip(launch_combine(y_sorted, topk_weights, scatter, T, H, k, y, st));
+}
+
+}  // namespace moe
+
 extern "C" {
 
 moe_status moe_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* topk_ids,
@@ -84,42 +138,13 @@ moe_status moe_forward_mxfp4(const float* logits, const uint16_t* x, int64_t T, 
                              uint32_t* bitmatrix, int32_t* counts, int32_t* offsets,
                              int32_t* gather, int32_t* scatter, uint16_t* y_sorted, uint16_t* y,
                              void* ws, size_t ws_bytes, void* stream) {
-  moe_status s = moe::check_route(logits, T, E, k, topk_ids, topk_weights);
+  moe_status s = moe::check_forward(logits, x, T, H, I, E, k, w1, w1_scale, w2, w2_scale,
+                                    topk_ids, topk_weights, bitmatrix, counts, offsets, gather,
+                                    scatter, y_sorted, y, ws, ws_bytes);
   if (s != MOE_OK) return s;
-  s = moe::check_bitmatrix(topk_ids, T, E, k, bitmatrix);
-  if (s != MOE_OK) return s;
-  s = moe::check_offsets(bitmatrix, topk_ids, T, E, k, counts, offsets, gather, scatter, ws,
-                         ws_bytes);
-  if (s != MOE_OK) return s;
-  s = moe::check_ffn(x, T, H, I, E, k, w1, w1_scale, w2, w2_scale, counts, offsets, gather,
-                     y_sorted, ws, ws_bytes);
-  if (s != MOE_OK) return s;
-  s = moe::check_combine(y_sorted, topk_weights, scatter, T, H, k, y);
-  if (s != MOE_OK) return s;
-  const hipStream_t st = as_stream(stream);
-  if (T == 0)
-    return from_hip(moe::launch_offsets(nullptr, nullptr, 0, E, k, counts, offsets, nullptr,
-                                        nullptr, nullptr, st));
-  moe::WsLayout L;
-  s = moe::workspace_layout(T, E, k, H, I, &L);
-  if (s != MOE_OK) return s;
-  // the routing side writes the FFN's row-tile plan: the one-launch front-end
-  // (T <= 64), else the expert-offsets kernel (T <= 512) or its scan step
-  const int tile_rows = moe::ffn_tile_rows(T, E, k);
-  char* wsb = static_cast<char*>(ws);
-  const moe::PlanOut plan{tile_rows, moe::ffn_tile_bound(T * k, E, tile_rows),
-                          reinterpret_cast<int32_t*>(wsb + L.ffn_plan_offset),
-                          wsb + L.ffn_plan_offset + 256};
-  bool plan_written = false;
-  hipError_t e = moe::launch_route_and_group(logits, T, E, k, topk_ids, topk_weights, bitmatrix,
-                                             counts, offsets, gather, scatter, ws, st, &plan,
-                                             &plan_written);
-  if (e != hipSuccess) return MOE_ERR_HIP;
-  e = moe::launch_ffn(x, T, H, I, E, k, w1, w1_scale, w2, w2_scale, counts, offsets, gather,
-                      swiglu_limit, y_sorted, ws, L.ffn_h_offset, L.ffn_plan_offset, L.tile_bound,
-                      st, nullptr, plan_written);
-  if (e != hipSuccess) return MOE_ERR_HIP;
-  return from_hip(moe::launch_combine(y_sorted, topk_weights, scatter, T, H, k, y, st));
+  return moe::forward_layer(logits, x, T, H, I, E, k, w1, w1_scale, w2, w2_scale, swiglu_limit,
+                            topk_ids, topk_weights, bitmatrix, counts, offsets, gather, scatter,
+                            y_sorted, y, ws, as_stream(stream));
 }
 
 moe_status moe_grouped_ffn_mxfp4_timed(const uint16_t* x, int64_t T, int32_t H, int32_t I,

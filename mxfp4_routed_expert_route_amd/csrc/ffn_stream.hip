@@ -64,7 +64,13 @@ void gemm_stream_kernel(
   const int gw = blk * 4 + (threadIdx.x >> 6);
   const int tile_id = gw / waves_per_tile;
   const int cg = gw - tile_id * waves_per_tile;
-  if (tile_id >= *n_tiles) return;   // per wavefront: no workgroup barrier in this kernel
+  // A workgroup's four wavefronts share one tile exactly when waves_per_tile is a
+  // multiple of 4; only then may the kernel take the paths with workgroup barriers
+  // (activation rows in LDS, the ring), and only then is this return uniform over
+  // the workgroup.  Otherwise each wavefront returns on its own, and no barrier
+  // follows.
+  const bool shared_tile = (waves_per_tile & 3) == 0;
+  if (tile_id >= *n_tiles) return;
   const RowTile rt = tiles[tile_id];
   const int r16 = lane & 15, g = lane >> 4;
   const int n_chunks = K / kFfnKChunk;
@@ -99,8 +105,8 @@ void gemm_stream_kernel(
   // loads -- as many 16-byte loads per chunk as the weights, mostly of rows past
   // the tile -- from the vector-memory queue.
   const int nvalid = rt.p_end - rt.p_begin;
-  const bool small_a = kDeep && MSUB == 1 && a_lds_rows > 0 && nvalid <= a_lds_rows;
-  const bool ring = kDeep && a_ring != 0 && !small_a;   // uniform (one tile)
+  const bool small_a = kDeep && MSUB == 1 && shared_tile && a_lds_rows > 0 && nvalid <= a_lds_rows;
+  const bool ring = kDeep && shared_tile && a_ring != 0 && !small_a;   // uniform (one tile)
   unsigned char* a_lds = reinterpret_cast<unsigned char*>(scale_lds + 4 * n_chunks * 16 * kFrag);
   const int a_row_bytes = K * 2;
   if (small_a) {   // uniform over the workgroup (one tile)

@@ -57,3 +57,25 @@ hipError_t launch_combine(const uint16_t* ys, const float* w, const int32_t* sca
                           int H, int k, uint16_t* y, hipStream_t stream);
 
 }  // namespace moe
+
+#include "../../include/moe_mxfp4.h"
+
+namespace moe {
+
+// The whole layer (moe_forward_mxfp4): the host checks of every step, then the
+// launches with workspace `ws` (at least moe_workspace_bytes for these sizes).
+moe_status check_forward(const float* logits, const uint16_t* x, int64_t T, int32_t H, int32_t I,
+                         int32_t E, int32_t k, const uint8_t* w1, const uint8_t* w1_scale,
+                         const uint8_t* w2, const uint8_t* w2_scale, const int32_t* topk_ids,
+                         const float* topk_weights, const uint32_t* bitmatrix,
+                         const int32_t* counts, const int32_t* offsets, const int32_t* gather,
+                         const int32_t* scatter, const uint16_t* y_sorted, const uint16_t* y,
+                         const void* ws, size_t ws_bytes);
+moe_status forward_layer(const float* logits, const uint16_t* x, int64_t T, int32_t H, int32_t I,
+                         int32_t E, int32_t k, const uint8_t* w1, const uint8_t* w1_scale,
+                         const uint8_t* w2, const uint8_t* w2_scale, float swiglu_limit,
+                         int32_t* topk_ids, float* topk_weights, uint32_t* bitmatrix,
+                         int32_t* counts, int32_t* offsets, int32_t* gather, int32_t* scatter,
+                         uint16_t* y_sorted, uint16_t* y, void* ws, hipStream_t st);
+
+}  // namespace moe
