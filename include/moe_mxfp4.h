@@ -214,6 +214,33 @@ moe_status moe_forward_mxfp4(const float* logits, const uint16_t* x, int64_t T, 
                              void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * moe_forward_mxfp4_noalloc -- moe_forward_mxfp4 for callers that cannot
+ * allocate device memory: code under HIP stream capture, tight serving loops,
+ * harnesses that forbid the allocator.  Same arguments, outputs, checks and
+ * kernels as moe_forward_mxfp4, minus the workspace: the library uses its own
+ * static device scratch of MOE_NOALLOC_SCRATCH_BYTES instead (one copy per GPU,
+ * held until the process ends; the call itself allocates nothing).
+ *   - Sizes whose moe_workspace_bytes(T, E, k, H, I) exceeds
+ *     MOE_NOALLOC_SCRATCH_BYTES return MOE_ERR_WORKSPACE_TOO_SMALL and enqueue
+ *     nothing (at E = 256, k = 6, H = 4096, I = 2048: up to T = 2729 tokens).
+ *   - Every call on one GPU shares that GPU's scratch, which keeps the last
+ *     call's contents (no kernel needs it cleared).  Calls that overlap on one
+ *     GPU (other streams, other threads) race; serialise them.
+ *   - The first call on a GPU looks up the scratch's device address there (a
+ *     HIP symbol query, no allocation); MOE_ERR_HIP if that fails.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+moe_status moe_forward_mxfp4_noalloc(const float* logits, const uint16_t* x, int64_t T,
+                                     int32_t H, int32_t I, int32_t E, int32_t k,
+                                     const uint8_t* w1, const uint8_t* w1_scale,
+                                     const uint8_t* w2, const uint8_t* w2_scale,
+                                     float swiglu_limit, int32_t* topk_ids, float* topk_weights,
+                                     uint32_t* bitmatrix, int32_t* counts, int32_t* offsets,
+                                     int32_t* gather, int32_t* scatter, uint16_t* y_sorted,
+                                     uint16_t* y, void* stream);
+
+/*
  * Workspace bytes that moe_expert_offsets and moe_grouped_ffn_mxfp4 need for
  * these sizes (one buffer of this size serves both calls, used one at a time,
  * and moe_route_and_group and moe_forward_mxfp4).

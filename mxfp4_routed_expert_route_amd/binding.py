@@ -50,6 +50,8 @@ _SIG = {
     "moe_combine": [_P, _P, _P, _I64, _I32, _I32, _P, _P],
     "moe_forward_mxfp4": [_P, _P, _I64, _I32, _I32, _I32, _I32, _P, _P, _P, _P, ctypes.c_float,
                           _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    "moe_forward_mxfp4_noalloc": [_P, _P, _I64, _I32, _I32, _I32, _I32, _P, _P, _P, _P,
+                                  ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "moe_read_probe": [_P, ctypes.c_size_t, _P, _P],
     "moe_workspace_bytes": [_I64, _I32, _I32, _I32, _I32],
     "moe_status_string": [ctypes.c_int],
@@ -181,6 +183,28 @@ def moe_forward_mxfp4(logits, x, k: int, w1, w1_scale, w2, w2_scale, swiglu_limi
         _ptr(scatter, torch.int32, "scatter"), _ptr(y_sorted, BF16, "y_sorted"),
         _ptr(y, BF16, "y"), _ptr(ws, torch.uint8, "ws"), ws.numel() if ws is not None else 0,
         _stream(stream)))
+
+
+# moe_forward_mxfp4_noalloc's static device scratch (MOE_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def moe_forward_mxfp4_noalloc(logits, x, k: int, w1, w1_scale, w2, w2_scale,
+                              swiglu_limit: float, topk_ids, topk_weights, bitmatrix, counts,
+                              offsets, gather, scatter, y_sorted, y, stream=None):
+    T, E = logits.shape
+    H = x.shape[1]
+    two_i = w1.shape[1]
+    _check("moe_forward_mxfp4_noalloc", load().moe_forward_mxfp4_noalloc(
+        _ptr(logits, torch.float32, "logits"), _ptr(x, BF16, "x"), T, H, two_i // 2, E, k,
+        _ptr(w1, torch.uint8, "w1"), _ptr(w1_scale, torch.uint8, "w1_scale"),
+        _ptr(w2, torch.uint8, "w2"), _ptr(w2_scale, torch.uint8, "w2_scale"),
+        float(swiglu_limit), _ptr(topk_ids, torch.int32, "topk_ids"),
+        _ptr(topk_weights, torch.float32, "topk_weights"),
+        _ptr(bitmatrix, torch.int32, "bitmatrix"), _ptr(counts, torch.int32, "counts"),
+        _ptr(offsets, torch.int32, "offsets"), _ptr(gather, torch.int32, "gather"),
+        _ptr(scatter, torch.int32, "scatter"), _ptr(y_sorted, BF16, "y_sorted"),
+        _ptr(y, BF16, "y"), _stream(stream)))
 
 
 READ_PROBE_SINK_WORDS = 2048

@@ -91,3 +91,26 @@ def test_error_codes_through_the_abi(lib):
     assert fwd(16, 4100, 2048, 256, 6, nulls, 0) == INVALID          # nulls are checked first
     assert fwd(-1, 4096, 2048, 256, 6, nulls, 0) == INVALID
     assert fwd(16, 4096, 2048, 256, 9, nulls, 0) == UNSUPPORTED      # k > 8
+
+
+def test_noalloc_entry_point_host_checks(lib):
+    # moe_forward_mxfp4_noalloc runs every host check before any HIP call: invalid
+    # arguments and sizes beyond its static scratch return without touching a GPU
+    P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    lib.moe_forward_mxfp4_noalloc.argtypes = [P, P, I64, I32, I32, I32, I32, P, P, P, P,
+                                              ctypes.c_float] + [P] * 10
+    lib.moe_workspace_bytes.argtypes = [I64, I32, I32, I32, I32]
+    lib.moe_workspace_bytes.restype = ctypes.c_size_t
+    fwd = lambda T, H, I, E, k, ptrs: lib.moe_forward_mxfp4_noalloc(
+        *ptrs[:2], T, H, I, E, k, *ptrs[2:6], 10.0, *ptrs[6:15], None)
+    scratch = 64 << 20   # MOE_NOALLOC_SCRATCH_BYTES
+    fake = [4096] * 15   # aligned stand-in device pointers: never dereferenced by the checks
+    assert fwd(16, 4096, 2048, 256, 6, [None] * 15) == INVALID
+    assert fwd(16, 4096, 2048, 256, 9, fake) == UNSUPPORTED
+    assert fwd(16, 4100, 2048, 256, 6, fake) == UNSUPPORTED
+    assert lib.moe_workspace_bytes(2729, 256, 6, 4096, 2048) <= scratch
+    assert lib.moe_workspace_bytes(2730, 256, 6, 4096, 2048) > scratch
+    assert fwd(2730, 4096, 2048, 256, 6, fake) == WS_SMALL
+    assert fwd(8191, 4096, 2048, 256, 6, fake) == WS_SMALL
+    header = open(HEADERS[0]).read()
+    assert re.search(r"#define MOE_NOALLOC_SCRATCH_BYTES \(\(size_t\)64 << 20\)", header)
