@@ -47,7 +47,7 @@ void gemm_stream_kernel(
     int ld_out, int a_lds_rows, int a_ring) {
   // kDeep: per wavefront [K/128][16][4] dwords of scales; after the four
   // wavefronts' scales, either a_lds_rows activation rows of K bf16 and a
-  // 512-byte zero block, or the ring (two slots of 16*MSUB rows of 528 bytes)
+  // 512-byte zero block, or the ring (two slots of 16*MSUB rows of 512 bytes)
   extern __shared__ uint32_t scale_lds[];
   const int lane = threadIdx.x & 63;
   // 32-row tiles: each XCD takes whole tiles (tile x, x+8, ... for XCD x, the
@@ -159,15 +159,20 @@ void gemm_stream_kernel(
     // lane L stages the scales of row (f = L/16, column L%16); with two fragments
     // per wavefront lanes 32..63 have no row.  The 8 scale bytes of a 256-element
     // chunk c2 (2 per lane group) go to the two dwords
-    // my_scales[((c2*16 + L%16)*kFrag + f)*2 + {0,1}]
+    // my_scales[(((c2*kFrag/2 + f/2)*16 + L%16)*2 + f%2)*2 + {0,1}]: each 16-byte
+    // LDS read of the K loop (fragments 2h, 2h+1 of one row) then sits at quad
+    // L%16 of its 256-byte block, a bank pattern without read conflicts (see the
+    // tiled kernel's activation layout)
     const int f = lane >> 4;
     const uint8_t* srow = wsc + (e_rows + wrow(f, r16)) * row_s;
     auto put = [&](int c, const uint4& d) {   // c counts 128-element chunks
       const int c2 = c / 2;
-      my_scales[(((c2 + 0) * 16 + r16) * kFrag + f) * 2 + 0] = d.x;
-      my_scales[(((c2 + 0) * 16 + r16) * kFrag + f) * 2 + 1] = d.y;
-      my_scales[(((c2 + 1) * 16 + r16) * kFrag + f) * 2 + 0] = d.z;
-      my_scales[(((c2 + 1) * 16 + r16) * kFrag + f) * 2 + 1] = d.w;
+      uint32_t* s0 = my_scales + ((((c2 + 0) * (kFrag / 2) + f / 2) * 16 + r16) * 2 + f % 2) * 2;
+      uint32_t* s1 = my_scales + ((((c2 + 1) * (kFrag / 2) + f / 2) * 16 + r16) * 2 + f % 2) * 2;
+      s0[0] = d.x;
+      s0[1] = d.y;
+      s1[0] = d.z;
+      s1[1] = d.w;
     };
     // four 16-byte loads in flight before their stores (a load-then-store loop
     // waits one memory latency per iteration, with every wavefront of the grid
@@ -261,11 +266,12 @@ void gemm_stream_kernel(
         a[0][t] = *reinterpret_cast<const bf16x8*>(a_mine + c2 * a_step + 16 * t);
     };
     auto compute2 = [&](const uint4 (&q)[kFrag][2], const bf16x8 (&a)[MSUB][8], int c2) {
-      // a row slot holds kFrag fragments x 2 dwords: one 16-byte read per two
-      const uint4 d0 = *reinterpret_cast<const uint4*>(my_scales + ((c2 * 16 + r16) * kFrag) * 2);
+      // one 16-byte read per two fragments (2 dwords each) of the lane's row
+      const uint4 d0 =
+          *reinterpret_cast<const uint4*>(my_scales + ((c2 * (kFrag / 2) + 0) * 16 + r16) * 4);
       uint4 d1 = d0;
       if constexpr (kFrag == 4)
-        d1 = *reinterpret_cast<const uint4*>(my_scales + ((c2 * 16 + r16) * kFrag) * 2 + 4);
+        d1 = *reinterpret_cast<const uint4*>(my_scales + ((c2 * (kFrag / 2) + 1) * 16 + r16) * 4);
       const uint32_t sd[4][2] = {{d0.x, d0.y}, {d0.z, d0.w}, {d1.x, d1.y}, {d1.z, d1.w}};
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
@@ -314,10 +320,14 @@ void gemm_stream_kernel(
     // Larger tiles with a_ring: the workgroup stages each 256-element activation
     // chunk once (16*MSUB rows x 512 bytes; 16/MSUB threads per row, each load
     // instruction reading 256/MSUB contiguous bytes of every row) into a two-slot
-    // LDS ring with rows padded to 528 bytes, one barrier per chunk; the chunk
-    // after next is in flight in registers meanwhile.
+    // LDS ring, one barrier per chunk; the chunk after next is in flight in
+    // registers meanwhile.  A slot is piece-major: 16-byte piece q (0..31) of row r
+    // at (q * 16*MSUB + (r ^ (q & 7))) * 16, so the reads of a K step (piece 8g + t
+    // of each lane's row) sit at bank quad r ^ t, a function of the row alone, and
+    // eight consecutive lanes storing one row's pieces hit distinct quads (the
+    // tiled kernel's activation layout states the measured rule).
     auto run_ring = [&]() __attribute__((always_inline)) {
-      constexpr int kRowPad = 528, kSlot = 16 * MSUB * kRowPad;
+      constexpr int kRR = 16 * MSUB, kSlot = 32 * kRR * 16;
       constexpr int kTpr = 16 / MSUB, kPc = 2 * MSUB;   // threads per row, pieces per thread
       const int sr = threadIdx.x / kTpr, sp = threadIdx.x % kTpr;
       uint32_t srow = kRsrcOutOfRange;
@@ -340,18 +350,20 @@ void gemm_stream_kernel(
                                                arsrc, srow + 16 * (sp + kTpr * i), c2 * 512, 0));
       };
       auto stage_store = [&](const uint4 (&r)[kPc], int slot) __attribute__((always_inline)) {
-        unsigned char* d = a_lds + slot * kSlot + sr * kRowPad + 16 * sp;
+        // piece sp + kTpr * i of row sr; kTpr is a multiple of 8, so the row XOR is sp & 7
+        unsigned char* d = a_lds + slot * kSlot + (sp * kRR + (sr ^ (sp & 7))) * 16;
 #pragma unroll
-        for (int i = 0; i < kPc; ++i) *reinterpret_cast<uint4*>(d + 16 * kTpr * i) = r[i];
+        for (int i = 0; i < kPc; ++i) *reinterpret_cast<uint4*>(d + kTpr * i * kRR * 16) = r[i];
       };
-      const unsigned char* a_rd = a_lds + r16 * kRowPad + 128 * g;
       auto read_a = [&](bf16x8 (&a)[MSUB][8], int c2) __attribute__((always_inline)) {
+        const unsigned char* base = a_lds + (c2 & 1) * kSlot;
 #pragma unroll
-        for (int mi = 0; mi < MSUB; ++mi)
+        for (int t = 0; t < 8; ++t) {
+          const int off = ((8 * g + t) * kRR + (r16 ^ t)) * 16;   // piece 8g + t
 #pragma unroll
-          for (int t = 0; t < 8; ++t)
-            a[mi][t] = *reinterpret_cast<const bf16x8*>(a_rd + mi * 16 * kRowPad + (c2 & 1) * kSlot +
-                                                        16 * t);
+          for (int mi = 0; mi < MSUB; ++mi)
+            a[mi][t] = *reinterpret_cast<const bf16x8*>(base + off + mi * 256);
+        }
       };
       uint4 sa[kPc];
       uint4 q0[kFrag][2], q1[kFrag][2];
@@ -464,7 +476,7 @@ hipError_t launch_stream_t(unsigned grid, hipStream_t stream, const uint16_t* ac
   size_t a_bytes = a_rows > 0 ? static_cast<size_t>(a_rows) * K * 2 + 512 : 0;
   // the ring: two chunks of 16*MSUB padded rows, within the workgroup's share of
   // LDS
-  const size_t ring_bytes = 2 * 16 * MSUB * 528;
+  const size_t ring_bytes = 2 * 16 * MSUB * 512;
   const size_t budget = max_lds;
   const int a_ring = wpt % 4 == 0 && lds + ring_bytes <= budget ? 1 : 0;
   if (a_ring && ring_bytes > a_bytes) a_bytes = ring_bytes;

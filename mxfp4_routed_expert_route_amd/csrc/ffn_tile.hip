@@ -15,8 +15,8 @@ namespace {
 // fragments) and all kMSub 16-row MFMA subtiles of the tile, so each dequantised
 // weight fragment feeds kMSub MFMAs.  The activation tile of each K chunk
 // (kMSub*16 rows x 128 bf16) is loaded once per workgroup into LDS
-// (double-buffered; rows padded by 16 bytes so that the 16 lanes of a read group
-// hit distinct banks) and read by all its wavefronts.  Weights go straight to
+// (double-buffered, in the conflict-free layout described at kAPieces) and read
+// by all its wavefronts.  Weights go straight to
 // registers, issued right after the chunk that frees their registers.  The E8M0
 // scales of the wavefronts' weight rows are staged in LDS for all of K while they
 // fit beside the activation buffers (K <= 4096 for both shapes; staging them
@@ -59,11 +59,25 @@ namespace {
 // (prefill batches: most experts are one tile, so there is no slice to share)
 // each XCD takes whole tiles instead: all 16 column blocks of a tile read its
 // activation chunks from one L2 (prefill-2048 W1 ~566 -> ~549 us).
-constexpr int kARowBytes = kFfnKChunk * 2 + 16;   // 256 B of bf16 + 16 B pad
+//
+// LDS layout of a staged activation chunk.  A chunk row is 256 bytes: kAPieces
+// pieces of 16 bytes (8 bf16).  MFMA step s of lane group g reads piece q = 4g + s
+// of its row (the K order the weights' lane layout gives), so the chunk is stored
+// piece-major -- [q][row] -- with the row index's bits 1..2 XOR'd by 2(q & 3):
+// byte offset (q * rows + (row ^ 2(q & 3))) * 16.  Measured on gfx950 (a probe of
+// ds_read_b128 / ds_write_b128 patterns with the SQ_LDS_BANK_CONFLICT counter), a
+// 128-bit read spends no conflict cycles when a lane's bank quad (address / 16
+// mod 16) depends only on its MFMA row (lane & 15), and extra cycles whenever it
+// also depends on the lane group: 272-byte padded rows, whose quad is
+// (row + 4g + s) mod 16, cost 4 cycles per read.  Here a read's quad is
+// row ^ 2s.  A 128-bit write takes 8 lanes at a time over 32 banks; the staging
+// below gives 8 consecutive lanes two rows x four pieces, whose quads (mod 8)
+// row ^ 2s are all distinct.
+constexpr int kAPieces = kFfnKChunk * 2 / 16;
 constexpr int kXcds = 8;
 
 template <int kMSub>
-constexpr int a_buf_bytes() { return kMSub * 16 * kARowBytes; }
+constexpr int a_buf_bytes() { return kMSub * 16 * kAPieces * 16; }
 // LDS of the staged E8M0 scales: per wavefront, one dword per (128-element chunk,
 // weight row) of its 64 rows
 inline size_t tile_scale_lds_bytes(int K, int waves) {
@@ -120,12 +134,13 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
   const bool store_cols = cg_raw < waves_per_tile;
   const int cg = store_cols ? cg_raw : waves_per_tile - 1;
 
-  // --- activation staging: thread t stages the 16-byte part t % 16 of rows
-  // t / 16 + kRowStride * i of the chunk: sixteen consecutive lanes cover one
-  // row's 256 contiguous bytes, so each load instruction reads whole 256-byte row
-  // pieces, and any multiple of 16 rows maps onto the workgroup
+  // --- activation staging: thread t stages piece aq = 4((t >> 3) & 3) + (t & 3) of
+  // rows ar + kRowStride * i, ar = 2(t >> 5) + ((t >> 2) & 1): four consecutive
+  // lanes read 64 contiguous bytes of one row, eight lanes two rows, 32 lanes two
+  // whole 256-byte rows; kRowStride rows per piece index i, so any multiple of 16
+  // rows maps onto the workgroup
   const __amdgpu_buffer_rsrc_t arsrc = make_rsrc(act, act_bytes);
-  const int ar = tid >> 4, aq = tid & 15;
+  const int ar = 2 * (tid >> 5) + ((tid >> 2) & 1), aq = 4 * ((tid >> 3) & 3) + (tid & 3);
   uint32_t aoff[kPieces];
 #pragma unroll
   for (int i = 0; i < kPieces; ++i) {
@@ -143,8 +158,8 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
     }
     aoff[i] = valid ? row * static_cast<uint32_t>(K) * 2u + 16u * aq : kRsrcOutOfRange;
   }
-  unsigned char* a_lds = tile_lds;                       // [2][kRows][kARowBytes]
-  const int a_store = ar * kARowBytes + aq * 16;
+  unsigned char* a_lds = tile_lds;                       // [2][kAPieces][kRows][16 B]
+  const int a_store = (aq * kRows + (ar ^ (2 * (aq & 3)))) * 16;
   // np: the pieces that hold rows of the subtiles a tile runs (a constant at each
   // call site); pieces past them are neither loaded nor stored
   auto load_a = [&](uint4 (&ra)[kPieces], int kc, int np) {
@@ -158,14 +173,21 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
 #pragma unroll
     for (int i = 0; i < kPieces; ++i)
       if (i < np)
-        *reinterpret_cast<uint4*>(a_lds + buf * kABuf + a_store + kRowStride * i * kARowBytes) =
-            ra[i];
+        *reinterpret_cast<uint4*>(a_lds + buf * kABuf + a_store + kRowStride * i * 16) = ra[i];
   };
 
   // --- weights: kFrag fragments of 16 rows, this lane's row in each
+  // The weights are the MFMA's A operand and the activations its B operand, so a
+  // lane of D holds rows 4g .. 4g+3 of each fragment (weight rows, i.e. output
+  // columns) for one activation row (lane & 15).  Lane m of fragment f loads weight
+  // row wrow(f, m), chosen so that a lane's D values are consecutive output
+  // columns: W2, 16 columns 16g .. 16g+15 of the wavefront's 64 (fragment f, row
+  // i at 16g + 4f + i); W1, 8 gate columns 8g .. 8g+7 of its 32 and the matching up
+  // columns.  The epilogue then stores 16 bytes per lane and instruction.
   auto wrow = [&](int f, int c16) {
-    return kW1 ? (f >= kGate ? half : 0) + cg * (16 * kGate) + (f % kGate) * 16 + c16
-               : cg * (16 * kFrag) + f * 16 + c16;
+    return kW1 ? (f >= kGate ? half : 0) + cg * (16 * kGate) + (c16 >> 2) * (4 * kGate) +
+                     (f % kGate) * 4 + (c16 & 3)
+               : cg * (16 * kFrag) + (c16 >> 2) * (4 * kFrag) + f * 4 + (c16 & 3);
   };
   const size_t row_q = static_cast<size_t>(K / 2), row_s = static_cast<size_t>(K / 32);
   const size_t e_rows = static_cast<size_t>(rt.expert) * n_rows;
@@ -245,9 +267,11 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
     float scl[kFrag];
 #pragma unroll
     for (int f = 0; f < kFrag; ++f) scl[f] = e8m0_as_f32((dw[f] >> (8 * g)) & 0xFFu);
-    const unsigned char* abase = a_lds + buf * kABuf + r16 * kARowBytes + 64 * g;
+    const unsigned char* abase = a_lds + buf * kABuf;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
+      // piece 4g + s of row 16 mi + r16 (see kAPieces)
+      const int a_rd = ((4 * g + s) * kRows + (r16 ^ (2 * s))) * 16;
       bf16x8 b[kFrag];
 #pragma unroll
       for (int f = 0; f < kFrag; ++f) {
@@ -258,10 +282,10 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
       // branch here would cut the MFMA stream into blocks that each wait on one LDS read
 #pragma unroll
       for (int mi = 0; mi < NS; ++mi) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(abase + mi * 16 * kARowBytes + 16 * s);
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(abase + a_rd + mi * 256);
 #pragma unroll
         for (int f = 0; f < kFrag; ++f)
-          acc[mi][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[f], acc[mi][f], 0, 0, 0);
+          acc[mi][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[f], a, acc[mi][f], 0, 0, 0);
       }
       if constexpr (kMSub == 8) __builtin_amdgcn_sched_barrier(0);
     }
@@ -347,24 +371,35 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
   }
 
   if (!store_cols) return;
+  // D of fragment f, lane (r16, g), element i: activation row 16 mi + r16, output
+  // column wrow(f, 4g + i); per lane these are consecutive from column wrow(0, 4g)
   const bool do_clamp = clamp != 0;
+  const int col0 = wrow(0, 4 * g);
 #pragma unroll
   for (int mi = 0; mi < kMSub; ++mi) {
     if (mi >= msub) continue;
+    const int p = rt.p_begin + mi * 16 + r16;
+    if (p >= rt.p_end) continue;
+    uint16_t* orow = out + static_cast<int64_t>(p) * ld_out + col0;
+    if (kW1) {
+      uint32_t w[2 * kGate];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int p = rt.p_begin + mi * 16 + 4 * g + i;
-      if (p >= rt.p_end) continue;
-      uint16_t* orow = out + static_cast<int64_t>(p) * ld_out;
-      if (kW1) {
+      for (int f = 0; f < kGate; ++f)
 #pragma unroll
-        for (int f = 0; f < kGate; ++f)
-          orow[wrow(f, r16)] =
-              f32_to_bf16_bits(swiglu(acc[mi][f][i], acc[mi][f + kGate][i], limit, do_clamp));
-      } else {
+        for (int i = 0; i < 4; i += 2)
+          w[2 * f + i / 2] =
+              pack_bf16x2(swiglu(acc[mi][f][i], acc[mi][f + kGate][i], limit, do_clamp),
+                          swiglu(acc[mi][f][i + 1], acc[mi][f + kGate][i + 1], limit, do_clamp));
+      *reinterpret_cast<uint4*>(orow) = make_uint4(w[0], w[1], w[2], w[3]);
+    } else {
+      uint32_t w[2 * kFrag];
 #pragma unroll
-        for (int f = 0; f < kFrag; ++f) orow[wrow(f, r16)] = f32_to_bf16_bits(acc[mi][f][i]);
-      }
+      for (int f = 0; f < kFrag; ++f)
+#pragma unroll
+        for (int i = 0; i < 4; i += 2)
+          w[2 * f + i / 2] = pack_bf16x2(acc[mi][f][i], acc[mi][f][i + 1]);
+      *reinterpret_cast<uint4*>(orow) = make_uint4(w[0], w[1], w[2], w[3]);
+      *reinterpret_cast<uint4*>(orow + 8) = make_uint4(w[4], w[5], w[6], w[7]);
     }
   }
 }
