@@ -222,14 +222,14 @@ moe_status moe_forward_mxfp4(const float* logits, const uint16_t* x, int64_t T, 
  * held until the process ends; the call itself allocates nothing).
  *   - Sizes whose moe_workspace_bytes(T, E, k, H, I) exceeds
  *     MOE_NOALLOC_SCRATCH_BYTES return MOE_ERR_WORKSPACE_TOO_SMALL and enqueue
- *     nothing (at E = 256, k = 6, H = 4096, I = 2048: up to T = 2729 tokens).
+ *     nothing (at E = 256, k = 6, H = 4096, I = 2048: up to T = 4032 tokens).
  *   - Every call on one GPU shares that GPU's scratch, which keeps the last
  *     call's contents (no kernel needs it cleared).  Calls that overlap on one
  *     GPU (other streams, other threads) race; serialise them.
  *   - The first call on a GPU looks up the scratch's device address there (a
  *     HIP symbol query, no allocation); MOE_ERR_HIP if that fails.
  */
-#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
 
 moe_status moe_forward_mxfp4_noalloc(const float* logits, const uint16_t* x, int64_t T,
                                      int32_t H, int32_t I, int32_t E, int32_t k,

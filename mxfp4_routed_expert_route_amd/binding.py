@@ -186,7 +186,7 @@ def moe_forward_mxfp4(logits, x, k: int, w1, w1_scale, w2, w2_scale, swiglu_limi
 
 
 # moe_forward_mxfp4_noalloc's static device scratch (MOE_NOALLOC_SCRATCH_BYTES)
-NOALLOC_SCRATCH_BYTES = 64 << 20
+NOALLOC_SCRATCH_BYTES = 128 << 20
 
 
 def moe_forward_mxfp4_noalloc(logits, x, k: int, w1, w1_scale, w2, w2_scale,

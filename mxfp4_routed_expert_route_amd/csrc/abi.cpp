@@ -60,8 +60,7 @@ moe_status forward_layer(const float* logits, const uint16_t* x, int64_t T, int3
                                         &plan_written);
   if (e != hipSuccess) return MOE_ERR_HIP;
   e = launch_ffn(x, T, H, I, E, k, w1, w1_scale, w2, w2_scale, counts, offsets, gather,
-                 swiglu_limit, y_sorted, ws, L.ffn_h_offset, L.ffn_plan_offset, L.tile_bound, st,
-                 nullptr, plan_written);
+                 swiglu_limit, y_sorted, ws, L, st, nullptr, plan_written);
   if (e != hipSuccess) return MOE_ERR_HIP;
   return from_hip(launch_combine(y_sorted, topk_weights, scatter, T, H, k, y, st));
 }
@@ -127,8 +126,7 @@ moe_status moe_grouped_ffn_mxfp4(const uint16_t* x, int64_t T, int32_t H, int32_
   s = moe::workspace_layout(T, E, k, H, I, &L);
   if (s != MOE_OK) return s;
   return from_hip(moe::launch_ffn(x, T, H, I, E, k, w1, w1_scale, w2, w2_scale, counts, offsets,
-                                  gather, swiglu_limit, y_sorted, ws, L.ffn_h_offset,
-                                  L.ffn_plan_offset, L.tile_bound, as_stream(stream)));
+                                  gather, swiglu_limit, y_sorted, ws, L, as_stream(stream)));
 }
 
 moe_status moe_forward_mxfp4(const float* logits, const uint16_t* x, int64_t T, int32_t H,
@@ -164,8 +162,7 @@ moe_status moe_grouped_ffn_mxfp4_timed(const uint16_t* x, int64_t T, int32_t H, 
   hipEvent_t ev[3] = {static_cast<hipEvent_t>(events[0]), static_cast<hipEvent_t>(events[1]),
                       static_cast<hipEvent_t>(events[2])};
   return from_hip(moe::launch_ffn(x, T, H, I, E, k, w1, w1_scale, w2, w2_scale, counts, offsets,
-                                  gather, swiglu_limit, y_sorted, ws, L.ffn_h_offset,
-                                  L.ffn_plan_offset, L.tile_bound, as_stream(stream), ev));
+                                  gather, swiglu_limit, y_sorted, ws, L, as_stream(stream), ev));
 }
 
 moe_status moe_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream) {

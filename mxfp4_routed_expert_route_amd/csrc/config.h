@@ -52,6 +52,10 @@ inline int ffn_tile_rows(int64_t T, int E, int k) {
   return avg_rows < 96 ? 80 : 128;
 }
 
+// The tiled kernels (80- and 128-row tiles) run the block-scaled FP8 x FP4 MFMAs
+// on two-part FP8 activations; the streaming kernels run bf16 MFMAs.
+inline bool ffn_tiled(int64_t T, int E, int k) { return ffn_tile_rows(T, E, k) >= 80; }
+
 struct RowTile {
   int32_t expert;
   int32_t p_begin;

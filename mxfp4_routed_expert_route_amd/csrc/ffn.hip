@@ -10,6 +10,7 @@
 #include "ffn_common.h"
 #include "launch.h"
 #include "plan.h"
+#include "validate.h"
 
 namespace moe {
 namespace {
@@ -39,12 +40,13 @@ hipError_t launch_ffn(const uint16_t* x, int64_t T, int H, int I, int E, int k,
                       const uint8_t* w1, const uint8_t* w1s, const uint8_t* w2,
                       const uint8_t* w2s, const int32_t* counts, const int32_t* offsets,
                       const int32_t* gather, float limit, uint16_t* y_sorted, void* ws,
-                      size_t h_offset, size_t plan_offset, int64_t /*tile_bound_min_rows*/,
-                      hipStream_t stream, hipEvent_t const* events, bool plan_ready) {
+                      const WsLayout& L, hipStream_t stream, hipEvent_t const* events,
+                      bool plan_ready) {
   const int64_t n_slots = T * k;
-  uint16_t* h = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + h_offset);
-  int32_t* n_tiles = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + plan_offset);
-  RowTile* tiles = reinterpret_cast<RowTile*>(static_cast<char*>(ws) + plan_offset + 256);
+  char* wsb = static_cast<char*>(ws);
+  uint16_t* h = reinterpret_cast<uint16_t*>(wsb + L.ffn_h_offset);
+  int32_t* n_tiles = reinterpret_cast<int32_t*>(wsb + L.ffn_plan_offset);
+  RowTile* tiles = reinterpret_cast<RowTile*>(wsb + L.ffn_plan_offset + 256);
   const bool clamp = limit > 0.f && limit <= 3.402823466e38f;   // finite and positive
   const int clamp_i = clamp ? 1 : 0;
   const int slots_i = static_cast<int>(n_slots);
@@ -62,6 +64,12 @@ hipError_t launch_ffn(const uint16_t* x, int64_t T, int H, int I, int E, int k,
     plan_kernel<<<1, 1024, 0, stream>>>(counts, offsets, E, tile_rows, n_slots, tile_bound,
                                         n_tiles, tiles);
     err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  const bool tiled = tile_rows >= 80;
+  if (tiled) {   // x in two-part FP8 for the tiled kernels (ahead of the W1 event)
+    err = launch_act_split(x, T, H, reinterpret_cast<uint8_t*>(wsb + L.ffn_xq_offset),
+                           reinterpret_cast<uint8_t*>(wsb + L.ffn_xs_offset), stream);
     if (err != hipSuccess) return err;
   }
   if (events) {
@@ -92,19 +100,27 @@ hipError_t launch_ffn(const uint16_t* x, int64_t T, int H, int I, int E, int k,
     err = launch_stream(false, msub, g2, stream, h, h_bytes, nullptr, k, slots_i, w2, w2s, t,
                         n_tiles, I, H, 0, wpt2, limit, 0, y_sorted, H);
   } else {
+    // Tiled path: block-scaled FP4 x FP8 MFMAs on two-part FP8 activations (x was
+    // split above); W1 writes h in that form, W2 reads it.
+    uint8_t* xq = reinterpret_cast<uint8_t*>(wsb + L.ffn_xq_offset);
+    uint8_t* xs = reinterpret_cast<uint8_t*>(wsb + L.ffn_xs_offset);
+    uint8_t* hs = reinterpret_cast<uint8_t*>(wsb + L.ffn_hs_offset);
     // 80-row tiles with at most 64 rows per expert on average (most experts one
     // tile, so no weight slice to share between an expert's tiles): each XCD takes
     // whole tiles, and a tile's activation chunks are fetched into one L2
     const bool whole = tile_rows == 80 && T * k / E <= 64;
-    err = launch_tile(true, tile_rows, tile_bound, stream, x, x_bytes, gather, k, slots_i, w1,
-                      w1s, tiles, n_tiles, H, 2 * I, I, limit, clamp_i, h, I, whole);
+    TileArgs t1{tile_bound, xq, x_bytes, xs, static_cast<uint32_t>(T * (H / 32)), gather, k,
+                slots_i, w1, w1s, tiles, n_tiles, H, 2 * I, I, limit, clamp_i, h, hs, I, whole};
+    TileArgs t2{tile_bound, reinterpret_cast<const uint8_t*>(h), h_bytes, hs,
+                static_cast<uint32_t>(n_slots * (I / 32)), nullptr, k, slots_i, w2, w2s, tiles,
+                n_tiles, I, H, 0, limit, 0, y_sorted, nullptr, H, whole};
+    err = launch_tile(true, tile_rows, t1, stream);
     if (err != hipSuccess) return err;
     if (events) {
       err = hipEventRecord(events[1], stream);
       if (err != hipSuccess) return err;
     }
-    err = launch_tile(false, tile_rows, tile_bound, stream, h, h_bytes, nullptr, k, slots_i, w2,
-                      w2s, tiles, n_tiles, I, H, 0, limit, 0, y_sorted, H, whole);
+    err = launch_tile(false, tile_rows, t2, stream);
   }
   if (err != hipSuccess || !events) return err;
   return hipEventRecord(events[2], stream);

@@ -12,11 +12,16 @@ namespace {
 // wavefronts owns one row tile and kWaves x 16 x kFrag weight rows.  A wavefront
 // holds kFrag 16-row weight fragments (W1: kFrag/2 gate fragments and the
 // matching up fragments, so each SwiGLU pair meets in one lane; W2: kFrag output
-// fragments) and all kMSub 16-row MFMA subtiles of the tile, so each dequantised
-// weight fragment feeds kMSub MFMAs.  The activation tile of each K chunk
-// (kMSub*16 rows x 128 bf16) is loaded once per workgroup into LDS
-// (double-buffered, in the conflict-free layout described at kAPieces) and read
-// by all its wavefronts.  Weights go straight to
+// fragments) and all kMSub 16-row MFMA subtiles of the tile, so each weight
+// fragment feeds kMSub MFMAs.  The products are gfx950's block-scaled FP4 x FP8
+// MFMAs (v_mfma_scale_f32_16x16x128_f8f6f4): the weights' E2M1 codes and E8M0
+// scales go in as they are stored -- no dequantisation -- and the activations as
+// two-part FP8 (hi + lo with an E8M0 scale per 32 elements, exact for bf16
+// inputs; ffn_common.h), one MFMA per part, so the products run at the FP8 rate
+// twice, i.e. the bf16 rate, without the dequantisation instructions of a bf16
+// MFMA path.  The activation tile of each K chunk (kMSub*16 rows x 128 elements,
+// 256 bytes a row) is loaded once per workgroup into LDS (double-buffered, in the
+// layout described at kAPieces) and read by all its wavefronts.  Weights go straight to
 // registers, issued right after the chunk that frees their registers.  The E8M0
 // scales of the wavefronts' weight rows are staged in LDS for all of K while they
 // fit beside the activation buffers (K <= 4096 for both shapes; staging them
@@ -60,19 +65,18 @@ namespace {
 // each XCD takes whole tiles instead: all 16 column blocks of a tile read its
 // activation chunks from one L2 (prefill-2048 W1 ~566 -> ~549 us).
 //
-// LDS layout of a staged activation chunk.  A chunk row is 256 bytes: kAPieces
-// pieces of 16 bytes (8 bf16).  MFMA step s of lane group g reads piece q = 4g + s
-// of its row (the K order the weights' lane layout gives), so the chunk is stored
-// piece-major -- [q][row] -- with the row index's bits 1..2 XOR'd by 2(q & 3):
-// byte offset (q * rows + (row ^ 2(q & 3))) * 16.  Measured on gfx950 (a probe of
+// LDS layout of a staged activation chunk.  A chunk row is 256 bytes, 16 pieces
+// of 16 bytes: pieces 0..7 hold the row's 128 hi bytes, 8..15 its lo bytes, in
+// the MFMA's FP8 lane order (a8_pos).  Lane group g reads hi pieces 2g, 2g+1 and
+// lo pieces 8+2g, 9+2g of its row, so the chunk is stored piece-major -- [q][row]
+// -- with bit 2 of the row index flipped in odd pieces: byte offset
+// (q * rows + (row ^ 4(q & 1))) * 16.  Measured on gfx950 (a probe of
 // ds_read_b128 / ds_write_b128 patterns with the SQ_LDS_BANK_CONFLICT counter), a
 // 128-bit read spends no conflict cycles when a lane's bank quad (address / 16
 // mod 16) depends only on its MFMA row (lane & 15), and extra cycles whenever it
-// also depends on the lane group: 272-byte padded rows, whose quad is
-// (row + 4g + s) mod 16, cost 4 cycles per read.  Here a read's quad is
-// row ^ 2s.  A 128-bit write takes 8 lanes at a time over 32 banks; the staging
-// below gives 8 consecutive lanes two rows x four pieces, whose quads (mod 8)
-// row ^ 2s are all distinct.
+// also depends on the lane group (272-byte padded rows, quad (row + 4g + s) mod
+// 16, cost 4 cycles per read); here a read's quad is row or row ^ 4.  A 128-bit
+// write takes 8 lanes at a time over 32 banks.
 constexpr int kAPieces = kFfnKChunk * 2 / 16;
 constexpr int kXcds = 8;
 
@@ -85,14 +89,22 @@ inline size_t tile_scale_lds_bytes(int K, int waves) {
 }
 constexpr size_t kTileLdsPerWorkgroup = 80 * 1024;   // two workgroups per CU
 constexpr size_t kCuLds = 160 * 1024;                 // one workgroup per CU
+// LDS of a workgroup: two activation buffers, a scale dword per thread for each
+// (the rows' block scales), and the staged weight scales (when they are staged)
+inline size_t tile_lds_bytes(int msub, int K, int waves, bool lds_scales) {
+  const size_t rows = static_cast<size_t>(msub) * 16;
+  return 2 * rows * kAPieces * 16 + 2 * static_cast<size_t>(64 * waves) * 4 +
+         (lds_scales ? tile_scale_lds_bytes(K, waves) : 0);
+}
 
 template <bool kW1, int kMSub, int kFrag, int kWaves, bool kLdsScales>
 __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
-    const uint16_t* __restrict__ act, uint32_t act_bytes, const int32_t* __restrict__ gather,
-    int k_top, int n_slots, const uint8_t* __restrict__ wq, const uint8_t* __restrict__ wsc,
+    const uint8_t* __restrict__ act, uint32_t act_bytes, const uint8_t* __restrict__ asc,
+    uint32_t asc_bytes, const int32_t* __restrict__ gather, int k_top, int n_slots,
+    const uint8_t* __restrict__ wq, const uint8_t* __restrict__ wsc,
     const RowTile* __restrict__ tiles, const int32_t* __restrict__ n_tiles, int K, int n_rows,
     int half, int waves_per_tile, int blocks_per_tile, float limit, int clamp,
-    uint16_t* __restrict__ out, int ld_out, int whole_tiles) {
+    void* __restrict__ out, uint8_t* __restrict__ out_sc, int ld_out, int whole_tiles) {
   // the fragment count is a parameter of the indexing below, but only four
   // fragments per wavefront (64 weight rows) are instantiated and tested
   static_assert(kFrag == 4, "four weight fragments per wavefront");
@@ -134,12 +146,18 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
   const bool store_cols = cg_raw < waves_per_tile;
   const int cg = store_cols ? cg_raw : waves_per_tile - 1;
 
-  // --- activation staging: thread t stages piece aq = 4((t >> 3) & 3) + (t & 3) of
-  // rows ar + kRowStride * i, ar = 2(t >> 5) + ((t >> 2) & 1): four consecutive
-  // lanes read 64 contiguous bytes of one row, eight lanes two rows, 32 lanes two
-  // whole 256-byte rows; kRowStride rows per piece index i, so any multiple of 16
-  // rows maps onto the workgroup
+  // --- activation staging: a chunk row is 256 bytes (128 hi, 128 lo; see a8_pos).
+  // Thread t stages piece aq = 4((t >> 3) & 3) + (t & 3) of rows ar + kRowStride * i,
+  // ar = 2(t >> 5) + ((t >> 2) & 1): four consecutive lanes read 64 contiguous
+  // bytes of one row, 32 lanes two whole rows; kRowStride rows per piece index i,
+  // so any multiple of 16 rows maps onto the workgroup.  (Measured: a mapping
+  // whose eight-lane groups take four rows x two pieces, conflict-free for the LDS
+  // writes below, but with four different rows per four lanes, made the prefill
+  // kernels ~10% slower; this one pays a 2-way LDS write conflict instead.)
+  // Thread t < kRows also stages the scale dword (the four E8M0 block scales of the
+  // chunk) of tile row t.
   const __amdgpu_buffer_rsrc_t arsrc = make_rsrc(act, act_bytes);
+  const __amdgpu_buffer_rsrc_t srsrc = make_rsrc(asc, asc_bytes);
   const int ar = 2 * (tid >> 5) + ((tid >> 2) & 1), aq = 4 * ((tid >> 3) & 3) + (tid & 3);
   uint32_t aoff[kPieces];
 #pragma unroll
@@ -158,22 +176,42 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
     }
     aoff[i] = valid ? row * static_cast<uint32_t>(K) * 2u + 16u * aq : kRsrcOutOfRange;
   }
+  uint32_t soff = kRsrcOutOfRange;   // byte offset of tile row tid's chunk-0 scale dword
+  if (tid < kRows) {
+    const int p = rt.p_begin + tid;
+    if (p < rt.p_end) {
+      if (kW1) {
+        const int slot = gather[p];
+        if (static_cast<unsigned>(slot) < static_cast<unsigned>(n_slots))
+          soff = static_cast<uint32_t>(slot / k_top) * static_cast<uint32_t>(K / 32);
+      } else {
+        soff = static_cast<uint32_t>(p) * static_cast<uint32_t>(K / 32);
+      }
+    }
+  }
   unsigned char* a_lds = tile_lds;                       // [2][kAPieces][kRows][16 B]
-  const int a_store = (aq * kRows + (ar ^ (2 * (aq & 3)))) * 16;
+  uint32_t* a_scl = reinterpret_cast<uint32_t*>(tile_lds + 2 * kABuf);   // [2][kThreads]
+  const int a_store = (aq * kRows + (ar ^ (4 * (aq & 1)))) * 16;
   // np: the pieces that hold rows of the subtiles a tile runs (a constant at each
   // call site); pieces past them are neither loaded nor stored
-  auto load_a = [&](uint4 (&ra)[kPieces], int kc, int np) {
+  // ra: the thread's pieces; rs: its scale dword.  Every thread loads and stores
+  // one (threads >= kRows read the out-of-range offset, i.e. zero, into slots
+  // nobody reads): a branch on the thread index inside the K loop would split the
+  // loop body and the register allocator then spills the accumulators.
+  auto load_a = [&](uint4 (&ra)[kPieces], uint32_t& rs, int kc, int np) {
 #pragma unroll
     for (int i = 0; i < kPieces; ++i)
       if (i < np)
         ra[i] = __builtin_bit_cast(
             uint4, __builtin_amdgcn_raw_buffer_load_b128(arsrc, aoff[i] + kc * 256, 0, 0));
+    rs = __builtin_amdgcn_raw_buffer_load_b32(srsrc, soff + kc * 4, 0, 0);
   };
-  auto store_a = [&](const uint4 (&ra)[kPieces], int buf, int np) {
+  auto store_a = [&](const uint4 (&ra)[kPieces], uint32_t rs, int buf, int np) {
 #pragma unroll
     for (int i = 0; i < kPieces; ++i)
       if (i < np)
         *reinterpret_cast<uint4*>(a_lds + buf * kABuf + a_store + kRowStride * i * 16) = ra[i];
+    a_scl[buf * kThreads + tid] = rs;
   };
 
   // --- weights: kFrag fragments of 16 rows, this lane's row in each
@@ -220,7 +258,7 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
   // --- 80-row tiles: scales of the wavefront's 64 weight rows, staged as
   // [chunk][16][4] dwords
   uint32_t* my_scales =
-      reinterpret_cast<uint32_t*>(tile_lds + 2 * kABuf) + wave * (n_chunks * 64);
+      reinterpret_cast<uint32_t*>(tile_lds + 2 * kABuf + 2 * kThreads * 4) + wave * (n_chunks * 64);
   if constexpr (kLdsScales) {
     const int f = lane >> 4;
     const uint8_t* srow = wsc + (e_rows + wrow(f, r16)) * row_s;
@@ -251,8 +289,14 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
 #pragma unroll
     for (int f = 0; f < kFrag; ++f) acc[mi][f] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // one chunk: activations from LDS buffer `buf`, weights in q, scale dwords in sd;
-  // subtiles 0 .. NS-1 (NS = kMSub, or fewer when the tile's rows end earlier)
+  // one chunk: activations (two-part FP8) and their block scales from LDS buffer
+  // `buf`, weights (FP4 codes) in q, weight scale dwords in sd; subtiles 0 .. NS-1
+  // (NS = kMSub, or fewer when the tile's rows end earlier).  Per subtile and
+  // fragment two block-scaled MFMAs (16 x 16 x 128: FP4 weights x FP8 activations),
+  // one on the hi parts and one on the lo parts.  The MFMA takes lane 16b + c's
+  // scale for row / column c and 32-element block b: a lane of group g passes the
+  // scales of block g.
+  typedef int v8i __attribute__((ext_vector_type(8)));
   auto compute = [&](auto ns_c, const uint4 (&q)[kFrag], const uint32_t (&sd)[kFrag], int kc,
                      int buf) {
     constexpr int NS = decltype(ns_c)::value;
@@ -264,30 +308,43 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
 #pragma unroll
       for (int f = 0; f < kFrag; ++f) dw[f] = sd[f];
     }
-    float scl[kFrag];
+    int wsc_g[kFrag];   // byte 0: the scale of this lane's weight row, block g
+    v8i wb[kFrag];      // 32 FP4 codes of this lane's weight row: elements 32g .. 32g+31
 #pragma unroll
-    for (int f = 0; f < kFrag; ++f) scl[f] = e8m0_as_f32((dw[f] >> (8 * g)) & 0xFFu);
+    for (int f = 0; f < kFrag; ++f) {
+      wsc_g[f] = static_cast<int>(dw[f] >> (8 * g));
+      wb[f] = v8i{static_cast<int>(q[f].x), static_cast<int>(q[f].y), static_cast<int>(q[f].z),
+                  static_cast<int>(q[f].w), 0, 0, 0, 0};
+    }
     const unsigned char* abase = a_lds + buf * kABuf;
+    const uint32_t* ascl = a_scl + buf * kThreads;
+    // every subtile up to NS, also those past the tile's rows (they hold zeros)
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      // piece 4g + s of row 16 mi + r16 (see kAPieces)
-      const int a_rd = ((4 * g + s) * kRows + (r16 ^ (2 * s))) * 16;
-      bf16x8 b[kFrag];
+    for (int mi = 0; mi < NS; ++mi) {
+      const int row = 16 * mi + r16;
+      // hi: pieces 2g, 2g+1 (bytes 32g .. 32g+31 of the chunk's hi half); lo: 8 further
+      const uint4 h0 = *reinterpret_cast<const uint4*>(abase + ((2 * g) * kRows + row) * 16);
+      const uint4 h1 = *reinterpret_cast<const uint4*>(abase + ((2 * g + 1) * kRows + (row ^ 4)) * 16);
+      const uint4 l0 = *reinterpret_cast<const uint4*>(abase + ((8 + 2 * g) * kRows + row) * 16);
+      const uint4 l1 = *reinterpret_cast<const uint4*>(abase + ((9 + 2 * g) * kRows + (row ^ 4)) * 16);
+      const int asc_g = static_cast<int>(ascl[row] >> (8 * g));
+      const v8i ah = v8i{static_cast<int>(h0.x), static_cast<int>(h0.y), static_cast<int>(h0.z),
+                         static_cast<int>(h0.w), static_cast<int>(h1.x), static_cast<int>(h1.y),
+                         static_cast<int>(h1.z), static_cast<int>(h1.w)};
+      const v8i al = v8i{static_cast<int>(l0.x), static_cast<int>(l0.y), static_cast<int>(l0.z),
+                         static_cast<int>(l0.w), static_cast<int>(l1.x), static_cast<int>(l1.y),
+                         static_cast<int>(l1.z), static_cast<int>(l1.w)};
 #pragma unroll
       for (int f = 0; f < kFrag; ++f) {
-        const uint32_t wd = s == 0 ? q[f].x : s == 1 ? q[f].y : s == 2 ? q[f].z : q[f].w;
-        b[f] = dequant8(wd, scl[f]);
+        // formats: A (weights) FP4 E2M1 = 4, B (activations) FP8 E4M3 = 0
+        acc[mi][f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wb[f], ah, acc[mi][f], 4, 0, 0,
+                                                                       wsc_g[f], 0, asc_g);
+        acc[mi][f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wb[f], al, acc[mi][f], 4, 0, 0,
+                                                                       wsc_g[f], 0, asc_g);
       }
-      // every subtile up to NS, also those past the tile's rows (they hold zeros): a
-      // branch here would cut the MFMA stream into blocks that each wait on one LDS read
-#pragma unroll
-      for (int mi = 0; mi < NS; ++mi) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(abase + a_rd + mi * 256);
-#pragma unroll
-        for (int f = 0; f < kFrag; ++f)
-          acc[mi][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b[f], a, acc[mi][f], 0, 0, 0);
-      }
-      if constexpr (kMSub == 8) __builtin_amdgcn_sched_barrier(0);
+      // one subtile's operands live at a time (the compiler would otherwise hoist
+      // every subtile's LDS reads next to the 128 accumulators and spill)
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -303,22 +360,23 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
       constexpr int NS = decltype(ns_c)::value;
       constexpr int NP = (NS * 16 + kRowStride - 1) / kRowStride;   // pieces in use
       uint4 ra0[kPieces], ra1[kPieces];
-      load_a(ra0, 0, NP);
+      uint32_t rs0 = 0, rs1 = 0;
+      load_a(ra0, rs0, 0, NP);
       load_w(q0, s0, 0);
       load_w(q1, s1, last >= 1 ? 1 : 0);
-      load_a(ra1, last >= 1 ? 1 : 0, NP);
-      store_a(ra0, 0, NP);
+      load_a(ra1, rs1, last >= 1 ? 1 : 0, NP);
+      store_a(ra0, rs0, 0, NP);
       __syncthreads();
       for (; kc + 2 <= n_chunks; kc += 2) {
-        load_a(ra0, kc + 2 <= last ? kc + 2 : last, NP);
+        load_a(ra0, rs0, kc + 2 <= last ? kc + 2 : last, NP);
         compute(ns_c, q0, s0, kc, 0);
         load_w(q0, s0, kc + 2 <= last ? kc + 2 : last);
-        store_a(ra1, 1, NP);
+        store_a(ra1, rs1, 1, NP);
         __syncthreads();
-        load_a(ra1, kc + 3 <= last ? kc + 3 : last, NP);
+        load_a(ra1, rs1, kc + 3 <= last ? kc + 3 : last, NP);
         compute(ns_c, q1, s1, kc + 1, 1);
         load_w(q1, s1, kc + 3 <= last ? kc + 3 : last);
-        store_a(ra0, 0, NP);
+        store_a(ra0, rs0, 0, NP);
         __syncthreads();
       }
       if (kc < n_chunks) compute(ns_c, q0, s0, kc, 0);   // odd chunk count: last chunk in q0
@@ -342,21 +400,22 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
       constexpr int NS = decltype(ns_c)::value;
       constexpr int NP = (NS * 16 + kRowStride - 1) / kRowStride;   // pieces in use
       uint4 ra[kPieces];
-      load_a(ra, 0, NP);
+      uint32_t rs = 0;
+      load_a(ra, rs, 0, NP);
       load_w(q0, s0, 0);
       load_w(q1, s1, last >= 1 ? 1 : 0);
-      store_a(ra, 0, NP);
+      store_a(ra, rs, 0, NP);
       __syncthreads();
       for (; kc + 2 <= n_chunks; kc += 2) {
-        load_a(ra, kc + 1, NP);
+        load_a(ra, rs, kc + 1, NP);
         compute(ns_c, q0, s0, kc, 0);
         load_w(q0, s0, kc + 2 <= last ? kc + 2 : last);
-        store_a(ra, 1, NP);
+        store_a(ra, rs, 1, NP);
         __syncthreads();
-        load_a(ra, kc + 2 <= last ? kc + 2 : last, NP);
+        load_a(ra, rs, kc + 2 <= last ? kc + 2 : last, NP);
         compute(ns_c, q1, s1, kc + 1, 1);
         load_w(q1, s1, kc + 3 <= last ? kc + 3 : last);
-        store_a(ra, 0, NP);
+        store_a(ra, rs, 0, NP);
         __syncthreads();
       }
       if (kc < n_chunks) compute(ns_c, q0, s0, kc, 0);   // odd chunk count
@@ -377,21 +436,45 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
   const int col0 = wrow(0, 4 * g);
 #pragma unroll
   for (int mi = 0; mi < kMSub; ++mi) {
-    if (mi >= msub) continue;
+    if (mi >= msub) continue;   // uniform over the workgroup
     const int p = rt.p_begin + mi * 16 + r16;
-    if (p >= rt.p_end) continue;
-    uint16_t* orow = out + static_cast<int64_t>(p) * ld_out + col0;
-    if (kW1) {
-      uint32_t w[2 * kGate];
+    if constexpr (kW1) {
+      // h in two-part FP8: the wavefront's 32 gate columns cg*32 .. cg*32+31 are one
+      // 32-element block of h's row, held by the four lanes r16 + 16g (8 each); the
+      // block's largest magnitude comes from two lane exchanges, which every lane
+      // takes part in
+      float hv[8];
+      uint32_t m = 0;
 #pragma unroll
       for (int f = 0; f < kGate; ++f)
 #pragma unroll
-        for (int i = 0; i < 4; i += 2)
-          w[2 * f + i / 2] =
-              pack_bf16x2(swiglu(acc[mi][f][i], acc[mi][f + kGate][i], limit, do_clamp),
-                          swiglu(acc[mi][f][i + 1], acc[mi][f + kGate][i + 1], limit, do_clamp));
-      *reinterpret_cast<uint4*>(orow) = make_uint4(w[0], w[1], w[2], w[3]);
+        for (int i = 0; i < 4; ++i) {
+          hv[4 * f + i] = swiglu(acc[mi][f][i], acc[mi][f + kGate][i], limit, do_clamp);
+          const uint32_t a = __float_as_uint(hv[4 * f + i]) & 0x7FFFFFFFu;
+          m = a > m ? a : m;
+        }
+      uint32_t o = static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 16, 64));
+      m = o > m ? o : m;
+      o = static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 32, 64));
+      m = o > m ? o : m;
+      const uint32_t s = a8_scale_byte(m);
+      const float inv = a8_inv_scale(s);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) hv[i] *= inv;
+      uint2 hi, lo;
+      a8_split8(hv, hi, lo);
+      if (p >= rt.p_end) continue;
+      // block cg = chunk cg / 4, block cg % 4 of it; this lane's 8 elements are
+      // elements 8g .. 8g+7 of the block
+      uint8_t* orow = static_cast<uint8_t*>(out) + static_cast<int64_t>(p) * (2 * ld_out) +
+                      (cg / 4) * 256;
+      const int pos = a8_pos(32 * (cg % 4) + 16 * (g >> 1)) + 8 * (g & 1);
+      *reinterpret_cast<uint2*>(orow + pos) = hi;
+      *reinterpret_cast<uint2*>(orow + 128 + pos) = lo;
+      if (g == 0) out_sc[static_cast<int64_t>(p) * (ld_out / 32) + cg] = static_cast<uint8_t>(s);
     } else {
+      if (p >= rt.p_end) continue;
+      uint16_t* orow = static_cast<uint16_t*>(out) + static_cast<int64_t>(p) * ld_out + col0;
       uint32_t w[2 * kFrag];
 #pragma unroll
       for (int f = 0; f < kFrag; ++f)
@@ -405,69 +488,44 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
 }
 
 template <bool kW1, int kMSub, int kFrag, int kWaves, bool kLdsScales>
-hipError_t launch_tile_t(int64_t tile_bound, hipStream_t stream, const uint16_t* act,
-                         uint32_t act_bytes, const int32_t* gather, int k_top, int n_slots,
-                         const uint8_t* wq, const uint8_t* wsc, const RowTile* tiles,
-                         const int32_t* n_tiles, int K, int n_rows, int half, float limit,
-                         int clamp, uint16_t* out, int ld_out, bool whole_tiles) {
+hipError_t launch_tile_t(const TileArgs& t, hipStream_t stream) {
   // wavefronts per row tile: W1 pairs `half` gate rows with as many up rows, 16 *
   // kFrag/2 of each per wavefront; W2 covers n_rows output rows, 16 * kFrag each
-  const int wpt = kW1 ? half / (8 * kFrag) : n_rows / (16 * kFrag);
+  const int wpt = kW1 ? t.half / (8 * kFrag) : t.n_rows / (16 * kFrag);
   const int bpt = (wpt + kWaves - 1) / kWaves;
-  size_t lds = 2 * static_cast<size_t>(a_buf_bytes<kMSub>());
-  if (kLdsScales) lds += tile_scale_lds_bytes(K, kWaves);
+  size_t lds = tile_lds_bytes(kMSub, t.K, kWaves, kLdsScales);
   // whole tiles per XCD cover row tiles in groups of 8, the column-block/XCD split
   // in pairs: round up to whole groups
-  const int64_t blocks = whole_tiles               ? (tile_bound + 7) / 8 * 8 * bpt
-                         : (bpt == 16 || bpt == 8) ? (tile_bound + 1) / 2 * 2 * bpt
-                                                   : tile_bound * bpt;
+  const int64_t blocks = t.whole_tiles               ? (t.tile_bound + 7) / 8 * 8 * bpt
+                         : (bpt == 16 || bpt == 8) ? (t.tile_bound + 1) / 2 * 2 * bpt
+                                                   : t.tile_bound * bpt;
   gemm_tile_kernel<kW1, kMSub, kFrag, kWaves, kLdsScales>
       <<<static_cast<unsigned>(blocks), 64 * kWaves, lds, stream>>>(
-      act, act_bytes, gather, k_top, n_slots, wq, wsc, tiles, n_tiles, K, n_rows, half, wpt, bpt,
-      limit, clamp, out, ld_out, whole_tiles ? 1 : 0);
+      t.act, t.act_bytes, t.asc, t.asc_bytes, t.gather, t.k_top, t.n_slots, t.wq, t.wsc, t.tiles,
+      t.n_tiles, t.K, t.n_rows, t.half, wpt, bpt, t.limit, t.clamp, t.out, t.out_sc, t.ld_out,
+      t.whole_tiles ? 1 : 0);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_tile(bool w1, int tile_rows, int64_t tile_bound, hipStream_t stream,
-                       const uint16_t* act, uint32_t act_bytes, const int32_t* gather, int k_top,
-                       int n_slots, const uint8_t* wq, const uint8_t* wsc, const RowTile* tiles,
-                       const int32_t* n_tiles, int K, int n_rows, int half, float limit, int clamp,
-                       uint16_t* out, int ld_out, bool whole_tiles) {
-  // 128-row tiles (one workgroup per CU) stage the scales in LDS while they fit
-  // beside the activation buffers in the CU's 160 KB (K <= 4096)
+hipError_t launch_tile(bool w1, int tile_rows, const TileArgs& t, hipStream_t stream) {
+  // The E8M0 weight scales are staged in LDS while they fit beside the activation
+  // buffers: in the CU's 160 KB for 128-row tiles (one workgroup per CU), in half
+  // of it for 80-row tiles (two per CU); K <= 4096 either way.  Otherwise they come
+  // with the weights.
   if (tile_rows == 128) {
-    if (2 * static_cast<size_t>(a_buf_bytes<8>()) + tile_scale_lds_bytes(K, 8) <= kCuLds)
-      return w1 ? launch_tile_t<true, 8, 4, 8, true>(tile_bound, stream, act, act_bytes, gather,
-                                                     k_top, n_slots, wq, wsc, tiles, n_tiles, K,
-                                                     n_rows, half, limit, clamp, out, ld_out, false)
-                : launch_tile_t<false, 8, 4, 8, true>(tile_bound, stream, act, act_bytes, gather,
-                                                      k_top, n_slots, wq, wsc, tiles, n_tiles, K,
-                                                      n_rows, half, limit, clamp, out, ld_out, false);
-    return w1 ? launch_tile_t<true, 8, 4, 8, false>(tile_bound, stream, act, act_bytes, gather,
-                                                    k_top, n_slots, wq, wsc, tiles, n_tiles, K,
-                                                    n_rows, half, limit, clamp, out, ld_out, false)
-              : launch_tile_t<false, 8, 4, 8, false>(tile_bound, stream, act, act_bytes, gather,
-                                                     k_top, n_slots, wq, wsc, tiles, n_tiles, K,
-                                                     n_rows, half, limit, clamp, out, ld_out, false);
+    if (tile_lds_bytes(8, t.K, 8, true) <= kCuLds)
+      return w1 ? launch_tile_t<true, 8, 4, 8, true>(t, stream)
+                : launch_tile_t<false, 8, 4, 8, true>(t, stream);
+    return w1 ? launch_tile_t<true, 8, 4, 8, false>(t, stream)
+              : launch_tile_t<false, 8, 4, 8, false>(t, stream);
   }
-  // 80-row tiles keep two workgroups per CU: the E8M0 scales are staged in LDS
-  // while they fit beside the activation buffers in half the CU's LDS (K <= 4096
-  // for 256-element rows of scales per wavefront), else they come with the weights
-  if (2 * static_cast<size_t>(a_buf_bytes<5>()) + tile_scale_lds_bytes(K, 4) <= kTileLdsPerWorkgroup)
-    return w1 ? launch_tile_t<true, 5, 4, 4, true>(tile_bound, stream, act, act_bytes, gather,
-                                                   k_top, n_slots, wq, wsc, tiles, n_tiles, K,
-                                                   n_rows, half, limit, clamp, out, ld_out, whole_tiles)
-              : launch_tile_t<false, 5, 4, 4, true>(tile_bound, stream, act, act_bytes, gather,
-                                                    k_top, n_slots, wq, wsc, tiles, n_tiles, K,
-                                                    n_rows, half, limit, clamp, out, ld_out, whole_tiles);
-  return w1 ? launch_tile_t<true, 5, 4, 4, false>(tile_bound, stream, act, act_bytes, gather,
-                                                  k_top, n_slots, wq, wsc, tiles, n_tiles, K,
-                                                  n_rows, half, limit, clamp, out, ld_out, whole_tiles)
-            : launch_tile_t<false, 5, 4, 4, false>(tile_bound, stream, act, act_bytes, gather,
-                                                   k_top, n_slots, wq, wsc, tiles, n_tiles, K,
-                                                   n_rows, half, limit, clamp, out, ld_out, whole_tiles);
+  if (tile_lds_bytes(5, t.K, 4, true) <= kTileLdsPerWorkgroup)
+    return w1 ? launch_tile_t<true, 5, 4, 4, true>(t, stream)
+              : launch_tile_t<false, 5, 4, 4, true>(t, stream);
+  return w1 ? launch_tile_t<true, 5, 4, 4, false>(t, stream)
+            : launch_tile_t<false, 5, 4, 4, false>(t, stream);
 }
 
 }  // namespace moe

@@ -24,12 +24,14 @@ hipError_t launch_offsets(const uint32_t* bm, const int32_t* ids, int64_t T, int
                           void* ws, hipStream_t stream, const PlanOut* plan = nullptr,
                           bool* plan_written = nullptr);
 
+struct WsLayout;
+
+// The grouped FFN; `L` is the workspace layout for these sizes (validate.h).
 hipError_t launch_ffn(const uint16_t* x, int64_t T, int H, int I, int E, int k,
                       const uint8_t* w1, const uint8_t* w1s, const uint8_t* w2,
                       const uint8_t* w2s, const int32_t* counts, const int32_t* offsets,
                       const int32_t* gather, float limit, uint16_t* y_sorted, void* ws,
-                      size_t h_offset, size_t plan_offset, int64_t tile_bound,
-                      hipStream_t stream, hipEvent_t const* events = nullptr,
+                      const WsLayout& L, hipStream_t stream, hipEvent_t const* events = nullptr,
                       bool plan_ready = false);
 
 // Where the one-launch front-end also writes the FFN's row-tile plan (count, then
@@ -48,6 +50,11 @@ hipError_t launch_route_and_group(const float* logits, int64_t T, int E, int k, 
                                   float* weights, uint32_t* bm, int32_t* counts, int32_t* offsets,
                                   int32_t* gather, int32_t* scatter, void* ws, hipStream_t stream,
                                   const PlanOut* plan = nullptr, bool* plan_written = nullptr);
+
+// x [rows][K] bf16 -> two-part FP8 rows (xq: [rows][2K] bytes) and their E8M0 block
+// scales (xs: [rows][K/32] bytes), the input form of the tiled FFN kernels.
+hipError_t launch_act_split(const uint16_t* x, int64_t rows, int K, uint8_t* xq, uint8_t* xs,
+                            hipStream_t stream);
 
 // Streaming-read marker: kReadProbeBlocks workgroups, one sink word each.
 constexpr int kReadProbeBlocks = 2048;

@@ -44,7 +44,17 @@ moe_status workspace_layout(int64_t T, int32_t E, int32_t k, int32_t H, int32_t 
   L.offsets_bytes = align_up(static_cast<size_t>(L.n_blocks) * E * sizeof(int32_t), 256);
   L.tile_bound = ffn_tile_bound(slots, E, kFfnMinTileRows);
   L.ffn_h_offset = 0;
-  L.ffn_plan_offset = align_up(static_cast<size_t>(slots) * static_cast<size_t>(I) * 2, 256);
+  size_t end = align_up(static_cast<size_t>(slots) * static_cast<size_t>(I) * 2, 256);
+  L.ffn_hs_offset = L.ffn_xq_offset = L.ffn_xs_offset = end;
+  if (ffn_tiled(T, E, k)) {   // two-part FP8 activations: scales of h, then x and its scales
+    L.ffn_hs_offset = end;
+    end = align_up(end + static_cast<size_t>(slots) * static_cast<size_t>(I / 32), 256);
+    L.ffn_xq_offset = end;
+    end = align_up(end + static_cast<size_t>(T) * static_cast<size_t>(H) * 2, 256);
+    L.ffn_xs_offset = end;
+    end = align_up(end + static_cast<size_t>(T) * static_cast<size_t>(H / 32), 256);
+  }
+  L.ffn_plan_offset = end;
   L.ffn_bytes = L.ffn_plan_offset + align_up(256 + static_cast<size_t>(L.tile_bound) * sizeof(RowTile), 256);
   L.total = L.offsets_bytes > L.ffn_bytes ? L.offsets_bytes : L.ffn_bytes;
   *out = L;

@@ -10,7 +10,11 @@ namespace moe {
 
 struct WsLayout {
   size_t offsets_bytes;   // per-block expert counts for moe_expert_offsets
-  size_t ffn_h_offset;    // bf16 [T*k][I] intermediate activations
+  size_t ffn_h_offset;    // [T*k][I] intermediate activations: bf16, or two-part FP8 (2 bytes
+                          // per value) on the tiled path
+  size_t ffn_hs_offset;   // tiled path: [T*k][I/32] E8M0 scales of h
+  size_t ffn_xq_offset;   // tiled path: [T][2H] bytes, x in two-part FP8
+  size_t ffn_xs_offset;   // tiled path: [T][H/32] E8M0 scales of x
   size_t ffn_plan_offset; // row-tile count + RowTile list
   size_t ffn_bytes;
   size_t total;

@@ -103,14 +103,14 @@ def test_noalloc_entry_point_host_checks(lib):
     lib.moe_workspace_bytes.restype = ctypes.c_size_t
     fwd = lambda T, H, I, E, k, ptrs: lib.moe_forward_mxfp4_noalloc(
         *ptrs[:2], T, H, I, E, k, *ptrs[2:6], 10.0, *ptrs[6:15], None)
-    scratch = 64 << 20   # MOE_NOALLOC_SCRATCH_BYTES
+    scratch = 128 << 20   # MOE_NOALLOC_SCRATCH_BYTES
     fake = [4096] * 15   # aligned stand-in device pointers: never dereferenced by the checks
     assert fwd(16, 4096, 2048, 256, 6, [None] * 15) == INVALID
     assert fwd(16, 4096, 2048, 256, 9, fake) == UNSUPPORTED
     assert fwd(16, 4100, 2048, 256, 6, fake) == UNSUPPORTED
-    assert lib.moe_workspace_bytes(2729, 256, 6, 4096, 2048) <= scratch
-    assert lib.moe_workspace_bytes(2730, 256, 6, 4096, 2048) > scratch
-    assert fwd(2730, 4096, 2048, 256, 6, fake) == WS_SMALL
+    assert lib.moe_workspace_bytes(4032, 256, 6, 4096, 2048) <= scratch
+    assert lib.moe_workspace_bytes(4033, 256, 6, 4096, 2048) > scratch
+    assert fwd(4033, 4096, 2048, 256, 6, fake) == WS_SMALL
     assert fwd(8191, 4096, 2048, 256, 6, fake) == WS_SMALL
     header = open(HEADERS[0]).read()
-    assert re.search(r"#define MOE_NOALLOC_SCRATCH_BYTES \(\(size_t\)64 << 20\)", header)
+    assert re.search(r"#define MOE_NOALLOC_SCRATCH_BYTES \(\(size_t\)128 << 20\)", header)

@@ -3,8 +3,8 @@ moe_forward_mxfp4 (caller workspace), through the C ABI.
 
 Two calls in a row on the same GPU, the second with a smaller input, so the
 second call runs on scratch that still holds the first call's contents: the
-prefill-2048 workload (80-row tiled FFN, offsets kernels and scan; 50 MB of the
-64 MiB scratch), then the verify-1+7 step (one-launch front-end, streaming FFN).
+prefill-2048 workload (80-row tiled FFN, offsets kernels and scan; 68 MB of the
+128 MiB scratch), then the verify-1+7 step (one-launch front-end, streaming FFN).
 Every output of each call must equal the workspace entry point's, bit for bit
 (the same kernels run on the same inputs; routing is also checked against the
 oracle).
@@ -74,7 +74,7 @@ def test_noalloc_rejects_sizes_beyond_the_scratch():
         pytest.skip("no GPU")
     from mxfp4_routed_expert_route_amd import binding, layer
     binding.load()
-    T, E, k, H, I = 2730, 256, 6, 4096, 2048   # 64 MiB + 4 KiB of workspace
+    T, E, k, H, I = 4033, 256, 6, 4096, 2048   # just over 128 MiB of workspace
     assert binding.moe_workspace_bytes(T, E, k, H, I) > binding.NOALLOC_SCRATCH_BYTES
     small = inputs.make_inputs(0)
     logits = torch.zeros((T, E), dtype=torch.float32, device="cuda")
