@@ -122,17 +122,18 @@ def measured_traffic(profile_name: str):
 
 def ffn_kernel_name(T: int, E: int, k: int, H: int) -> str:
     """The W1 kernel the library picks for these sizes (its row-tile rule; the
-    80-row kernel stages E8M0 scales in LDS while they fit beside the activations
-    in 80 KB, the 128-row kernel while they fit in the CU's 160 KB)."""
+    80-row kernel stages E8M0 weight scales in LDS while they fit beside the
+    activations in 80 KB, the 128-row kernel weight and activation scales while
+    they fit in the CU's 160 KB)."""
     if T <= 16 or T * k // E <= 8:
         return "gemm_stream_kernel<true, 1, true, 2>"
     if T * k // E <= 24:
         return "gemm_stream_kernel<true, 2, true, 4>"
     if T * k // E < 96:
         lds_scales = 2 * 80 * 256 + 2 * 256 * 4 + 4 * (H // 128) * 64 * 4 <= 80 * 1024
-        return f"gemm_tile_kernel<true, 5, 4, 4, {'true' if lds_scales else 'false'}>"
-    lds_scales = 2 * 128 * 256 + 2 * 512 * 4 + 8 * (H // 128) * 64 * 4 <= 160 * 1024
-    return f"gemm_tile_kernel<true, 8, 4, 8, {'true' if lds_scales else 'false'}>"
+        return f"gemm_tile_kernel<true, 5, 4, 4, {'true' if lds_scales else 'false'}, false>"
+    tiled = H % 2048 == 0 and 2 * 128 * 256 + 128 * (H // 128 + 1) * 4 + 8 * (H // 128) * 64 * 4 <= 160 * 1024
+    return f"gemm_tile_kernel<true, 8, 4, 8, {'true, true' if tiled else 'false, false'}>"
 
 
 def blas_threads() -> int:

@@ -91,13 +91,13 @@ constexpr size_t kTileLdsPerWorkgroup = 80 * 1024;   // two workgroups per CU
 constexpr size_t kCuLds = 160 * 1024;                 // one workgroup per CU
 // LDS of a workgroup: two activation buffers, a scale dword per thread for each
 // (the rows' block scales), and the staged weight scales (when they are staged)
-inline size_t tile_lds_bytes(int msub, int K, int waves, bool lds_scales) {
+inline size_t tile_lds_bytes(int msub, int K, int waves, bool lds_scales, bool tile_ascales) {
   const size_t rows = static_cast<size_t>(msub) * 16;
-  return 2 * rows * kAPieces * 16 + 2 * static_cast<size_t>(64 * waves) * 4 +
-         (lds_scales ? tile_scale_lds_bytes(K, waves) : 0);
+  const size_t ascales = tile_ascales ? rows * (K / 128 + 1) * 4 : 2 * static_cast<size_t>(64 * waves) * 4;
+  return 2 * rows * kAPieces * 16 + ascales + (lds_scales ? tile_scale_lds_bytes(K, waves) : 0);
 }
 
-template <bool kW1, int kMSub, int kFrag, int kWaves, bool kLdsScales>
+template <bool kW1, int kMSub, int kFrag, int kWaves, bool kLdsScales, bool kTileAScales>
 __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
     const uint8_t* __restrict__ act, uint32_t act_bytes, const uint8_t* __restrict__ asc,
     uint32_t asc_bytes, const int32_t* __restrict__ gather, int k_top, int n_slots,
@@ -176,9 +176,13 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
     }
     aoff[i] = valid ? row * static_cast<uint32_t>(K) * 2u + 16u * aq : kRsrcOutOfRange;
   }
-  uint32_t soff = kRsrcOutOfRange;   // byte offset of tile row tid's chunk-0 scale dword
-  if (tid < kRows) {
-    const int p = rt.p_begin + tid;
+  // Activation block scales: with kTileAScales every thread stages K/512 dwords of
+  // tile row tid / 4 (all of K) once, before the K loop; otherwise thread tid < kRows
+  // stages the scale dword of tile row tid with each chunk
+  const int srow_t = kTileAScales ? tid / 4 : tid;
+  uint32_t soff = kRsrcOutOfRange;   // byte offset of tile row srow_t's scales
+  if (srow_t < kRows) {
+    const int p = rt.p_begin + srow_t;
     if (p < rt.p_end) {
       if (kW1) {
         const int slot = gather[p];
@@ -190,7 +194,9 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
     }
   }
   unsigned char* a_lds = tile_lds;                       // [2][kAPieces][kRows][16 B]
-  uint32_t* a_scl = reinterpret_cast<uint32_t*>(tile_lds + 2 * kABuf);   // [2][kThreads]
+  // [2][kThreads] dwords, or with kTileAScales [kRows][a_scl_stride] for all of K
+  uint32_t* a_scl = reinterpret_cast<uint32_t*>(tile_lds + 2 * kABuf);
+  const int a_scl_stride = K / 128 + 1;   // dwords per row: odd, so 16 rows hit 16 banks
   const int a_store = (aq * kRows + (ar ^ (4 * (aq & 1)))) * 16;
   // np: the pieces that hold rows of the subtiles a tile runs (a constant at each
   // call site); pieces past them are neither loaded nor stored
@@ -204,15 +210,28 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
       if (i < np)
         ra[i] = __builtin_bit_cast(
             uint4, __builtin_amdgcn_raw_buffer_load_b128(arsrc, aoff[i] + kc * 256, 0, 0));
-    rs = __builtin_amdgcn_raw_buffer_load_b32(srsrc, soff + kc * 4, 0, 0);
+    if constexpr (!kTileAScales) rs = __builtin_amdgcn_raw_buffer_load_b32(srsrc, soff + kc * 4, 0, 0);
   };
   auto store_a = [&](const uint4 (&ra)[kPieces], uint32_t rs, int buf, int np) {
 #pragma unroll
     for (int i = 0; i < kPieces; ++i)
       if (i < np)
         *reinterpret_cast<uint4*>(a_lds + buf * kABuf + a_store + kRowStride * i * 16) = ra[i];
-    a_scl[buf * kThreads + tid] = rs;
+    if constexpr (!kTileAScales) a_scl[buf * kThreads + tid] = rs;
   };
+  if constexpr (kTileAScales) {
+    // K/128 dwords per row, four threads per row, K/512 consecutive dwords each
+    // (the host takes this path for K a multiple of 2048: whole 16-byte groups)
+    const int n_dw = K / 512, d0 = (tid & 3) * n_dw;
+    for (int j = 0; j < n_dw; j += 4) {
+      const uint4 v = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(srsrc, soff + 4 * (d0 + j), 0, 0));
+      if (srow_t < kRows) {
+        uint32_t* d = a_scl + srow_t * a_scl_stride + d0 + j;
+        d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+      }
+    }
+  }
 
   // --- weights: kFrag fragments of 16 rows, this lane's row in each
   // The weights are the MFMA's A operand and the activations its B operand, so a
@@ -258,7 +277,9 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
   // --- 80-row tiles: scales of the wavefront's 64 weight rows, staged as
   // [chunk][16][4] dwords
   uint32_t* my_scales =
-      reinterpret_cast<uint32_t*>(tile_lds + 2 * kABuf + 2 * kThreads * 4) + wave * (n_chunks * 64);
+      reinterpret_cast<uint32_t*>(tile_lds + 2 * kABuf +
+                                  (kTileAScales ? kRows * (K / 128 + 1) : 2 * kThreads) * 4) +
+      wave * (n_chunks * 64);
   if constexpr (kLdsScales) {
     const int f = lane >> 4;
     const uint8_t* srow = wsc + (e_rows + wrow(f, r16)) * row_s;
@@ -317,7 +338,8 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
                   static_cast<int>(q[f].w), 0, 0, 0, 0};
     }
     const unsigned char* abase = a_lds + buf * kABuf;
-    const uint32_t* ascl = a_scl + buf * kThreads;
+    const uint32_t* ascl = kTileAScales ? a_scl + kc : a_scl + buf * kThreads;
+    const int ascl_row = kTileAScales ? a_scl_stride : 1;
     // every subtile up to NS, also those past the tile's rows (they hold zeros)
 #pragma unroll
     for (int mi = 0; mi < NS; ++mi) {
@@ -327,7 +349,7 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
       const uint4 h1 = *reinterpret_cast<const uint4*>(abase + ((2 * g + 1) * kRows + (row ^ 4)) * 16);
       const uint4 l0 = *reinterpret_cast<const uint4*>(abase + ((8 + 2 * g) * kRows + row) * 16);
       const uint4 l1 = *reinterpret_cast<const uint4*>(abase + ((9 + 2 * g) * kRows + (row ^ 4)) * 16);
-      const int asc_g = static_cast<int>(ascl[row] >> (8 * g));
+      const int asc_g = static_cast<int>(ascl[row * ascl_row] >> (8 * g));
       const v8i ah = v8i{static_cast<int>(h0.x), static_cast<int>(h0.y), static_cast<int>(h0.z),
                          static_cast<int>(h0.w), static_cast<int>(h1.x), static_cast<int>(h1.y),
                          static_cast<int>(h1.z), static_cast<int>(h1.w)};
@@ -487,19 +509,19 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
   }
 }
 
-template <bool kW1, int kMSub, int kFrag, int kWaves, bool kLdsScales>
+template <bool kW1, int kMSub, int kFrag, int kWaves, bool kLdsScales, bool kTileAScales>
 hipError_t launch_tile_t(const TileArgs& t, hipStream_t stream) {
   // wavefronts per row tile: W1 pairs `half` gate rows with as many up rows, 16 *
   // kFrag/2 of each per wavefront; W2 covers n_rows output rows, 16 * kFrag each
   const int wpt = kW1 ? t.half / (8 * kFrag) : t.n_rows / (16 * kFrag);
   const int bpt = (wpt + kWaves - 1) / kWaves;
-  size_t lds = tile_lds_bytes(kMSub, t.K, kWaves, kLdsScales);
+  size_t lds = tile_lds_bytes(kMSub, t.K, kWaves, kLdsScales, kTileAScales);
   // whole tiles per XCD cover row tiles in groups of 8, the column-block/XCD split
   // in pairs: round up to whole groups
   const int64_t blocks = t.whole_tiles               ? (t.tile_bound + 7) / 8 * 8 * bpt
                          : (bpt == 16 || bpt == 8) ? (t.tile_bound + 1) / 2 * 2 * bpt
                                                    : t.tile_bound * bpt;
-  gemm_tile_kernel<kW1, kMSub, kFrag, kWaves, kLdsScales>
+  gemm_tile_kernel<kW1, kMSub, kFrag, kWaves, kLdsScales, kTileAScales>
       <<<static_cast<unsigned>(blocks), 64 * kWaves, lds, stream>>>(
       t.act, t.act_bytes, t.asc, t.asc_bytes, t.gather, t.k_top, t.n_slots, t.wq, t.wsc, t.tiles,
       t.n_tiles, t.K, t.n_rows, t.half, wpt, bpt, t.limit, t.clamp, t.out, t.out_sc, t.ld_out,
@@ -513,19 +535,21 @@ hipError_t launch_tile(bool w1, int tile_rows, const TileArgs& t, hipStream_t st
   // The E8M0 weight scales are staged in LDS while they fit beside the activation
   // buffers: in the CU's 160 KB for 128-row tiles (one workgroup per CU), in half
   // of it for 80-row tiles (two per CU); K <= 4096 either way.  Otherwise they come
-  // with the weights.
+  // with the weights.  128-row tiles also stage the activations' block scales for
+  // all of K when those fit too (K a multiple of 2048 up to 4096: each thread
+  // stages whole 16-byte groups); 80-row tiles stage them per chunk.
   if (tile_rows == 128) {
-    if (tile_lds_bytes(8, t.K, 8, true) <= kCuLds)
-      return w1 ? launch_tile_t<true, 8, 4, 8, true>(t, stream)
-                : launch_tile_t<false, 8, 4, 8, true>(t, stream);
-    return w1 ? launch_tile_t<true, 8, 4, 8, false>(t, stream)
-              : launch_tile_t<false, 8, 4, 8, false>(t, stream);
+    if (t.K % 2048 == 0 && tile_lds_bytes(8, t.K, 8, true, true) <= kCuLds)
+      return w1 ? launch_tile_t<true, 8, 4, 8, true, true>(t, stream)
+                : launch_tile_t<false, 8, 4, 8, true, true>(t, stream);
+    return w1 ? launch_tile_t<true, 8, 4, 8, false, false>(t, stream)
+              : launch_tile_t<false, 8, 4, 8, false, false>(t, stream);
   }
-  if (tile_lds_bytes(5, t.K, 4, true) <= kTileLdsPerWorkgroup)
-    return w1 ? launch_tile_t<true, 5, 4, 4, true>(t, stream)
-              : launch_tile_t<false, 5, 4, 4, true>(t, stream);
-  return w1 ? launch_tile_t<true, 5, 4, 4, false>(t, stream)
-            : launch_tile_t<false, 5, 4, 4, false>(t, stream);
+  if (tile_lds_bytes(5, t.K, 4, true, false) <= kTileLdsPerWorkgroup)
+    return w1 ? launch_tile_t<true, 5, 4, 4, true, false>(t, stream)
+              : launch_tile_t<false, 5, 4, 4, true, false>(t, stream);
+  return w1 ? launch_tile_t<true, 5, 4, 4, false, false>(t, stream)
+            : launch_tile_t<false, 5, 4, 4, false, false>(t, stream);
 }
 
 }  // namespace moe
