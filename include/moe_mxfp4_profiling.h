@@ -15,7 +15,8 @@
  *
  * moe_read_probe is the "achievable read bandwidth" marker measured beside the
  * FFN kernels: a plain streaming read of `bytes` bytes of device memory at `buf`
- * (16-byte loads, four in flight per lane, grid-stride), enqueued on `stream`.
+ * (8192 workgroups, each reading one contiguous slab with non-temporal 16-byte
+ * loads, eight in flight per lane), enqueued on `stream`.
  * Workgroup b writes the XOR of the 32-bit words it read to sink[b], so the XOR
  * of all MOE_READ_PROBE_SINK_WORDS sink words is the XOR of every 32-bit word of
  * the buffer (a check that every byte was read).  `buf` and `sink` are device
@@ -33,7 +34,7 @@
 extern "C" {
 #endif
 
-#define MOE_READ_PROBE_SINK_WORDS 2048
+#define MOE_READ_PROBE_SINK_WORDS 8192
 
 moe_status moe_grouped_ffn_mxfp4_timed(const uint16_t* x, int64_t T, int32_t H, int32_t I,
                                        int32_t E, int32_t k, const uint8_t* w1,

@@ -207,7 +207,7 @@ def moe_forward_mxfp4_noalloc(logits, x, k: int, w1, w1_scale, w2, w2_scale,
         _ptr(y, BF16, "y"), _stream(stream)))
 
 
-READ_PROBE_SINK_WORDS = 2048
+READ_PROBE_SINK_WORDS = 8192
 
 
 def moe_read_probe(buf, sink, stream=None):

@@ -57,7 +57,7 @@ hipError_t launch_act_split(const uint16_t* x, int64_t rows, int K, uint8_t* xq,
                             hipStream_t stream);
 
 // Streaming-read marker: kReadProbeBlocks workgroups, one sink word each.
-constexpr int kReadProbeBlocks = 2048;
+constexpr int kReadProbeBlocks = 8192;
 hipError_t launch_read_probe(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
 
 hipError_t launch_combine(const uint16_t* ys, const float* w, const int32_t* scatter, int64_t T,

@@ -1,8 +1,9 @@
 """moe_read_probe (the streaming-read marker of the bench) reads every byte.
 
 The XOR of the per-workgroup sink words must equal the XOR of all 32-bit words
-of the buffer, computed on the host; sizes cover a buffer smaller than one pass
-of the grid, a ragged tail past the unrolled loop, and a large buffer.
+of the buffer, computed on the host; sizes cover a buffer smaller than the grid
+(most workgroups read nothing), slabs that end inside the unrolled loop's last
+step, and a large buffer.
 """
 from __future__ import annotations
 
@@ -16,7 +17,7 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("n_bytes", [16, 4096 * 16 + 48, 64 << 20])
+@pytest.mark.parametrize("n_bytes", [16, 8192 * 16 * 37 + 48, 64 << 20])
 def test_read_probe_reads_every_word(n_bytes):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
