@@ -347,7 +347,9 @@ class Runner:
         touched = int((counts > 0).sum())
         w1_pe = 2 * I * H // 2 + 2 * I * H // 32          # W1 codes + E8M0 scales per expert
         w2_pe = H * I // 2 + H * I // 32
-        w1_alg = touched * w1_pe + T * H * 2               # + activations read once
+        # + x read once, h written once (2 bytes per element; the tiled kernels' two-part
+        # FP8 form adds one scale byte per 32 elements, not counted)
+        w1_alg = touched * w1_pe + T * H * 2 + T * k * I * 2
         layer_alg = touched * (w1_pe + w2_pe) + 2 * T * H * 2 + T * E * 4
         ms_per_step = elapsed * 1e3 / args.steps
         w1_flops = 2.0 * T * k * 2 * I * H
