@@ -340,32 +340,60 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
     const unsigned char* abase = a_lds + buf * kABuf;
     const uint32_t* ascl = kTileAScales ? a_scl + kc : a_scl + buf * kThreads;
     const int ascl_row = kTileAScales ? a_scl_stride : 1;
-    // every subtile up to NS, also those past the tile's rows (they hold zeros)
-#pragma unroll
-    for (int mi = 0; mi < NS; ++mi) {
+    // one subtile's operands: hi pieces 2g, 2g+1 (bytes 32g .. 32g+31 of the chunk's
+    // hi half), lo pieces 8 further, and the block scale of row 16 mi + r16
+    auto read_sub = [&](int mi, v8i& ah, v8i& al, int& asc_g) {
       const int row = 16 * mi + r16;
-      // hi: pieces 2g, 2g+1 (bytes 32g .. 32g+31 of the chunk's hi half); lo: 8 further
       const uint4 h0 = *reinterpret_cast<const uint4*>(abase + ((2 * g) * kRows + row) * 16);
       const uint4 h1 = *reinterpret_cast<const uint4*>(abase + ((2 * g + 1) * kRows + (row ^ 4)) * 16);
       const uint4 l0 = *reinterpret_cast<const uint4*>(abase + ((8 + 2 * g) * kRows + row) * 16);
       const uint4 l1 = *reinterpret_cast<const uint4*>(abase + ((9 + 2 * g) * kRows + (row ^ 4)) * 16);
-      const int asc_g = static_cast<int>(ascl[row * ascl_row] >> (8 * g));
-      const v8i ah = v8i{static_cast<int>(h0.x), static_cast<int>(h0.y), static_cast<int>(h0.z),
-                         static_cast<int>(h0.w), static_cast<int>(h1.x), static_cast<int>(h1.y),
-                         static_cast<int>(h1.z), static_cast<int>(h1.w)};
-      const v8i al = v8i{static_cast<int>(l0.x), static_cast<int>(l0.y), static_cast<int>(l0.z),
-                         static_cast<int>(l0.w), static_cast<int>(l1.x), static_cast<int>(l1.y),
-                         static_cast<int>(l1.z), static_cast<int>(l1.w)};
+      asc_g = static_cast<int>(ascl[row * ascl_row] >> (8 * g));
+      ah = v8i{static_cast<int>(h0.x), static_cast<int>(h0.y), static_cast<int>(h0.z),
+               static_cast<int>(h0.w), static_cast<int>(h1.x), static_cast<int>(h1.y),
+               static_cast<int>(h1.z), static_cast<int>(h1.w)};
+      al = v8i{static_cast<int>(l0.x), static_cast<int>(l0.y), static_cast<int>(l0.z),
+               static_cast<int>(l0.w), static_cast<int>(l1.x), static_cast<int>(l1.y),
+               static_cast<int>(l1.z), static_cast<int>(l1.w)};
+    };
+    // Every subtile up to NS, also those past the tile's rows (they hold zeros).
+    // The next subtile's operands are read into the other register set before this
+    // subtile's MFMAs, so the LDS reads are in flight while they run and never write
+    // registers an issued MFMA still reads (which costs wait states); the hi MFMAs
+    // of all fragments go before the lo ones, so no MFMA waits on the one before it.
+    // (Not in the 128-row kernel that loads the weight scales with the weights:
+    // there the second register set does not fit beside its other registers.)
+    constexpr bool kTwoSets = !(kMSub == 8 && !kLdsScales);
+    v8i ah0, al0, ah1, al1;
+    int as0 = 0, as1 = 0;
+    read_sub(0, ah0, al0, as0);
 #pragma unroll
-      for (int f = 0; f < kFrag; ++f) {
-        // formats: A (weights) FP4 E2M1 = 4, B (activations) FP8 E4M3 = 0
+    for (int mi = 0; mi < NS; ++mi) {
+      if constexpr (kTwoSets) {
+        if (mi + 1 < NS) {
+          if (mi & 1)
+            read_sub(mi + 1, ah0, al0, as0);
+          else
+            read_sub(mi + 1, ah1, al1, as1);
+        }
+      } else if (mi > 0) {
+        read_sub(mi, ah0, al0, as0);
+      }
+      const bool second = kTwoSets && (mi & 1);
+      const v8i ah = second ? ah1 : ah0;
+      const v8i al = second ? al1 : al0;
+      const int asc_g = second ? as1 : as0;
+      // formats: A (weights) FP4 E2M1 = 4, B (activations) FP8 E4M3 = 0
+#pragma unroll
+      for (int f = 0; f < kFrag; ++f)
         acc[mi][f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wb[f], ah, acc[mi][f], 4, 0, 0,
                                                                        wsc_g[f], 0, asc_g);
+#pragma unroll
+      for (int f = 0; f < kFrag; ++f)
         acc[mi][f] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wb[f], al, acc[mi][f], 4, 0, 0,
                                                                        wsc_g[f], 0, asc_g);
-      }
-      // one subtile's operands live at a time (the compiler would otherwise hoist
-      // every subtile's LDS reads next to the 128 accumulators and spill)
+      // at most two subtiles' operands live at a time (the compiler would otherwise
+      // hoist every subtile's LDS reads next to the 128 accumulators and spill)
       __builtin_amdgcn_sched_barrier(0);
     }
   };
