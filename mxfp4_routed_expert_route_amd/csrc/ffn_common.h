@@ -5,16 +5,18 @@
 // clamp (txtmix.com article, §9): gate capped at +limit, up clamped to
 // [-limit, +limit], both before the SwiGLU product.
 //
-// Every GEMM wavefront owns weight rows of one row tile's expert as 16-column MFMA
-// fragments -- four (64 rows) in the tiled kernel and the 32-row streaming tiles,
+// Every GEMM wavefront owns weight rows of one row tile's expert as 16-row MFMA
+// fragments -- four (64 rows) in the tiled kernels and the 32-row streaming tiles,
 // two (32 rows) in the 16-row streaming tiles; for W1 half of them gate rows and
-// half the matching up rows, so each SwiGLU pair meets in one lane.  Codes are
-// dequantised in registers with the gfx950 scaled FP4->BF16 convert (scale passed
-// as an fp32 whose exponent field is the E8M0 byte; 0xFF maps to a NaN scale) and
-// fed to v_mfma_f32_16x16x32_bf16 as the B operand; activations are the A
-// operand.  Within one MFMA the K order of the 32 products does not matter as long
-// as A and B agree, which frees the lane-to-K assignment for memory efficiency.
-// fp32 accumulation throughout.
+// half the matching up rows, so each SwiGLU pair meets in one lane.  Streaming
+// kernels (decode shapes) dequantise the codes in registers with the gfx950 scaled
+// FP4->BF16 convert (scale passed as an fp32 whose exponent field is the E8M0 byte;
+// 0xFF maps to a NaN scale) and feed them to v_mfma_f32_16x16x32_bf16 as the B
+// operand, activations being the A operand; within one MFMA the K order of the 32
+// products does not matter as long as A and B agree, which frees the lane-to-K
+// assignment for memory efficiency.  Tiled kernels (prefill shapes) feed codes and
+// scales as stored to the block-scaled FP4 x FP8 MFMA (ffn_tile.hip) with the
+// activations in the two-part FP8 form below.  fp32 accumulation throughout.
 #pragma once
 #include "config.h"
 #include "device.h"
