@@ -36,6 +36,7 @@ import gc
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -91,12 +92,23 @@ class HipEvents:
         return f.value
 
 
+def _code_only(text: str) -> str:
+    """C/C++ source with comments removed and whitespace runs collapsed, so that a
+    comment edit does not read as a kernel change (string literals are not
+    special-cased: the kernel sources hold none with comment markers)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def sources_digest(paths) -> str:
-    """sha256 over the named source files, in the order given."""
+    """sha256 over the code (comments and whitespace dropped) of the named source
+    files, in the order given."""
     h = hashlib.sha256()
     for p in paths:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
+        h.update(b"\0")
     return h.hexdigest()
 
 

@@ -50,6 +50,17 @@ def test_traffic_dropped_when_a_source_changes(tmp_path, monkeypatch, change):
     assert bench.measured_traffic(name) is None
 
 
+def test_traffic_kept_across_comment_edits_only(tmp_path, monkeypatch):
+    (tmp_path / "a.hip").write_text("int f(int x) { return x + 1; }  // add one\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    digest = bench.sources_digest(["a.hip"])
+    name = _profile(tmp_path, monkeypatch, ["a.hip"], digest[:16])
+    (tmp_path / "a.hip").write_text("/* increment */\nint f(int x) {\n  return x + 1;   // one more\n}\n")
+    assert bench.measured_traffic(name) == 123456
+    (tmp_path / "a.hip").write_text("int f(int x) { return x + 2; }  // add one\n")
+    assert bench.measured_traffic(name) is None
+
+
 def test_traffic_missing_profile_is_none(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     assert bench.measured_traffic("absent.md") is None
