@@ -132,11 +132,13 @@ def measured_traffic(profile_name: str):
         return None
 
 
-def ffn_kernel_name(T: int, E: int, k: int, H: int) -> str:
+def ffn_kernel_name(T: int, E: int, k: int, H: int, I: int) -> str:
     """The W1 kernel the library picks for these sizes (its row-tile rule; the
     80-row kernel stages E8M0 weight scales in LDS while they fit beside the
     activations in 80 KB, the 128-row kernel weight and activation scales while
     they fit in the CU's 160 KB)."""
+    if T * k < E and H in (2048, 4096) and I in (2048, 4096):
+        return f"gemv_kernel<true, {H // 2048}>"
     if T <= 16 or T * k // E <= 8:
         return "gemm_stream_kernel<true, 1, true, 2>"
     if T * k // E <= 24:
@@ -368,7 +370,7 @@ class Runner:
         layer_flops = 2.0 * T * k * 3 * H * I
         hbm_gbs = w1_alg / (w1_ms * 1e-3) / 1e9
         tflops = w1_flops / (w1_ms * 1e-3) / 1e12
-        kname = "W1 gate|up + clamped SwiGLU (" + ffn_kernel_name(T, E, k, H) + ")"
+        kname = "W1 gate|up + clamped SwiGLU (" + ffn_kernel_name(T, E, k, H, I) + ")"
         traffic = measured_traffic(PROFILES[wl.index]) if wl.index in PROFILES else None
         # The W1 kernel's bound: its FLOPs per algorithmic byte against the ratio of
         # the two peaks (bf16 ridge: 312.5 FLOP/B).  Decode and the 48-row prefill

@@ -49,7 +49,7 @@ moe_status forward_layer(const float* logits, const uint16_t* x, int64_t T, int3
   if (s != MOE_OK) return s;
   // the routing side writes the FFN's row-tile plan: the one-launch front-end
   // (T <= 64), else the expert-offsets kernel (T <= 512) or its scan step
-  const int tile_rows = ffn_tile_rows(T, E, k);
+  const int tile_rows = ffn_tile_rows(T, E, k, H, I);
   char* wsb = static_cast<char*>(ws);
   const PlanOut plan{tile_rows, ffn_tile_bound(T * k, E, tile_rows),
                      reinterpret_cast<int32_t*>(wsb + L.ffn_plan_offset),

@@ -2,11 +2,12 @@
 // W1 (gate|up with the clamped SwiGLU epilogue) and W2.
 //
 // A plan kernel cuts each expert's rows [offsets[e], offsets[e+1]) into row tiles
-// (16, 32, 80 or 128 rows, chosen from T and the mean rows per expert); only experts
-// with rows get tiles.  Few rows per expert (decode shapes): the streaming kernel
-// (ffn_stream.hip), one independent wavefront per (tile, 64 weight rows), bound
-// by HBM.  Many rows: the tiled kernel (ffn_tile.hip), four wavefronts sharing an
-// LDS activation tile.
+// (1, 16, 32, 80 or 128 rows, chosen from T, the mean rows per expert and the
+// dims); only experts with rows get tiles.  Fewer rows than experts (decode,
+// verify): the GEMV kernel (ffn_gemv.hip), weights streamed past one row per
+// tile on the vector ALUs.  Few rows per expert: the streaming kernel (ffn_stream.hip),
+// bf16 MFMAs, bound by HBM.  Many rows: the tiled kernels (ffn_tile.hip),
+// block-scaled FP4 x FP8 MFMAs on an LDS activation tile.
 #include "ffn_common.h"
 #include "launch.h"
 #include "plan.h"
@@ -56,7 +57,7 @@ hipError_t launch_ffn(const uint16_t* x, int64_t T, int H, int I, int E, int k,
   // Few rows per expert -> weight streaming with 16- or 32-row tiles; else 80- or 128-row
   // tiles (ffn_tile_rows).  The plan may already be in the workspace (written by
   // the one-launch front-end of moe_forward_mxfp4 under the same rule).
-  const int tile_rows = ffn_tile_rows(T, E, k);
+  const int tile_rows = ffn_tile_rows(T, E, k, H, I);
   const int64_t tile_bound = ffn_tile_bound(n_slots, E, tile_rows);
 
   hipError_t err = hipSuccess;
@@ -77,7 +78,18 @@ hipError_t launch_ffn(const uint16_t* x, int64_t T, int H, int I, int E, int k,
     if (err != hipSuccess) return err;
   }
 
-  if (tile_rows <= 32) {
+  if (tile_rows == kFfnGemvTileRows) {
+    // decode GEMV: W1 4 gate rows (and their up rows) per wavefront, W2 8 rows
+    err = launch_gemv(true, tile_bound, stream, x, gather, k, slots_i, w1, w1s, tiles, n_tiles, H,
+                      2 * I, I, limit, clamp_i, h, I);
+    if (err != hipSuccess) return err;
+    if (events) {
+      err = hipEventRecord(events[1], stream);
+      if (err != hipSuccess) return err;
+    }
+    err = launch_gemv(false, tile_bound, stream, h, nullptr, k, slots_i, w2, w2s, tiles, n_tiles,
+                      I, H, 0, limit, 0, y_sorted, H);
+  } else if (tile_rows <= 32) {
     // W1: 8 * frags gate rows (and as many up rows) per wavefront; W2: 16 * frags rows
     const int frags = stream_frags(tile_rows / 16);
     const int wpt1 = I / (8 * frags), wpt2 = H / (16 * frags);

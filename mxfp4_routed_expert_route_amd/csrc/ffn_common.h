@@ -141,5 +141,11 @@ struct TileArgs {
 };
 // tile_rows: 80 (80 x 256 workgroups) or 128 (128 x 512 workgroups)
 hipError_t launch_tile(bool w1, int tile_rows, const TileArgs& args, hipStream_t stream);
+// Decode GEMV (1-row tiles, K = 2048 or 4096, ffn_gemv_dims): act as for
+// launch_stream (bf16 rows; W1 gathered through `gather`), out bf16 [n_slots][ld_out].
+hipError_t launch_gemv(bool w1, int64_t tile_bound, hipStream_t stream, const uint16_t* act,
+                       const int32_t* gather, int k_top, int n_slots, const uint8_t* wq,
+                       const uint8_t* wsc, const RowTile* tiles, const int32_t* n_tiles, int K,
+                       int n_rows, int half, float limit, int clamp, uint16_t* out, int ld_out);
 
 }  // namespace moe

@@ -1,0 +1,271 @@
+// Weight-streaming GEMV for decode batches: one-row tiles.
+//
+// With fewer rows than experts (T * k < E: a decode or speculative-verify step)
+// an expert holds one row, sometimes two, and the FFN is a stream of the touched
+// experts' weights past their few activation rows (txtmix.com article, §8:
+// decode speed is bandwidth over the bytes read per token).  The matrix cores
+// would idle on 16-row tiles that hold one real row, so this kernel multiplies on
+// the vector ALUs and spends its effort on the read pattern instead: every load
+// instruction of a wavefront reads 1 KB of one weight row, contiguous (lane l:
+// bytes 16l .. 16l+15, i.e. K elements 32l .. 32l+31 of a 2048-element slice),
+// non-temporal, and a wavefront's weight rows are consecutive, so it reads 8 KB
+// runs.  A read-only probe of this pattern streams the verify step's W1 (46
+// experts x 4096 rows x 2 KB) at 6.6 TB/s against 5.6-5.7 TB/s for the
+// 16-rows-by-64-bytes pattern of the MFMA kernels.
+//
+// A wavefront streams groups of 8 weight rows of one row tile's expert (W1: 4 gate
+// rows and the matching 4 up rows; W2: 8 output rows), all of K for each, K 2048 or
+// 4096.  Per 1 KB slice of a row: the lane's 32 E2M1 codes are converted to bf16
+// with their E8M0 scale (the gfx950 scaled convert; exact) and multiplied by the
+// lane's 32 activations with two-element dot products into fp32.  Each group's 8
+// sums are reduced over the 64 lanes with lane exchanges, and W1 applies the
+// clamped SwiGLU.  A tile is one row: an expert with several rows gets several
+// tiles, whose wavefronts read its weights at about the same time (the second read
+// mostly from cache); one activation row keeps the registers for two groups of
+// weights in flight.  No LDS, no workgroup barrier: every wavefront runs on its
+// own.
+#include <type_traits>
+
+#include "ffn_common.h"
+
+namespace moe {
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kGemvRows = 8;         // weight rows per wavefront
+constexpr int kGemvSlice = 2048;     // K elements per 1 KB row slice (64 lanes x 32)
+constexpr int kGemvMaxWaves = 2048;  // wavefronts per launch: two per SIMD
+
+__device__ __forceinline__ uint4 load_nt(const uint8_t* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Lane exchanges of the final reduction: x of lane ^ 16 (a swizzle within 32
+// lanes), of lane ^ 8 (DPP row_ror:8), of lane ^ 7 within 8 lanes (row_half_mirror),
+// of lane ^ 2 and lane ^ 1 (quad permutations); lane mappings checked on the GPU.
+__device__ __forceinline__ float swz_xor16(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x),
+                                                               0x401F));
+}
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), kCtrl,
+                                                            0xF, 0xF, false));
+}
+constexpr int kDppXor8 = 0x128, kDppMirror8 = 0x141, kDppXor2 = 0x4E, kDppXor1 = 0xB1;
+
+// 32 E2M1 codes (16 bytes, element 2m in the low nibble of byte m) with E8M0 scale
+// `scale` -> 16 bf16 pairs, pair m = elements 2m, 2m+1
+__device__ __forceinline__ void dequant32(const uint4 q, float scale, bf16x2 (&w)[16]) {
+  const uint32_t d[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    w[4 * i + 0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[i], scale, 0);
+    w[4 * i + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[i], scale, 1);
+    w[4 * i + 2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[i], scale, 2);
+    w[4 * i + 3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[i], scale, 3);
+  }
+}
+
+// acc + sum over the 32 elements of w * a (a: 32 bf16 as 4 x 16 bytes, pair m in
+// dword m), fp32
+__device__ __forceinline__ float dot32(const bf16x2 (&w)[16], const uint4 (&a)[4], float acc) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const uint32_t d[4] = {a[c].x, a[c].y, a[c].z, a[c].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      acc = __builtin_amdgcn_fdot2_f32_bf16(w[4 * c + i], __builtin_bit_cast(bf16x2, d[i]), acc,
+                                            false);
+  }
+  return acc;
+}
+
+// Each row tile (one row) gets `wpt` wavefronts; wavefront w of a tile owns the
+// groups of 8 weight rows w, w + wpt, w + 2 wpt, ... (so the tile's wavefronts read
+// adjacent rows at the same time) and streams them with one group in flight while
+// it computes the previous one.  act: W1 x rows ([T][K] bf16, tile row p -> token
+// gather[p] / k_top); W2 h rows ([n_slots][K] bf16, tile row p -> row p).  out: W1
+// h ([n_slots][ld_out] bf16, columns = gate rows), W2 y_sorted ([n_slots][ld_out]
+// bf16).
+template <bool kW1, int kSlices>
+__global__ __launch_bounds__(256) void gemv_kernel(
+    const uint16_t* __restrict__ act, const int32_t* __restrict__ gather, int k_top, int n_slots,
+    const uint8_t* __restrict__ wq, const uint8_t* __restrict__ wsc,
+    const RowTile* __restrict__ tiles, const int32_t* __restrict__ n_tiles, int n_rows, int half,
+    int groups, int wpt, float limit, int clamp, uint16_t* __restrict__ out, int ld_out) {
+  constexpr int K = kSlices * kGemvSlice;
+  const int lane = threadIdx.x & 63;
+  // wavefront-uniform values are made visibly so (scalar registers, scalar branches)
+  const int wave = static_cast<int>(blockIdx.x) * 4 +
+                   __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int tile_id = wave / wpt;
+  const int w_in = wave - tile_id * wpt;
+  if (tile_id >= *n_tiles || w_in >= groups) return;   // per wavefront (no barrier here)
+  const RowTile rt = tiles[tile_id];
+  const int p = __builtin_amdgcn_readfirstlane(rt.p_begin);   // the tile's one row
+  const int expert = __builtin_amdgcn_readfirstlane(rt.expert);
+
+  const size_t e_rows = static_cast<size_t>(expert) * n_rows;
+  const uint8_t* wbase = wq + e_rows * (K / 2) + 16 * lane;
+  const uint8_t* sbase = wsc + e_rows * (K / 32) + lane;
+  // weight row j of group g (W1: j < 4 gate rows 4 g + j, j >= 4 the matching up
+  // rows; W2: output rows 8 g + j)
+  auto wrow = [&](int g, int j) {
+    return kW1 ? (j < 4 ? 4 * g + j : half + 4 * g + (j - 4)) : kGemvRows * g + j;
+  };
+  auto load_group = [&](int g, uint4 (&q)[kGemvRows][kSlices],
+                        uint32_t (&sb)[kGemvRows][kSlices]) {
+#pragma unroll
+    for (int i = 0; i < kSlices; ++i)
+#pragma unroll
+      for (int j = 0; j < kGemvRows; ++j) {
+        const size_t row = static_cast<size_t>(wrow(g, j));
+        q[j][i] = load_nt(wbase + row * (K / 2) + 1024 * i);
+        sb[j][i] = sbase[row * (K / 32) + 64 * i];
+      }
+  };
+  uint4 a[kSlices][4];   // the lane's activations (filled below)
+  const int idx = (lane >> 2) & 7;   // the row whose sum a lane holds after the reduction
+  // group g from q / sb: products, reduction over the lanes, epilogue
+  auto finish_group = [&](int g, const uint4 (&q)[kGemvRows][kSlices],
+                          const uint32_t (&sb)[kGemvRows][kSlices]) {
+    float v[kGemvRows];
+#pragma unroll
+    for (int j = 0; j < kGemvRows; ++j) {
+      v[j] = 0.f;
+#pragma unroll
+      for (int i = 0; i < kSlices; ++i) {
+        bf16x2 w[16];
+        dequant32(q[j][i], e8m0_as_f32(sb[j][i]), w);
+        v[j] = dot32(w, a[i], v[j]);
+        // one row slice's 32 converted weights live at a time (the compiler would
+        // otherwise convert every slice of the group first and run out of registers)
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // Reduce the 8 row sums over the 64 lanes, halving the values a lane holds at
+    // each exchange: lanes with bit 4 of the lane set keep the upper half of their
+    // values, the others the lower half, each adding its partner's copy; then the
+    // same over lane bits 3 and 2 (8 -> 4 -> 2 -> 1 values).  The bit-2 partner is
+    // the mirror lane (lane ^ 7), which holds the same values.  A lane then holds
+    // row (lane >> 2) & 7 summed over 8 lanes, and the exchanges with lane ^ 2,
+    // lane ^ 1 and lane ^ 32 complete the sum over all 64 lanes.
+    const bool up16 = (lane & 16) != 0, up8 = (lane & 8) != 0, up4 = (lane & 4) != 0;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const float send = up16 ? v[m] : v[m + 4];
+      const float keep = up16 ? v[m + 4] : v[m];
+      v[m] = keep + swz_xor16(send);
+    }
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const float send = up8 ? v[m] : v[m + 2];
+      const float keep = up8 ? v[m + 2] : v[m];
+      v[m] = keep + dpp<kDppXor8>(send);
+    }
+    {
+      const float send = up4 ? v[0] : v[1];
+      const float keep = up4 ? v[1] : v[0];
+      v[0] = keep + dpp<kDppMirror8>(send);
+    }
+    float sum = v[0];
+    sum += dpp<kDppXor2>(sum);
+    sum += dpp<kDppXor1>(sum);
+    sum += __shfl_xor(sum, 32, 64);
+    if (kW1) {
+      // gate rows are rows 0..3 (lane bit 4 clear), their up rows 4..7 (lane ^ 16)
+      const float up = swz_xor16(sum);
+      if ((lane & 0x33) == 0)   // one lane per gate row
+        out[static_cast<int64_t>(p) * ld_out + 4 * g + idx] =
+            f32_to_bf16_bits(swiglu(sum, up, limit, clamp != 0));
+    } else if ((lane & 0x23) == 0) {   // one lane per row
+      out[static_cast<int64_t>(p) * ld_out + kGemvRows * g + idx] = f32_to_bf16_bits(sum);
+    }
+  };
+
+  // two register sets: the next group's loads are issued before the current group
+  // is computed.  The first group's loads go out before the activation row's
+  // (which wait on the gather index).
+  uint4 qa[kGemvRows][kSlices], qb[kGemvRows][kSlices];
+  uint32_t sa[kGemvRows][kSlices], sbb[kGemvRows][kSlices];
+  int g = w_in;
+  load_group(g, qa, sa);
+
+  // the lane's activations of slice i: elements 2048 i + 32 lane .. +31
+  {
+    int64_t row = p;
+    bool valid = true;
+    if (kW1) {
+      const int slot = __builtin_amdgcn_readfirstlane(gather[p]);
+      valid = static_cast<unsigned>(slot) < static_cast<unsigned>(n_slots);
+      row = valid ? slot / k_top : 0;
+    }
+    const uint4* src = reinterpret_cast<const uint4*>(act + row * K + 32 * lane);
+#pragma unroll
+    for (int i = 0; i < kSlices; ++i)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint4 d = src[i * (kGemvSlice / 8) + c];
+        a[i][c] = valid ? d : make_uint4(0u, 0u, 0u, 0u);
+      }
+  }
+
+#pragma unroll 1
+  for (;;) {
+    const int g1 = g + wpt;
+    if (g1 < groups) load_group(g1, qb, sbb);
+    finish_group(g, qa, sa);
+    if (g1 >= groups) break;
+    const int g2 = g1 + wpt;
+    if (g2 < groups) load_group(g2, qa, sa);
+    finish_group(g1, qb, sbb);
+    if (g2 >= groups) break;
+    g = g2;
+  }
+}
+
+template <bool kW1, int kSlices>
+hipError_t launch_gemv_t(unsigned grid, hipStream_t stream, const uint16_t* act,
+                         const int32_t* gather, int k_top, int n_slots, const uint8_t* wq,
+                         const uint8_t* wsc, const RowTile* tiles, const int32_t* n_tiles,
+                         int n_rows, int half, int groups, int wpt, float limit, int clamp,
+                         uint16_t* out, int ld_out) {
+  gemv_kernel<kW1, kSlices><<<grid, 256, 0, stream>>>(act, gather, k_top, n_slots, wq, wsc, tiles,
+                                                      n_tiles, n_rows, half, groups, wpt, limit,
+                                                      clamp, out, ld_out);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemv(bool w1, int64_t tile_bound, hipStream_t stream, const uint16_t* act,
+                       const int32_t* gather, int k_top, int n_slots, const uint8_t* wq,
+                       const uint8_t* wsc, const RowTile* tiles, const int32_t* n_tiles, int K,
+                       int n_rows, int half, float limit, int clamp, uint16_t* out, int ld_out) {
+  // groups of 8 weight rows per tile (W1: 4 gate rows and their up rows), and
+  // wavefronts per tile: about two per SIMD over the possible tiles (at most
+  // kGemvMaxWaves in all), a multiple of 4 so a workgroup's wavefronts share a tile
+  const int groups = w1 ? half / 4 : n_rows / kGemvRows;
+  int64_t wpt = kGemvMaxWaves / (tile_bound > 0 ? tile_bound : 1);
+  wpt = wpt < 4 ? 4 : wpt / 4 * 4;
+  if (wpt > groups) wpt = (groups + 3) / 4 * 4;
+  const int64_t waves = tile_bound * wpt;
+  const unsigned grid = static_cast<unsigned>((waves + 3) / 4);
+  if (grid == 0) return hipSuccess;
+  const int w = static_cast<int>(wpt);
+  const bool two = K == 2 * kGemvSlice;
+  if (w1)
+    return two ? launch_gemv_t<true, 2>(grid, stream, act, gather, k_top, n_slots, wq, wsc, tiles,
+                                        n_tiles, n_rows, half, groups, w, limit, clamp, out, ld_out)
+               : launch_gemv_t<true, 1>(grid, stream, act, gather, k_top, n_slots, wq, wsc, tiles,
+                                        n_tiles, n_rows, half, groups, w, limit, clamp, out, ld_out);
+  return two ? launch_gemv_t<false, 2>(grid, stream, act, gather, k_top, n_slots, wq, wsc, tiles,
+                                       n_tiles, n_rows, half, groups, w, limit, clamp, out, ld_out)
+             : launch_gemv_t<false, 1>(grid, stream, act, gather, k_top, n_slots, wq, wsc, tiles,
+                                       n_tiles, n_rows, half, groups, w, limit, clamp, out, ld_out);
+}
+
+}  // namespace moe

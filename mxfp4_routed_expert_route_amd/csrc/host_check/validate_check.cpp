@@ -47,7 +47,45 @@ int main() {
   WsLayout L;
   expect("layout", workspace_layout(8191, 256, 6, 4096, 2048, &L), MOE_OK);
   if (L.n_blocks != 16 || L.offsets_bytes != 16 * 256 * 4) { std::printf("FAIL offsets layout\n"); ++failures; }
-  if (L.tile_bound != 256 + 49146 / kFfnMinTileRows) { std::printf("FAIL tile bound\n"); ++failures; }
+  if (L.tile_bound != (49146 + (kFfnMinTileRows - 1) * 256) / kFfnMinTileRows) {
+    std::printf("FAIL tile bound\n"); ++failures;
+  }
+  // decode sizes (T k < E, K of 2048 / 4096): 1-row tiles on the GEMV kernels
+  WsLayout G;
+  expect("layout gemv", workspace_layout(8, 256, 6, 4096, 2048, &G), MOE_OK);
+  if (ffn_tile_rows(8, 256, 6, 4096, 2048) != kFfnGemvTileRows || G.tile_bound != 48) {
+    std::printf("FAIL gemv tile rule / bound\n"); ++failures;
+  }
+  if (ffn_tile_rows(8, 256, 6, 256, 128) != 16 || ffn_tile_rows(43, 256, 6, 4096, 2048) != 16) {
+    std::printf("FAIL gemv tile rule limits\n"); ++failures;
+  }
+  // ffn_tile_bound against the exact tile count of random and extreme row counts
+  {
+    unsigned rng = 12345u;
+    auto next = [&]() { rng = rng * 1664525u + 1013904223u; return rng >> 8; };
+    const int sizes[] = {2, 16, 32, 80, 128};
+    for (int trial = 0; trial < 2000; ++trial) {
+      const int E = 1 + static_cast<int>(next() % 300);
+      const int R = sizes[trial % 5];
+      static int c[300];
+      int64_t n = 0, tiles = 0;
+      for (int e = 0; e < E; ++e) {
+        const unsigned kind = trial % 4;   // sparse, 1 mod R, skewed, uniform
+        c[e] = kind == 0 ? (next() % 5 == 0 ? static_cast<int>(next() % 4) : 0)
+             : kind == 1 ? static_cast<int>(R * (next() % 3) + 1)
+             : kind == 2 ? (e == 0 ? static_cast<int>(next() % 5000) : static_cast<int>(next() % 3))
+                         : static_cast<int>(next() % 200);
+        n += c[e];
+        tiles += (c[e] + R - 1) / R;
+      }
+      if (tiles > ffn_tile_bound(n, E, R)) {
+        std::printf("FAIL tile bound trial %d: %lld tiles > %lld\n", trial,
+                    static_cast<long long>(tiles), static_cast<long long>(ffn_tile_bound(n, E, R)));
+        ++failures;
+        break;
+      }
+    }
+  }
   if (L.ffn_plan_offset < (size_t)49146 * 2048 * 2 || L.total < L.ffn_bytes || L.total < L.offsets_bytes) {
     std::printf("FAIL ffn layout\n"); ++failures;
   }

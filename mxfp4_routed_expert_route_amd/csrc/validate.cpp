@@ -42,11 +42,14 @@ moe_status workspace_layout(int64_t T, int32_t E, int32_t k, int32_t H, int32_t 
   const int64_t slots = T * k;
   L.n_blocks = (T + kOffsBlockTokens - 1) / kOffsBlockTokens;
   L.offsets_bytes = align_up(static_cast<size_t>(L.n_blocks) * E * sizeof(int32_t), 256);
-  L.tile_bound = ffn_tile_bound(slots, E, kFfnMinTileRows);
+  {   // plan room for the smallest tile the FFN can take at these sizes
+    const int rows = ffn_tile_rows(T, E, k, H, I);
+    L.tile_bound = ffn_tile_bound(slots, E, rows < kFfnMinTileRows ? rows : kFfnMinTileRows);
+  }
   L.ffn_h_offset = 0;
   size_t end = align_up(static_cast<size_t>(slots) * static_cast<size_t>(I) * 2, 256);
   L.ffn_hs_offset = L.ffn_xq_offset = L.ffn_xs_offset = end;
-  if (ffn_tiled(T, E, k)) {   // two-part FP8 activations: scales of h, then x and its scales
+  if (ffn_tiled(T, E, k, H, I)) {   // two-part FP8 activations: scales of h, then x and its scales
     L.ffn_hs_offset = end;
     end = align_up(end + static_cast<size_t>(slots) * static_cast<size_t>(I / 32), 256);
     L.ffn_xq_offset = end;

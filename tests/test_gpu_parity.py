@@ -232,6 +232,42 @@ def test_streaming_activation_paths(T, E, k, H, I, seed, limit):
     whole_layer_parity(tiny(T, E, k, H, I, seed, skew=True), limit)
 
 
+@pytest.mark.parametrize("T,E,k,H,I,seed,hot", [
+    (7, 16, 2, 2048, 2048, 41, None),   # K = 2048 for both GEMMs: one 1 KB slice per row
+    (2, 16, 4, 4096, 2048, 42, None),   # W1 two slices per row, W2 one
+    (3, 16, 3, 2048, 4096, 43, None),   # W1 one slice, W2 two
+    (7, 16, 2, 2048, 2048, 44, 5),      # expert 5 takes every token: 7 one-row tiles
+    (1, 8, 2, 4096, 4096, 45, None),    # one token
+])
+@pytest.mark.parametrize("limit", [10.0, None])
+def test_gemv_decode_path(T, E, k, H, I, seed, hot, limit):
+    # fewer rows than experts (T k < E) and K of 2048 or 4096: the one-row tiles of
+    # the GEMV kernels, through the separate calls and the one-call layer
+    inp = tiny(T, E, k, H, I, seed)
+    if hot is not None:
+        inp["logits"][:, hot] += 100.0
+    _say(f"[parity] gemv T={T} E={E} k={k} H={H} I={I} limit={limit}")
+    ref = oracle.moe_layer(inp, limit)
+    for fused in (False, True):
+        b = run_gpu(inp, limit, fused)
+        check_routing(b, ref, E, k)
+        ffn_close(b.y_sorted.float().cpu().numpy(), ref["y_sorted"])
+        ffn_close(b.y.float().cpu().numpy(), ref["y"])
+
+
+def test_gemv_nan_and_extreme_scales():
+    inp = tiny(6, 16, 2, 2048, 2048, 46)
+    ids, _ = oracle.route(inp["logits"], 2)
+    e1, e2 = int(ids[0, 0]), int(ids[1, 1])
+    w1_s = inp["w1_s"].copy()
+    w2_s = inp["w2_s"].copy()
+    w1_s[e1, 3, 10] = 255     # NaN block in gate row 3 (h column 3) of a touched expert
+    w1_s[e2, :, 0] = 0        # 2^-127 blocks
+    w2_s[e2, 17, 5] = 255     # NaN block in output row 17
+    inp = dict(inp, w1_s=w1_s, w2_s=w2_s)
+    whole_layer_parity(inp, 10.0)
+
+
 def test_single_expert():
     # E = 1, k = 1: every token routes to expert 0 with weight 1
     whole_layer_parity(tiny(50, 1, 1, 128, 128, 18), 10.0)
