@@ -53,7 +53,7 @@ CSRC = "mxfp4_routed_expert_route_amd/csrc"
 # Committed rocprofv3 summary per workload: W1 HBM bytes per launch (FETCH_SIZE and
 # WRITE_SIZE, scaled by the copy calibration), valid while the digest of the
 # kernel sources it names still matches.
-PROFILES = {1: "ffn_w1_stream_verify-1+7.md", 2: "ffn_stream_burst-64x8.md",
+PROFILES = {1: "ffn_gemv_verify-1+7.md", 2: "ffn_stream_burst-64x8.md",
             3: "ffn_tile_prefill-2048.md", 4: "ffn_tile_skewed-8191.md"}
 
 
