@@ -35,7 +35,10 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kGemvRows = 8;         // weight rows per wavefront
 constexpr int kGemvSlice = 2048;     // K elements per 1 KB row slice (64 lanes x 32)
-constexpr int kGemvMaxWaves = 2048;  // wavefronts per launch: two per SIMD
+// wavefronts per launch: with two resident per SIMD, six rounds of them (measured on
+// the verify step's W1 / W2: 2,048 wavefronts 70.6 / 39.0 us, 3,072 68.3 / 36.9,
+// 12,288 67.3 / 34.8, 24,576 -- one group each -- 75.3 / 35.6)
+constexpr int kGemvMaxWaves = 12288;
 
 __device__ __forceinline__ uint4 load_nt(const uint8_t* p) {
   const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
@@ -246,8 +249,8 @@ hipError_t launch_gemv(bool w1, int64_t tile_bound, hipStream_t stream, const ui
                        const uint8_t* wsc, const RowTile* tiles, const int32_t* n_tiles, int K,
                        int n_rows, int half, float limit, int clamp, uint16_t* out, int ld_out) {
   // groups of 8 weight rows per tile (W1: 4 gate rows and their up rows), and
-  // wavefronts per tile: about two per SIMD over the possible tiles (at most
-  // kGemvMaxWaves in all), a multiple of 4 so a workgroup's wavefronts share a tile
+  // wavefronts per tile: kGemvMaxWaves over the possible tiles, a multiple of 4 so
+  // a workgroup's wavefronts share a tile, at most one per group
   const int groups = w1 ? half / 4 : n_rows / kGemvRows;
   int64_t wpt = kGemvMaxWaves / (tile_bound > 0 ? tile_bound : 1);
   wpt = wpt < 4 ? 4 : wpt / 4 * 4;
