@@ -17,9 +17,10 @@ W1 / W2 kernel times and roofline fractions.
 
 Timing, per workload: W untimed warm-up steps, then exactly K steps bracketed by
 torch.cuda.synchronize() and the host clock.  Inside the timed region every
-event_every-th step runs the separate calls with the instrumented FFN entry
-point, which records HIP events on the library's stream around the W1 and W2
-kernels.  Two copies of the expert weights alternate between steps so that a
+event_every-th step runs the instrumented one-call layer (moe_forward_mxfp4_timed:
+the same kernels, plus HIP events on the library's stream around the W1 and W2
+kernels); with --separate-routing, the separate calls with the instrumented FFN
+entry point.  Two copies of the expert weights alternate between steps so that a
 step never finds the previous step's weights in the 256 MB last-level cache (as
 in a real model, where other layers run in between).
 
@@ -243,9 +244,10 @@ class Runner:
                      ptr(b.scatter), ptr(b.y_sorted), ptr(b.y), ptr(b.ws), b.ws.numel(), S))
 
     def step(self, i, evs=None, ffn_events=None, c=None):
-        """One layer.  evs: 8 events around every call (breakdown pass only);
-        ffn_events: the 3 events inside the FFN call.  With neither (and the
-        default routing), the layer is one moe_forward_mxfp4 call."""
+        """One layer.  evs: 8 events around every call (breakdown pass only: the
+        separate calls); ffn_events: the 3 events inside the FFN step.  Without evs
+        (and with the default routing) the layer is one moe_forward_mxfp4 call, or
+        one moe_forward_mxfp4_timed call with ffn_events."""
         lib, S, sep = self.lib, self.S, self.args.separate_routing
         c = self.calls[i % len(self.calls)] if c is None else c
         record = self.hip.rt.hipEventRecord
@@ -255,8 +257,12 @@ class Runner:
                 from mxfp4_routed_expert_route_amd import binding
                 raise binding.MoeError(name, rc)
 
-        if evs is None and ffn_events is None and not sep:
-            check(lib.moe_forward_mxfp4(*c["forward"]), "moe_forward_mxfp4")
+        if evs is None and not sep:
+            if ffn_events is None:
+                check(lib.moe_forward_mxfp4(*c["forward"]), "moe_forward_mxfp4")
+            else:
+                check(lib.moe_forward_mxfp4_timed(*c["forward"][:-1], ffn_events,
+                                                  c["forward"][-1]), "moe_forward_mxfp4_timed")
             return
         if evs is not None:
             record(evs[0], S)
@@ -465,10 +471,11 @@ def main():
     ap.add_argument("--separate-routing", action="store_true",
                     help="route with moe_route + moe_build_bitmatrix + moe_expert_offsets instead "
                          "of the fused moe_route_and_group (same outputs)")
-    ap.add_argument("--event-every", type=int, default=4,
-                    help="in the timed region, every n-th step runs the FFN call that records "
-                         "HIP events around W1 and W2 (an event costs GPU time, so the others "
-                         "run without)")
+    ap.add_argument("--event-every", type=int, default=10,
+                    help="in the timed region, every n-th step runs the call that records "
+                         "HIP events around W1 and W2 (the three event records cost ~10 us of "
+                         "GPU time per instrumented step on the verify layer, so the others run "
+                         "without)")
     ap.add_argument("--graph-steps", type=int, default=100,
                     help="after the timed region, replay the layer captured as HIP graphs this "
                          "many times and report graph_us_per_layer (0: skip)")
@@ -512,6 +519,8 @@ def main():
                         [F, P, P, SZ, P]),
                        ("moe_forward_mxfp4", [P, P, I64, I32, I32, I32, I32, P, P, P, P, F] +
                         [P] * 10 + [SZ, P]),
+                       ("moe_forward_mxfp4_timed", [P, P, I64, I32, I32, I32, I32, P, P, P, P,
+                                                    F] + [P] * 10 + [SZ, P, P]),
                        ("moe_combine", [P, P, P, I64, I32, I32, P, P])):
         getattr(lib, name).argtypes = argt
         getattr(lib, name).restype = ctypes.c_int
@@ -568,8 +577,8 @@ def main():
                    "parallelism": "single GPU",
                    "calls": ("moe_route + moe_build_bitmatrix + moe_expert_offsets + "
                              "moe_grouped_ffn_mxfp4 + moe_combine" if args.separate_routing else
-                             "moe_forward_mxfp4 (every event_every-th step: moe_route_and_group + "
-                             "moe_grouped_ffn_mxfp4_timed + moe_combine)")},
+                             "moe_forward_mxfp4 (every event_every-th step: "
+                             "moe_forward_mxfp4_timed)")},
         "roofline": h["roofline"],
         "event_every": max(1, args.event_every),
         "workloads": {inputs.workload(i).name: r for i, r in results.items()},

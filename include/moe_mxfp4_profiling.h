@@ -1,6 +1,6 @@
 /*
- * moe_mxfp4_profiling.h -- instrumented variant of moe_grouped_ffn_mxfp4 for
- * measurement tools.
+ * moe_mxfp4_profiling.h -- instrumented variants of moe_grouped_ffn_mxfp4 and
+ * moe_forward_mxfp4 for measurement tools.
  *
  * For callers that time the grouped FFN's kernels one by one (benchmarks, the
  * roofline report): it does exactly what moe_grouped_ffn_mxfp4 does (same
@@ -12,6 +12,17 @@
  * Each entry is a hipEvent_t created by the caller (passed as void*); all three
  * must be non-NULL when T > 0.  Elapsed time between consecutive events is the
  * duration of one kernel.  T = 0 records nothing.
+ *
+ * moe_forward_mxfp4_timed is the same for the whole layer: exactly what
+ * moe_forward_mxfp4 does (same arguments, checks, kernels and stream), with the
+ * three events recorded inside its FFN step:
+ *   events[0]  after the routing front-end and the row-tile plan, before W1
+ *   events[1]  after the W1 kernel, before the W2 kernel
+ *   events[2]  after the W2 kernel.  Where the decode GEMV path (fewer routed rows
+ *              than experts) folds the weighted combine into its W2 launch, that
+ *              launch is the W2 kernel here; on the other paths the combine
+ *              follows events[2].
+ * All three must be non-NULL when T > 0; T = 0 records nothing.
  *
  * moe_read_probe is the "achievable read bandwidth" marker measured beside the
  * FFN kernels: a plain streaming read of `bytes` bytes of device memory at `buf`
@@ -43,6 +54,15 @@ moe_status moe_grouped_ffn_mxfp4_timed(const uint16_t* x, int64_t T, int32_t H, 
                                        const int32_t* offsets, const int32_t* gather,
                                        float swiglu_limit, uint16_t* y_sorted, void* ws,
                                        size_t ws_bytes, void* const* events, void* stream);
+
+moe_status moe_forward_mxfp4_timed(const float* logits, const uint16_t* x, int64_t T, int32_t H,
+                                   int32_t I, int32_t E, int32_t k, const uint8_t* w1,
+                                   const uint8_t* w1_scale, const uint8_t* w2,
+                                   const uint8_t* w2_scale, float swiglu_limit, int32_t* topk_ids,
+                                   float* topk_weights, uint32_t* bitmatrix, int32_t* counts,
+                                   int32_t* offsets, int32_t* gather, int32_t* scatter,
+                                   uint16_t* y_sorted, uint16_t* y, void* ws, size_t ws_bytes,
+                                   void* const* events, void* stream);
 
 moe_status moe_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 

@@ -52,6 +52,9 @@ _SIG = {
                           _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
     "moe_forward_mxfp4_noalloc": [_P, _P, _I64, _I32, _I32, _I32, _I32, _P, _P, _P, _P,
                                   ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+    "moe_forward_mxfp4_timed": [_P, _P, _I64, _I32, _I32, _I32, _I32, _P, _P, _P, _P,
+                                ctypes.c_float, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                ctypes.c_size_t, _P, _P],
     "moe_read_probe": [_P, ctypes.c_size_t, _P, _P],
     "moe_workspace_bytes": [_I64, _I32, _I32, _I32, _I32],
     "moe_status_string": [ctypes.c_int],
@@ -183,6 +186,32 @@ def moe_forward_mxfp4(logits, x, k: int, w1, w1_scale, w2, w2_scale, swiglu_limi
         _ptr(scatter, torch.int32, "scatter"), _ptr(y_sorted, BF16, "y_sorted"),
         _ptr(y, BF16, "y"), _ptr(ws, torch.uint8, "ws"), ws.numel() if ws is not None else 0,
         _stream(stream)))
+
+
+def moe_forward_mxfp4_timed(logits, x, k: int, w1, w1_scale, w2, w2_scale, swiglu_limit: float,
+                            topk_ids, topk_weights, bitmatrix, counts, offsets, gather, scatter,
+                            y_sorted, y, ws, events, stream=None):
+    """moe_forward_mxfp4 plus three HIP events recorded around its W1 and W2
+    kernels; `events` holds three hipEvent_t handles (ints) created by the caller."""
+    T, E = logits.shape
+    H = x.shape[1]
+    two_i = w1.shape[1]
+    ev = None
+    if events is not None:
+        if len(events) != 3:
+            raise ValueError("events must hold three hipEvent_t handles")
+        ev = (ctypes.c_void_p * 3)(*events)
+    _check("moe_forward_mxfp4_timed", load().moe_forward_mxfp4_timed(
+        _ptr(logits, torch.float32, "logits"), _ptr(x, BF16, "x"), T, H, two_i // 2, E, k,
+        _ptr(w1, torch.uint8, "w1"), _ptr(w1_scale, torch.uint8, "w1_scale"),
+        _ptr(w2, torch.uint8, "w2"), _ptr(w2_scale, torch.uint8, "w2_scale"),
+        float(swiglu_limit), _ptr(topk_ids, torch.int32, "topk_ids"),
+        _ptr(topk_weights, torch.float32, "topk_weights"),
+        _ptr(bitmatrix, torch.int32, "bitmatrix"), _ptr(counts, torch.int32, "counts"),
+        _ptr(offsets, torch.int32, "offsets"), _ptr(gather, torch.int32, "gather"),
+        _ptr(scatter, torch.int32, "scatter"), _ptr(y_sorted, BF16, "y_sorted"),
+        _ptr(y, BF16, "y"), _ptr(ws, torch.uint8, "ws"), ws.numel() if ws is not None else 0,
+        ev, _stream(stream)))
 
 
 # moe_forward_mxfp4_noalloc's static device scratch (MOE_NOALLOC_SCRATCH_BYTES)

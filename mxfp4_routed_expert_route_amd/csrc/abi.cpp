@@ -40,7 +40,8 @@ moe_status forward_layer(const float* logits, const uint16_t* x, int64_t T, int3
                          const uint8_t* w2, const uint8_t* w2_scale, float swiglu_limit,
                          int32_t* topk_ids, float* topk_weights, uint32_t* bitmatrix,
                          int32_t* counts, int32_t* offsets, int32_t* gather, int32_t* scatter,
-                         uint16_t* y_sorted, uint16_t* y, void* ws, hipStream_t st) {
+                         uint16_t* y_sorted, uint16_t* y, void* ws, hipStream_t st,
+                         hipEvent_t const* events) {
   if (T == 0)
     return from_hip(launch_offsets(nullptr, nullptr, 0, E, k, counts, offsets, nullptr, nullptr,
                                    nullptr, st));
@@ -59,9 +60,13 @@ moe_status forward_layer(const float* logits, const uint16_t* x, int64_t T, int3
                                         counts, offsets, gather, scatter, ws, st, &plan,
                                         &plan_written);
   if (e != hipSuccess) return MOE_ERR_HIP;
+  // on the decode GEMV path the W2 launch also writes y (same arithmetic as the combine)
+  const CombineArgs fold{topk_ids, topk_weights, scatter, y};
+  bool combined = false;
   e = launch_ffn(x, T, H, I, E, k, w1, w1_scale, w2, w2_scale, counts, offsets, gather,
-                 swiglu_limit, y_sorted, ws, L, st, nullptr, plan_written);
+                 swiglu_limit, y_sorted, ws, L, st, events, plan_written, &fold, &combined);
   if (e != hipSuccess) return MOE_ERR_HIP;
+  if (combined) return MOE_OK;
   return from_hip(launch_combine(y_sorted, topk_weights, scatter, T, H, k, y, st));
 }
 
@@ -163,6 +168,28 @@ moe_status moe_grouped_ffn_mxfp4_timed(const uint16_t* x, int64_t T, int32_t H, 
                       static_cast<hipEvent_t>(events[2])};
   return from_hip(moe::launch_ffn(x, T, H, I, E, k, w1, w1_scale, w2, w2_scale, counts, offsets,
                                   gather, swiglu_limit, y_sorted, ws, L, as_stream(stream), ev));
+}
+
+moe_status moe_forward_mxfp4_timed(const float* logits, const uint16_t* x, int64_t T, int32_t H,
+                                   int32_t I, int32_t E, int32_t k, const uint8_t* w1,
+                                   const uint8_t* w1_scale, const uint8_t* w2,
+                                   const uint8_t* w2_scale, float swiglu_limit, int32_t* topk_ids,
+                                   float* topk_weights, uint32_t* bitmatrix, int32_t* counts,
+                                   int32_t* offsets, int32_t* gather, int32_t* scatter,
+                                   uint16_t* y_sorted, uint16_t* y, void* ws, size_t ws_bytes,
+                                   void* const* events, void* stream) {
+  moe_status s = moe::check_forward(logits, x, T, H, I, E, k, w1, w1_scale, w2, w2_scale,
+                                    topk_ids, topk_weights, bitmatrix, counts, offsets, gather,
+                                    scatter, y_sorted, y, ws, ws_bytes);
+  if (s != MOE_OK) return s;
+  if (T > 0 && (!events || !events[0] || !events[1] || !events[2]))
+    return MOE_ERR_INVALID_ARGUMENT;
+  hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
+  if (T > 0)
+    for (int i = 0; i < 3; ++i) ev[i] = static_cast<hipEvent_t>(events[i]);
+  return moe::forward_layer(logits, x, T, H, I, E, k, w1, w1_scale, w2, w2_scale, swiglu_limit,
+                            topk_ids, topk_weights, bitmatrix, counts, offsets, gather, scatter,
+                            y_sorted, y, ws, as_stream(stream), T > 0 ? ev : nullptr);
 }
 
 moe_status moe_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream) {

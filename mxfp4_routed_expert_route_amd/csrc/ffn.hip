@@ -42,7 +42,8 @@ hipError_t launch_ffn(const uint16_t* x, int64_t T, int H, int I, int E, int k,
                       const uint8_t* w2s, const int32_t* counts, const int32_t* offsets,
                       const int32_t* gather, float limit, uint16_t* y_sorted, void* ws,
                       const WsLayout& L, hipStream_t stream, hipEvent_t const* events,
-                      bool plan_ready) {
+                      bool plan_ready, const CombineArgs* combine, bool* combined) {
+  if (combined) *combined = false;
   const int64_t n_slots = T * k;
   char* wsb = static_cast<char*>(ws);
   uint16_t* h = reinterpret_cast<uint16_t*>(wsb + L.ffn_h_offset);
@@ -87,8 +88,15 @@ hipError_t launch_ffn(const uint16_t* x, int64_t T, int H, int I, int E, int k,
       err = hipEventRecord(events[1], stream);
       if (err != hipSuccess) return err;
     }
-    err = launch_gemv(false, tile_bound, stream, h, nullptr, k, slots_i, w2, w2s, tiles, n_tiles,
-                      I, H, 0, limit, 0, y_sorted, H);
+    if (combine) {   // W2 and the combine in one launch, token by token
+      err = launch_gemv_w2_combine(T, k, E, slots_i, stream, h, combine->topk_ids,
+                                   combine->topk_weights, combine->scatter, w2, w2s, I, H,
+                                   y_sorted, combine->y);
+      if (err == hipSuccess && combined) *combined = true;
+    } else {
+      err = launch_gemv(false, tile_bound, stream, h, nullptr, k, slots_i, w2, w2s, tiles,
+                        n_tiles, I, H, 0, limit, 0, y_sorted, H);
+    }
   } else if (tile_rows <= 32) {
     // W1: 8 * frags gate rows (and as many up rows) per wavefront; W2: 16 * frags rows
     const int frags = stream_frags(tile_rows / 16);

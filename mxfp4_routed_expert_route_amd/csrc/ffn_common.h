@@ -148,4 +148,12 @@ hipError_t launch_gemv(bool w1, int64_t tile_bound, hipStream_t stream, const ui
                        const uint8_t* wsc, const RowTile* tiles, const int32_t* n_tiles, int K,
                        int n_rows, int half, float limit, int clamp, uint16_t* out, int ld_out);
 
+// W2 of the decode GEMV path with the weighted combine folded in (ffn_gemv.hip):
+// y_sorted as launch_gemv(false, ...) writes it and y as the combine kernel does,
+// one wavefront per (token, 8 output columns).
+hipError_t launch_gemv_w2_combine(int64_t T, int k_top, int E, int n_slots, hipStream_t stream,
+                                  const uint16_t* h, const int32_t* ids, const float* topw,
+                                  const int32_t* scatter, const uint8_t* wq, const uint8_t* wsc,
+                                  int K, int n_rows, uint16_t* y_sorted, uint16_t* y);
+
 }  // namespace moe

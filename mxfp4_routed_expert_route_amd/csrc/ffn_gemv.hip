@@ -23,7 +23,8 @@
 // tiles, whose wavefronts read its weights at about the same time (the second read
 // mostly from cache); one activation row keeps the registers for two groups of
 // weights in flight.  No LDS, no workgroup barrier: every wavefront runs on its
-// own.
+// own.  In the one-call layer, W2 runs with the weighted combine folded in
+// (gemv_w2_combine_kernel, one workgroup per token and 32 output columns).
 #include <type_traits>
 
 #include "ffn_common.h"
@@ -86,6 +87,75 @@ __device__ __forceinline__ float dot32(const bf16x2 (&w)[16], const uint4 (&a)[4
   return acc;
 }
 
+// The 8 row sums of a group: v[j] = sum over the lane's elements of row j's
+// dequantised weights times the lane's activations, fp32, slice by slice.
+// scale(j, i): the E8M0 scale byte of row j, slice i, for this lane.
+template <int kSlices, typename Scale>
+__device__ __forceinline__ void gemv_dot8(const uint4 (&q)[kGemvRows][kSlices], Scale scale,
+                                          const uint4 (&a)[kSlices][4], float (&v)[kGemvRows]) {
+#pragma unroll
+  for (int j = 0; j < kGemvRows; ++j) {
+    v[j] = 0.f;
+#pragma unroll
+    for (int i = 0; i < kSlices; ++i) {
+      bf16x2 w[16];
+      dequant32(q[j][i], e8m0_as_f32(scale(j, i)), w);
+      v[j] = dot32(w, a[i], v[j]);
+      // one row slice's 32 converted weights live at a time (the compiler would
+      // otherwise convert every slice of the group first and run out of registers)
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+// Reduce the 8 row sums over the 64 lanes, halving the values a lane holds at each
+// exchange: lanes with bit 4 of the lane set keep the upper half of their values,
+// the others the lower half, each adding its partner's copy; then the same over
+// lane bits 3 and 2 (8 -> 4 -> 2 -> 1 values).  The bit-2 partner is the mirror
+// lane (lane ^ 7), which holds the same values.  A lane then holds row
+// (lane >> 2) & 7 summed over 8 lanes, and the exchanges with lane ^ 2, lane ^ 1
+// and lane ^ 32 complete the sum over all 64 lanes, which every lane holding that
+// row returns.
+__device__ __forceinline__ float gemv_reduce8(float (&v)[kGemvRows], int lane) {
+  const bool up16 = (lane & 16) != 0, up8 = (lane & 8) != 0, up4 = (lane & 4) != 0;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const float send = up16 ? v[m] : v[m + 4];
+    const float keep = up16 ? v[m + 4] : v[m];
+    v[m] = keep + swz_xor16(send);
+  }
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const float send = up8 ? v[m] : v[m + 2];
+    const float keep = up8 ? v[m + 2] : v[m];
+    v[m] = keep + dpp<kDppXor8>(send);
+  }
+  {
+    const float send = up4 ? v[0] : v[1];
+    const float keep = up4 ? v[1] : v[0];
+    v[0] = keep + dpp<kDppMirror8>(send);
+  }
+  float sum = v[0];
+  sum += dpp<kDppXor2>(sum);
+  sum += dpp<kDppXor1>(sum);
+  return sum + __shfl_xor(sum, 32, 64);
+}
+
+// The lane's activations of a K-row: slice i, elements 2048 i + 32 lane .. +31
+// (zeros for an invalid row)
+template <int kSlices>
+__device__ __forceinline__ void gemv_load_act(const uint16_t* row_base, bool valid, int lane,
+                                              uint4 (&a)[kSlices][4]) {
+  const uint4* src = reinterpret_cast<const uint4*>(row_base + 32 * lane);
+#pragma unroll
+  for (int i = 0; i < kSlices; ++i)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint4 d = src[i * (kGemvSlice / 8) + c];
+      a[i][c] = valid ? d : make_uint4(0u, 0u, 0u, 0u);
+    }
+}
+
 // Each row tile (one row) gets `wpt` wavefronts; wavefront w of a tile owns the
 // groups of 8 weight rows w, w + wpt, w + 2 wpt, ... (so the tile's wavefronts read
 // adjacent rows at the same time) and streams them with one group in flight while
@@ -136,48 +206,8 @@ __global__ __launch_bounds__(256) void gemv_kernel(
   auto finish_group = [&](int g, const uint4 (&q)[kGemvRows][kSlices],
                           const uint32_t (&sb)[kGemvRows][kSlices]) {
     float v[kGemvRows];
-#pragma unroll
-    for (int j = 0; j < kGemvRows; ++j) {
-      v[j] = 0.f;
-#pragma unroll
-      for (int i = 0; i < kSlices; ++i) {
-        bf16x2 w[16];
-        dequant32(q[j][i], e8m0_as_f32(sb[j][i]), w);
-        v[j] = dot32(w, a[i], v[j]);
-        // one row slice's 32 converted weights live at a time (the compiler would
-        // otherwise convert every slice of the group first and run out of registers)
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    // Reduce the 8 row sums over the 64 lanes, halving the values a lane holds at
-    // each exchange: lanes with bit 4 of the lane set keep the upper half of their
-    // values, the others the lower half, each adding its partner's copy; then the
-    // same over lane bits 3 and 2 (8 -> 4 -> 2 -> 1 values).  The bit-2 partner is
-    // the mirror lane (lane ^ 7), which holds the same values.  A lane then holds
-    // row (lane >> 2) & 7 summed over 8 lanes, and the exchanges with lane ^ 2,
-    // lane ^ 1 and lane ^ 32 complete the sum over all 64 lanes.
-    const bool up16 = (lane & 16) != 0, up8 = (lane & 8) != 0, up4 = (lane & 4) != 0;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const float send = up16 ? v[m] : v[m + 4];
-      const float keep = up16 ? v[m + 4] : v[m];
-      v[m] = keep + swz_xor16(send);
-    }
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const float send = up8 ? v[m] : v[m + 2];
-      const float keep = up8 ? v[m + 2] : v[m];
-      v[m] = keep + dpp<kDppXor8>(send);
-    }
-    {
-      const float send = up4 ? v[0] : v[1];
-      const float keep = up4 ? v[1] : v[0];
-      v[0] = keep + dpp<kDppMirror8>(send);
-    }
-    float sum = v[0];
-    sum += dpp<kDppXor2>(sum);
-    sum += dpp<kDppXor1>(sum);
-    sum += __shfl_xor(sum, 32, 64);
+    gemv_dot8<kSlices>(q, [&](int j, int i) { return sb[j][i]; }, a, v);
+    const float sum = gemv_reduce8(v, lane);
     if (kW1) {
       // gate rows are rows 0..3 (lane bit 4 clear), their up rows 4..7 (lane ^ 16)
       const float up = swz_xor16(sum);
@@ -197,7 +227,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(
   int g = w_in;
   load_group(g, qa, sa);
 
-  // the lane's activations of slice i: elements 2048 i + 32 lane .. +31
+  // the lane's activations of the tile's row
   {
     int64_t row = p;
     bool valid = true;
@@ -206,14 +236,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(
       valid = static_cast<unsigned>(slot) < static_cast<unsigned>(n_slots);
       row = valid ? slot / k_top : 0;
     }
-    const uint4* src = reinterpret_cast<const uint4*>(act + row * K + 32 * lane);
-#pragma unroll
-    for (int i = 0; i < kSlices; ++i)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const uint4 d = src[i * (kGemvSlice / 8) + c];
-        a[i][c] = valid ? d : make_uint4(0u, 0u, 0u, 0u);
-      }
+    gemv_load_act<kSlices>(act + row * K, valid, lane, a);
   }
 
 #pragma unroll 1
@@ -228,6 +251,177 @@ __global__ __launch_bounds__(256) void gemv_kernel(
     if (g2 >= groups) break;
     g = g2;
   }
+}
+
+// gemv_dot8 with the lane's activations fetched half a slice at a time (act(i, c):
+// 16-byte chunk c of slice i): the same products summed in the same order per row,
+// with 8 activation and 8 converted-weight registers live instead of 16 and 16.
+template <int kSlices, typename Scale, typename Act>
+__device__ __forceinline__ void gemv_dot8_halves(const uint4 (&q)[kGemvRows][kSlices], Scale scale,
+                                                 Act act, float (&v)[kGemvRows]) {
+#pragma unroll
+  for (int j = 0; j < kGemvRows; ++j) v[j] = 0.f;
+#pragma unroll
+  for (int i = 0; i < kSlices; ++i)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const uint4 ac[2] = {act(i, 2 * hh), act(i, 2 * hh + 1)};
+#pragma unroll
+      for (int j = 0; j < kGemvRows; ++j) {
+        const float sc = e8m0_as_f32(scale(j, i));
+        const uint32_t d[2] = {hh ? q[j][i].z : q[j][i].x, hh ? q[j][i].w : q[j][i].y};
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const uint32_t ad[4] = {ac[c].x, ac[c].y, ac[c].z, ac[c].w};
+          bf16x2 w[4];
+          w[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[c], sc, 0);
+          w[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[c], sc, 1);
+          w[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[c], sc, 2);
+          w[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[c], sc, 3);
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+            v[j] = __builtin_amdgcn_fdot2_f32_bf16(w[m], __builtin_bit_cast(bf16x2, ad[m]), v[j],
+                                                   false);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+}
+
+// W2 with the weighted combine, for the one-call layer on the GEMV path.  A
+// workgroup takes one token t and 32 output columns (a wavefront per group of 8),
+// and first copies the token's k rows of h (rows scatter[t k + j]) into LDS, where
+// its four wavefronts read them.  Each wavefront then runs over the k choices in
+// slot order j: for choice j (expert e = ids[t k + j], sorted row p) it computes
+// y_sorted[p] on its 8 columns exactly as gemv_kernel<false> does (same products in
+// the same order, same reduction) and stores it, and adds w[t k + j] times that
+// bf16 value to the column's fp32 sum, in j order, as the combine kernel does; y[t]
+// is rounded once at the end.  So y and y_sorted are bit-identical to the separate
+// W2 and combine launches, without the combine's launch and its re-read of
+// y_sorted.  The next choice's weight loads go out before the current one is
+// computed; k is a template argument so that the loop unrolls and every wait
+// counts only older loads.  The token's choices sit in lanes 0..k-1 (read once),
+// the scale bytes arrive as two dwords per lane and reach their lanes by a lane
+// permute, and the products take half a slice of activations at a time: about 110
+// VGPRs at K = 2048, four wavefronts per SIMD, so a verify-sized grid (8 tokens x
+// 4096 columns: 4096 wavefronts) is resident at once.
+template <int kSlices, int kTop>
+__global__ __launch_bounds__(256, kSlices == 1 ? 4 : 2) void gemv_w2_combine_kernel(
+    const uint16_t* __restrict__ h, const int32_t* __restrict__ ids,
+    const float* __restrict__ topw, const int32_t* __restrict__ scatter, int T, int E,
+    int n_slots, const uint8_t* __restrict__ wq, const uint8_t* __restrict__ wsc, int n_rows,
+    int blocks_per_token, uint16_t* __restrict__ y_sorted, uint16_t* __restrict__ y,
+    int ld_out) {
+  constexpr int K = kSlices * kGemvSlice;
+  constexpr int kRow16 = K / 8;   // 16-byte words per h row
+  constexpr int k_top = kTop;
+  __shared__ uint4 h_lds[kTop * kRow16];
+  const int t = static_cast<int>(blockIdx.x) / blocks_per_token;
+  if (t >= T) return;   // whole workgroup (before the barrier)
+  const int lane = threadIdx.x & 63;
+  const int g = (static_cast<int>(blockIdx.x) - t * blocks_per_token) * 4 +
+                __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+  const int idx = (lane >> 2) & 7;   // the column a lane holds after the reduction
+  const bool stores = (lane & 0x23) == 0;   // one lane per column
+
+  // the token's k choices, lane j holding choice j: expert, sorted row, weight (an
+  // invalid choice, expert or row out of range, contributes nothing)
+  int lane_e = -1, lane_p = -1;
+  float lane_w = 0.f;
+  if (lane < k_top) {
+    const int64_t s = static_cast<int64_t>(t) * k_top + lane;
+    lane_e = ids[s];
+    lane_p = scatter[s];
+    lane_w = topw[s];
+  }
+  const bool lane_ok = static_cast<unsigned>(lane_e) < static_cast<unsigned>(E) &&
+                       static_cast<unsigned>(lane_p) < static_cast<unsigned>(n_slots);
+  if (!lane_ok) lane_e = -1;
+  auto expert_of = [&](int j) { return __builtin_amdgcn_readlane(lane_e, j); };   // -1: none
+  auto row_of = [&](int j) { return __builtin_amdgcn_readlane(lane_p, j); };
+
+  // Scales: the group's 8 rows x 64 blocks of a slice are read as two dwords per lane
+  // (rows 4m + lane / 16, blocks 4 (lane % 16) .. +3) and each lane's byte (block
+  // lane of row r) is fetched from its holder with a lane permute when used.
+  auto load_w = [&](int e, uint4 (&q)[kGemvRows][kSlices], uint32_t (&sd)[2][kSlices]) {
+    const size_t e_rows = static_cast<size_t>(e >= 0 ? e : 0) * n_rows;
+    const uint8_t* wbase = wq + e_rows * (K / 2) + 16 * lane;
+    const uint8_t* sbase = wsc + e_rows * (K / 32);
+#pragma unroll
+    for (int i = 0; i < kSlices; ++i)
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const size_t row = static_cast<size_t>(kGemvRows * g + 4 * m + (lane >> 4));
+        sd[m][i] = *reinterpret_cast<const uint32_t*>(sbase + row * (K / 32) + 64 * i +
+                                                      4 * (lane & 15));
+      }
+#pragma unroll
+    for (int i = 0; i < kSlices; ++i)
+#pragma unroll
+      for (int jj = 0; jj < kGemvRows; ++jj) {
+        const size_t row = static_cast<size_t>(kGemvRows * g + jj);
+        q[jj][i] = load_nt(wbase + row * (K / 2) + 1024 * i);
+      }
+  };
+  const int byte_shift = 8 * (lane & 3);
+  auto scale_byte = [&](const uint32_t (&sd)[2][kSlices], int r, int i) -> uint32_t {
+    const int holder = 16 * (r & 3) + (lane >> 2);
+    const uint32_t d = static_cast<uint32_t>(
+        __builtin_amdgcn_ds_bpermute(4 * holder, static_cast<int>(sd[r >> 2][i])));
+    return (d >> byte_shift) & 0xFFu;
+  };
+  float acc = 0.f;
+  auto finish = [&](int j, const uint4 (&q)[kGemvRows][kSlices], const uint32_t (&sd)[2][kSlices]) {
+    const uint4* src = h_lds + j * kRow16 + 4 * lane;
+    float v[kGemvRows];
+    gemv_dot8_halves<kSlices>(
+        q, [&](int r, int i) { return scale_byte(sd, r, i); },
+        [&](int i, int c) { return src[i * (kGemvSlice / 8) + c]; }, v);
+    const float sum = gemv_reduce8(v, lane);
+    if (expert_of(j) < 0) return;   // uniform over the wavefront
+    const uint16_t b = f32_to_bf16_bits(sum);
+    const float w = __builtin_bit_cast(
+        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lane_w), j));
+    acc = fmaf(w, bf16_bits_to_f32(b), acc);
+    if (stores) y_sorted[static_cast<int64_t>(row_of(j)) * ld_out + kGemvRows * g + idx] = b;
+  };
+
+  // the token's k rows of h (zeros for an invalid choice) into LDS, their loads
+  // issued ahead of the first two choices' weight loads
+  uint4 st[kTop][kRow16 / 256];
+#pragma unroll
+  for (int j = 0; j < k_top; ++j) {
+    const int row = expert_of(j) >= 0 ? row_of(j) : 0;
+    const uint4* src = reinterpret_cast<const uint4*>(h + static_cast<int64_t>(row) * K);
+#pragma unroll
+    for (int c = 0; c < kRow16 / 256; ++c) st[j][c] = src[256 * c + threadIdx.x];
+  }
+  uint4 qa[kGemvRows][kSlices], qb[kGemvRows][kSlices];
+  uint32_t sa[2][kSlices], sbb[2][kSlices];
+  load_w(expert_of(0), qa, sa);
+  if (k_top > 1) load_w(expert_of(1), qb, sbb);
+#pragma unroll
+  for (int j = 0; j < k_top; ++j) {
+    const bool ok = expert_of(j) >= 0;
+#pragma unroll
+    for (int c = 0; c < kRow16 / 256; ++c)
+      h_lds[j * kRow16 + 256 * c + threadIdx.x] = ok ? st[j][c] : make_uint4(0u, 0u, 0u, 0u);
+  }
+  __syncthreads();
+  // choice j computed while choice j + 1's loads are in flight (k is a template
+  // argument so that the loop unrolls and every wait counts only older loads)
+#pragma unroll
+  for (int j = 0; j < k_top; ++j) {
+    if (j % 2 == 0) {
+      finish(j, qa, sa);
+      if (j + 2 < k_top) load_w(expert_of(j + 2), qa, sa);
+    } else {
+      finish(j, qb, sbb);
+      if (j + 2 < k_top) load_w(expert_of(j + 2), qb, sbb);
+    }
+  }
+  if (stores)
+    y[static_cast<int64_t>(t) * ld_out + kGemvRows * g + idx] = f32_to_bf16_bits(acc);
 }
 
 template <bool kW1, int kSlices>
@@ -269,6 +463,56 @@ hipError_t launch_gemv(bool w1, int64_t tile_bound, hipStream_t stream, const ui
                                        n_tiles, n_rows, half, groups, w, limit, clamp, out, ld_out)
              : launch_gemv_t<false, 1>(grid, stream, act, gather, k_top, n_slots, wq, wsc, tiles,
                                        n_tiles, n_rows, half, groups, w, limit, clamp, out, ld_out);
+}
+
+namespace {
+
+template <int kSlices, int kTop>
+void launch_w2c(unsigned grid, hipStream_t stream, const uint16_t* h, const int32_t* ids,
+                const float* topw, const int32_t* scatter, int T, int E, int n_slots,
+                const uint8_t* wq, const uint8_t* wsc, int n_rows, int per_token,
+                uint16_t* y_sorted, uint16_t* y) {
+  gemv_w2_combine_kernel<kSlices, kTop><<<grid, 256, 0, stream>>>(
+      h, ids, topw, scatter, T, E, n_slots, wq, wsc, n_rows, per_token, y_sorted, y, n_rows);
+}
+
+template <int kSlices>
+void launch_w2c_k(int k_top, unsigned grid, hipStream_t stream, const uint16_t* h,
+                  const int32_t* ids, const float* topw, const int32_t* scatter, int T, int E,
+                  int n_slots, const uint8_t* wq, const uint8_t* wsc, int n_rows, int per_token,
+                  uint16_t* y_sorted, uint16_t* y) {
+#define MOE_W2C(KT)                                                                          \
+  case KT:                                                                                   \
+    launch_w2c<kSlices, KT>(grid, stream, h, ids, topw, scatter, T, E, n_slots, wq, wsc,     \
+                            n_rows, per_token, y_sorted, y);                                 \
+    break;
+  switch (k_top) {
+    MOE_W2C(1) MOE_W2C(2) MOE_W2C(3) MOE_W2C(4) MOE_W2C(5) MOE_W2C(6) MOE_W2C(7) MOE_W2C(8)
+  }
+#undef MOE_W2C
+}
+
+}  // namespace
+
+hipError_t launch_gemv_w2_combine(int64_t T, int k_top, int E, int n_slots, hipStream_t stream,
+                                  const uint16_t* h, const int32_t* ids, const float* topw,
+                                  const int32_t* scatter, const uint8_t* wq, const uint8_t* wsc,
+                                  int K, int n_rows, uint16_t* y_sorted, uint16_t* y) {
+  static_assert(kMaxK == 8, "one instantiation per k");
+  if (k_top < 1 || k_top > kMaxK) return hipErrorInvalidValue;
+  // four wavefronts (32 columns) per workgroup; the token's k rows of h in LDS
+  // (at most 8 rows of 8 KB)
+  const int per_token = n_rows / (4 * kGemvRows);
+  const unsigned grid = static_cast<unsigned>(T * per_token);
+  if (grid == 0) return hipSuccess;
+  const int t = static_cast<int>(T);
+  if (K == 2 * kGemvSlice)
+    launch_w2c_k<2>(k_top, grid, stream, h, ids, topw, scatter, t, E, n_slots, wq, wsc, n_rows,
+                    per_token, y_sorted, y);
+  else
+    launch_w2c_k<1>(k_top, grid, stream, h, ids, topw, scatter, t, E, n_slots, wq, wsc, n_rows,
+                    per_token, y_sorted, y);
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -26,13 +26,25 @@ hipError_t launch_offsets(const uint32_t* bm, const int32_t* ids, int64_t T, int
 
 struct WsLayout;
 
-// The grouped FFN; `L` is the workspace layout for these sizes (validate.h).
+// The weighted combine's inputs and output, for an FFN launch that may fold the
+// combine into its W2 step.
+struct CombineArgs {
+  const int32_t* topk_ids;
+  const float* topk_weights;
+  const int32_t* scatter;
+  uint16_t* y;
+};
+
+// The grouped FFN; `L` is the workspace layout for these sizes (validate.h).  With
+// `combine` set, the decode GEMV path (one-row tiles) also writes the combined y
+// from its W2 step and sets *combined; other paths leave the combine to the caller.
 hipError_t launch_ffn(const uint16_t* x, int64_t T, int H, int I, int E, int k,
                       const uint8_t* w1, const uint8_t* w1s, const uint8_t* w2,
                       const uint8_t* w2s, const int32_t* counts, const int32_t* offsets,
                       const int32_t* gather, float limit, uint16_t* y_sorted, void* ws,
                       const WsLayout& L, hipStream_t stream, hipEvent_t const* events = nullptr,
-                      bool plan_ready = false);
+                      bool plan_ready = false, const CombineArgs* combine = nullptr,
+                      bool* combined = nullptr);
 
 // Where the one-launch front-end also writes the FFN's row-tile plan (count, then
 // the tile list; see ffn.hip).
@@ -83,6 +95,7 @@ moe_status forward_layer(const float* logits, const uint16_t* x, int64_t T, int3
                          const uint8_t* w2, const uint8_t* w2_scale, float swiglu_limit,
                          int32_t* topk_ids, float* topk_weights, uint32_t* bitmatrix,
                          int32_t* counts, int32_t* offsets, int32_t* gather, int32_t* scatter,
-                         uint16_t* y_sorted, uint16_t* y, void* ws, hipStream_t st);
+                         uint16_t* y_sorted, uint16_t* y, void* ws, hipStream_t st,
+                         hipEvent_t const* events = nullptr);
 
 }  // namespace moe

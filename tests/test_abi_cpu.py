@@ -34,7 +34,8 @@ def test_header_declares_the_five_calls():
     names = declared_functions()
     for n in ("moe_route", "moe_build_bitmatrix", "moe_expert_offsets", "moe_route_and_group",
               "moe_grouped_ffn_mxfp4", "moe_combine", "moe_workspace_bytes", "moe_status_string",
-              "moe_grouped_ffn_mxfp4_timed", "moe_forward_mxfp4", "moe_read_probe"):
+              "moe_grouped_ffn_mxfp4_timed", "moe_forward_mxfp4", "moe_forward_mxfp4_timed",
+              "moe_read_probe"):
         assert n in names
 
 
@@ -91,6 +92,17 @@ def test_error_codes_through_the_abi(lib):
     assert fwd(16, 4100, 2048, 256, 6, nulls, 0) == INVALID          # nulls are checked first
     assert fwd(-1, 4096, 2048, 256, 6, nulls, 0) == INVALID
     assert fwd(16, 4096, 2048, 256, 9, nulls, 0) == UNSUPPORTED      # k > 8
+    # the timed one-call layer: the same checks, then its three events
+    lib.moe_forward_mxfp4_timed.argtypes = lib.moe_forward_mxfp4.argtypes[:-1] + [P, P]
+    ws = lib.moe_workspace_bytes(16, 256, 6, 4096, 2048)
+    fake = [4096] * 16   # aligned stand-in device pointers: never dereferenced by the checks
+    timed = lambda T, ptrs, ws_bytes, ev: lib.moe_forward_mxfp4_timed(
+        *ptrs[:2], T, 4096, 2048, 256, 6, *ptrs[2:6], 10.0, *ptrs[6:16], ws_bytes, ev, None)
+    no_events = (ctypes.c_void_p * 3)(None, None, None)
+    assert timed(16, nulls, 0, None) == INVALID                       # null pointers first
+    assert timed(16, fake, ws - 1, None) == WS_SMALL
+    assert timed(16, fake, ws, None) == INVALID                       # no event array
+    assert timed(16, fake, ws, no_events) == INVALID                  # null events
 
 
 def test_noalloc_entry_point_host_checks(lib):
