@@ -104,6 +104,10 @@ __device__ __forceinline__ float swiglu(float g, float u, float limit, bool clam
 // experts x 4096 rows of 2 KB, 12 wavefronts per CU): 5,888 wavefronts of 32 rows
 // read the 377 MB in 66.7 us against 73.2 us for 2,944 wavefronts of 64 rows.
 constexpr int kStreamFrags16 = 2;
+// 32-row streaming tiles: LDS per wavefront for the weight transit (two 16-row
+// fragments x 128 bytes), and the weight loads' cache-policy operand
+constexpr size_t kStreamTransitBytes = 4096;
+constexpr int kStreamWeightAux = 2;   // non-temporal
 inline int stream_frags(int msub) { return msub == 1 ? kStreamFrags16 : 4; }
 
 // A K chunk is 128 elements: 64 bytes of codes and 4 scale bytes per weight row.

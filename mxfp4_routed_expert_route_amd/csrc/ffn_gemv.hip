@@ -35,10 +35,11 @@ namespace {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kGemvRows = 8;         // weight rows per wavefront
+constexpr int kGemvNt = 2;           // cache-policy operand of a buffer load: non-temporal
 constexpr int kGemvSlice = 2048;     // K elements per 1 KB row slice (64 lanes x 32)
-// wavefronts per launch: with two resident per SIMD, six rounds of them (measured on
-// the verify step's W1 / W2: 2,048 wavefronts 70.6 / 39.0 us, 3,072 68.3 / 36.9,
-// 12,288 67.3 / 34.8, 24,576 -- one group each -- 75.3 / 35.6)
+// wavefronts per launch, at most: with two resident per SIMD, six rounds of them
+// (measured on the verify step's W1 / W2: 2,048 wavefronts 70.6 / 39.0 us, 3,072
+// 68.3 / 36.9, 12,288 67.3 / 34.8, 24,576 -- one group each -- 75.3 / 35.6)
 constexpr int kGemvMaxWaves = 12288;
 
 __device__ __forceinline__ uint4 load_nt(const uint8_t* p) {
@@ -85,6 +86,17 @@ __device__ __forceinline__ float dot32(const bf16x2 (&w)[16], const uint4 (&a)[4
                                             false);
   }
   return acc;
+}
+
+// The E8M0 scale byte of row j (0..7) of a group for this lane (block `lane` of the
+// slice), from the dword pair a group's scales are read in: the dword of rows
+// 4 (j / 4) + lane / 16 holds blocks 4 (lane % 16) .. +3, so row j's block `lane` is
+// byte lane % 4 of lane 16 (j % 4) + lane / 4's dword `sd` (the one for j / 4).
+__device__ __forceinline__ uint32_t gemv_scale_byte(uint32_t sd, int j, int lane) {
+  const int holder = 16 * (j & 3) + (lane >> 2);
+  const uint32_t d =
+      static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(4 * holder, static_cast<int>(sd)));
+  return (d >> (8 * (lane & 3))) & 0xFFu;
 }
 
 // The 8 row sums of a group: v[j] = sum over the lane's elements of row j's
@@ -141,19 +153,15 @@ __device__ __forceinline__ float gemv_reduce8(float (&v)[kGemvRows], int lane) {
   return sum + __shfl_xor(sum, 32, 64);
 }
 
-// The lane's activations of a K-row: slice i, elements 2048 i + 32 lane .. +31
-// (zeros for an invalid row)
+// The lane's activations of a K-row: slice i, elements 2048 i + 32 lane .. +31.
 template <int kSlices>
-__device__ __forceinline__ void gemv_load_act(const uint16_t* row_base, bool valid, int lane,
+__device__ __forceinline__ void gemv_load_act(const uint16_t* row_base, int lane,
                                               uint4 (&a)[kSlices][4]) {
   const uint4* src = reinterpret_cast<const uint4*>(row_base + 32 * lane);
 #pragma unroll
   for (int i = 0; i < kSlices; ++i)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const uint4 d = src[i * (kGemvSlice / 8) + c];
-      a[i][c] = valid ? d : make_uint4(0u, 0u, 0u, 0u);
-    }
+    for (int c = 0; c < 4; ++c) a[i][c] = src[i * (kGemvSlice / 8) + c];
 }
 
 // Each row tile (one row) gets `wpt` wavefronts; wavefront w of a tile owns the
@@ -181,32 +189,51 @@ __global__ __launch_bounds__(256) void gemv_kernel(
   const int p = __builtin_amdgcn_readfirstlane(rt.p_begin);   // the tile's one row
   const int expert = __builtin_amdgcn_readfirstlane(rt.expert);
 
+  // the expert's codes and scales as buffer resources: each load below is a scalar
+  // row offset plus the lane's 32-bit offset (no 64-bit address arithmetic per lane)
   const size_t e_rows = static_cast<size_t>(expert) * n_rows;
-  const uint8_t* wbase = wq + e_rows * (K / 2) + 16 * lane;
-  const uint8_t* sbase = wsc + e_rows * (K / 32) + lane;
+  const __amdgpu_buffer_rsrc_t wrs =
+      make_rsrc(wq + e_rows * (K / 2), static_cast<uint32_t>(n_rows) * (K / 2));
+  const __amdgpu_buffer_rsrc_t srs =
+      make_rsrc(wsc + e_rows * (K / 32), static_cast<uint32_t>(n_rows) * (K / 32));
+  const int lane16 = 16 * lane;
+  const int lane_s = (lane >> 4) * (K / 32) + 4 * (lane & 15);
   // weight row j of group g (W1: j < 4 gate rows 4 g + j, j >= 4 the matching up
   // rows; W2: output rows 8 g + j)
   auto wrow = [&](int g, int j) {
     return kW1 ? (j < 4 ? 4 * g + j : half + 4 * g + (j - 4)) : kGemvRows * g + j;
   };
-  auto load_group = [&](int g, uint4 (&q)[kGemvRows][kSlices],
-                        uint32_t (&sb)[kGemvRows][kSlices]) {
+  // A group's codes: one 1 KB load per row and slice, non-temporal.  Its scales: two
+  // dwords per lane and slice (rows wrow(g, 4m + lane / 16), blocks 4 (lane % 16) ..
+  // +3 of the slice), from which each lane takes its byte (block `lane` of row j)
+  // with a lane permute when it is used.
+  auto load_group = [&](int g, uint4 (&q)[kGemvRows][kSlices], uint32_t (&sd)[2][kSlices]) {
 #pragma unroll
     for (int i = 0; i < kSlices; ++i)
 #pragma unroll
-      for (int j = 0; j < kGemvRows; ++j) {
-        const size_t row = static_cast<size_t>(wrow(g, j));
-        q[j][i] = load_nt(wbase + row * (K / 2) + 1024 * i);
-        sb[j][i] = sbase[row * (K / 32) + 64 * i];
-      }
+      for (int m = 0; m < 2; ++m)
+        sd[m][i] = __builtin_amdgcn_raw_buffer_load_b32(
+            srs, lane_s + 64 * i, __builtin_amdgcn_readfirstlane(wrow(g, 4 * m) * (K / 32)), 0);
+#pragma unroll
+    for (int i = 0; i < kSlices; ++i)
+#pragma unroll
+      for (int j = 0; j < kGemvRows; ++j)
+        q[j][i] = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                       wrs, lane16 + 1024 * i,
+                       __builtin_amdgcn_readfirstlane(wrow(g, j) * (K / 2)), kGemvNt));
+    // keep the loads where they stand: hoisted into the previous group's products
+    // they would hold a third register set
+    __builtin_amdgcn_sched_barrier(0);
   };
   uint4 a[kSlices][4];   // the lane's activations (filled below)
   const int idx = (lane >> 2) & 7;   // the row whose sum a lane holds after the reduction
-  // group g from q / sb: products, reduction over the lanes, epilogue
+  // group g from q / sd: products, reduction over the lanes, epilogue
   auto finish_group = [&](int g, const uint4 (&q)[kGemvRows][kSlices],
-                          const uint32_t (&sb)[kGemvRows][kSlices]) {
+                          const uint32_t (&sd)[2][kSlices]) {
     float v[kGemvRows];
-    gemv_dot8<kSlices>(q, [&](int j, int i) { return sb[j][i]; }, a, v);
+    gemv_dot8<kSlices>(q, [&](int j, int i) { return gemv_scale_byte(sd[j >> 2][i], j, lane); },
+                       a, v);
     const float sum = gemv_reduce8(v, lane);
     if (kW1) {
       // gate rows are rows 0..3 (lane bit 4 clear), their up rows 4..7 (lane ^ 16)
@@ -219,38 +246,37 @@ __global__ __launch_bounds__(256) void gemv_kernel(
     }
   };
 
-  // two register sets: the next group's loads are issued before the current group
-  // is computed.  The first group's loads go out before the activation row's
-  // (which wait on the gather index).
+  // Two register sets: the next group's loads are issued before the current group
+  // is computed.  The wavefront's groups are w_in + r wpt, r < groups / wpt (an even
+  // count), so every load is issued on every path (no load sits under a branch,
+  // which would make the compiler's later waits count as if it had not been taken)
+  // and each wait counts only older loads.  The first group's loads go out before
+  // the activation row's (which wait on the gather index).
   uint4 qa[kGemvRows][kSlices], qb[kGemvRows][kSlices];
-  uint32_t sa[kGemvRows][kSlices], sbb[kGemvRows][kSlices];
+  uint32_t sa[2][kSlices], sbb[2][kSlices];
   int g = w_in;
   load_group(g, qa, sa);
-
-  // the lane's activations of the tile's row
   {
+    // W1: the tile row's token.  gather comes from moe_expert_offsets; an entry out
+    // of range (outside that contract) reads token 0 instead, so that the loads stay
+    // in bounds and unconditional (its h row is then unspecified).
     int64_t row = p;
-    bool valid = true;
     if (kW1) {
       const int slot = __builtin_amdgcn_readfirstlane(gather[p]);
-      valid = static_cast<unsigned>(slot) < static_cast<unsigned>(n_slots);
-      row = valid ? slot / k_top : 0;
+      row = static_cast<unsigned>(slot) < static_cast<unsigned>(n_slots) ? slot / k_top : 0;
     }
-    gemv_load_act<kSlices>(act + row * K, valid, lane, a);
+    gemv_load_act<kSlices>(act + row * K, lane, a);
   }
-
 #pragma unroll 1
   for (;;) {
-    const int g1 = g + wpt;
-    if (g1 < groups) load_group(g1, qb, sbb);
+    load_group(g + wpt, qb, sbb);
     finish_group(g, qa, sa);
-    if (g1 >= groups) break;
-    const int g2 = g1 + wpt;
-    if (g2 < groups) load_group(g2, qa, sa);
-    finish_group(g1, qb, sbb);
-    if (g2 >= groups) break;
-    g = g2;
+    if (g + 2 * wpt >= groups) break;
+    load_group(g + 2 * wpt, qa, sa);
+    finish_group(g + wpt, qb, sbb);
+    g += 2 * wpt;
   }
+  finish_group(g + wpt, qb, sbb);
 }
 
 // gemv_dot8 with the lane's activations fetched half a slice at a time (act(i, c):
@@ -363,19 +389,12 @@ __global__ __launch_bounds__(256, kSlices == 1 ? 4 : 2) void gemv_w2_combine_ker
         q[jj][i] = load_nt(wbase + row * (K / 2) + 1024 * i);
       }
   };
-  const int byte_shift = 8 * (lane & 3);
-  auto scale_byte = [&](const uint32_t (&sd)[2][kSlices], int r, int i) -> uint32_t {
-    const int holder = 16 * (r & 3) + (lane >> 2);
-    const uint32_t d = static_cast<uint32_t>(
-        __builtin_amdgcn_ds_bpermute(4 * holder, static_cast<int>(sd[r >> 2][i])));
-    return (d >> byte_shift) & 0xFFu;
-  };
   float acc = 0.f;
   auto finish = [&](int j, const uint4 (&q)[kGemvRows][kSlices], const uint32_t (&sd)[2][kSlices]) {
     const uint4* src = h_lds + j * kRow16 + 4 * lane;
     float v[kGemvRows];
     gemv_dot8_halves<kSlices>(
-        q, [&](int r, int i) { return scale_byte(sd, r, i); },
+        q, [&](int r, int i) { return gemv_scale_byte(sd[r >> 2][i], r, lane); },
         [&](int i, int c) { return src[i * (kGemvSlice / 8) + c]; }, v);
     const float sum = gemv_reduce8(v, lane);
     if (expert_of(j) < 0) return;   // uniform over the wavefront
@@ -442,13 +461,17 @@ hipError_t launch_gemv(bool w1, int64_t tile_bound, hipStream_t stream, const ui
                        const int32_t* gather, int k_top, int n_slots, const uint8_t* wq,
                        const uint8_t* wsc, const RowTile* tiles, const int32_t* n_tiles, int K,
                        int n_rows, int half, float limit, int clamp, uint16_t* out, int ld_out) {
-  // groups of 8 weight rows per tile (W1: 4 gate rows and their up rows), and
-  // wavefronts per tile: kGemvMaxWaves over the possible tiles, a multiple of 4 so
-  // a workgroup's wavefronts share a tile, at most one per group
+  // groups of 8 weight rows per tile (W1: 4 gate rows and their up rows; a power of
+  // two, 256 to 1024, at the GEMV sizes), and wavefronts per tile: the largest power
+  // of two within kGemvMaxWaves over the possible tiles and within half the groups
+  // (at least 4: a workgroup's wavefronts share a tile), so that every wavefront
+  // gets an even number of groups
   const int groups = w1 ? half / 4 : n_rows / kGemvRows;
-  int64_t wpt = kGemvMaxWaves / (tile_bound > 0 ? tile_bound : 1);
-  wpt = wpt < 4 ? 4 : wpt / 4 * 4;
-  if (wpt > groups) wpt = (groups + 3) / 4 * 4;
+  if (groups < 8 || (groups & (groups - 1)) != 0) return hipErrorInvalidValue;
+  int64_t wpt_max = kGemvMaxWaves / (tile_bound > 0 ? tile_bound : 1);
+  if (wpt_max > groups / 2) wpt_max = groups / 2;   // two groups or more per wavefront
+  int64_t wpt = 4;
+  while (wpt * 2 <= wpt_max) wpt *= 2;
   const int64_t waves = tile_bound * wpt;
   const unsigned grid = static_cast<unsigned>((waves + 3) / 4);
   if (grid == 0) return hipSuccess;

@@ -17,8 +17,11 @@ namespace {
 // elements: each lane takes 32 bytes (two scale blocks) of each of its kFrag
 // rows, so a weight row is visited 128 bytes at a time -- measured on MI355X,
 // 128-byte visits of this many concurrent rows stream about 20% faster than
-// 64-byte ones.  Two register stages of weights: the next chunk streams in while
-// this one computes.  The E8M0 scales of the wavefront's 16*kFrag rows are staged
+// 64-byte ones.  With 32-row tiles the loads themselves read 8 rows x 128
+// contiguous bytes each (non-temporal) and the chunk reaches the MFMA layout
+// through 4 KB of LDS per wavefront (the burst step: W1 406 -> 385 us, W2 225 ->
+// 217-221 us, bit-identical).  Two register stages of weights: the next chunk
+// streams in while this one computes.  The E8M0 scales of the wavefront's 16*kFrag rows are staged
 // in LDS once, laid out so that one (two fragments) or two (four) 16-byte LDS
 // reads per chunk give a lane the scales of its rows; they never enter the
 // vector-memory queue.  Activations take one of
@@ -44,7 +47,7 @@ void gemm_stream_kernel(
     int k_top, int n_slots, const uint8_t* __restrict__ wq, const uint8_t* __restrict__ wsc,
     const RowTile* __restrict__ tiles, const int32_t* __restrict__ n_tiles, int K, int n_rows,
     int half, int waves_per_tile, float limit, int clamp, uint16_t* __restrict__ out,
-    int ld_out, int a_lds_rows, int a_ring) {
+    int ld_out, int a_lds_rows, int a_ring, int wt_off) {
   // kDeep: per wavefront [K/128][16][4] dwords of scales; after the four
   // wavefronts' scales, either a_lds_rows activation rows of K bf16 and a
   // 512-byte zero block, or the ring (two slots of 16*MSUB rows of 512 bytes)
@@ -244,12 +247,77 @@ void gemm_stream_kernel(
     // 256-element chunks, two weight register stages; `run` is the K loop for the
     // LDS-held rows and the per-wavefront activation loads, `run_ring` for the ring.
     const int n2 = n_chunks / 2;   // 256-element chunks (even: n_chunks % 4 == 0)
-    auto load_w2 = [&](uint4 (&q)[kFrag][2], int c2) {
+    // 32-row tiles: each weight load instruction reads 8 rows x 128 contiguous bytes
+    // (lane l: row 8h + l/8 of fragment f, bytes 16 (l%8) .. +15 of the chunk), and
+    // the wavefront moves the chunk through LDS into the MFMA layout (transit).
+    // Measured on MI355X with a read-only probe of W2's bytes (1 GiB, 64 rows per
+    // wavefront, eight loads in flight): this pattern reads 6.9 TB/s, the MFMA
+    // layout's own pattern (16 rows x 4 runs of 16 bytes per instruction) 5.6.
+    constexpr bool kR8 = MSUB == 2;
+    // (the expert made visibly wavefront-uniform: a scalar resource, no per-load loop)
+    const size_t e_rows_u =
+        static_cast<size_t>(__builtin_amdgcn_readfirstlane(rt.expert)) * n_rows;
+    const __amdgpu_buffer_rsrc_t wrs =
+        make_rsrc(wq + e_rows_u * row_q, static_cast<uint32_t>(n_rows * row_q));
+    uint32_t r8off[kFrag][2];
 #pragma unroll
-      for (int f = 0; f < kFrag; ++f) {
-        const uint8_t* src = bq[f] + c2 * 128 + 32 * g;   // lane group g: bytes 32g..32g+31
-        q[f][0] = *reinterpret_cast<const uint4*>(src);
-        q[f][1] = *reinterpret_cast<const uint4*>(src + 16);
+    for (int f = 0; f < kFrag; ++f)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        r8off[f][h] = static_cast<uint32_t>(wrow(f, 8 * h + (lane >> 3))) *
+                          static_cast<uint32_t>(row_q) + 16u * (lane & 7);
+    auto load_w2 = [&](uint4 (&q)[kFrag][2], int c2) {
+      if constexpr (kR8) {
+#pragma unroll
+        for (int f = 0; f < kFrag; ++f)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            q[f][h] = __builtin_bit_cast(
+                uint4, __builtin_amdgcn_raw_buffer_load_b128(wrs, r8off[f][h], c2 * 128,
+                                                             kStreamWeightAux));
+      } else {
+#pragma unroll
+        for (int f = 0; f < kFrag; ++f) {
+          const uint8_t* src = bq[f] + c2 * 128 + 32 * g;   // lane group g: bytes 32g..32g+31
+          q[f][0] = *reinterpret_cast<const uint4*>(src);
+          q[f][1] = *reinterpret_cast<const uint4*>(src + 16);
+        }
+      }
+    };
+    // Transit of one chunk, two fragments at a time through the wavefront's 4 KB of
+    // LDS: row r's 16-byte block b (of 8) of fragment pair member m sits in 256-byte
+    // line 8m + r/2 at quad 8 (r%2) + (b ^ r/2), so the stores (8 lanes: one row's 8
+    // blocks) and the loads (16 lanes: rows 0..15, one block each) each touch
+    // distinct quads.  LDS operations of a wavefront execute in order, so the loads
+    // see the stores and the next stores follow the loads; the empty asm statements
+    // keep the compiler from moving them across each other.
+    unsigned char* wt = reinterpret_cast<unsigned char*>(scale_lds) + wt_off +
+                        (threadIdx.x >> 6) * kStreamTransitBytes;
+    uint32_t wt_st[2], wt_ld[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = 8 * h + (lane >> 3), b = lane & 7;
+      wt_st[h] = static_cast<uint32_t>((r >> 1) * 256 + ((r & 1) * 8 + (b ^ (r >> 1))) * 16);
+      const int bj = 2 * g + h;   // the MFMA layout: row r16, blocks 2g and 2g + 1
+      wt_ld[h] = static_cast<uint32_t>((r16 >> 1) * 256 + ((r16 & 1) * 8 + (bj ^ (r16 >> 1))) * 16);
+    }
+    auto transit = [&](uint4 (&q)[kFrag][2]) __attribute__((always_inline)) {
+      if constexpr (kR8) {
+#pragma unroll
+        for (int fp = 0; fp < kFrag; fp += 2) {
+#pragma unroll
+          for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+              *reinterpret_cast<uint4*>(wt + m * 2048 + wt_st[h]) = q[fp + m][h];
+          asm volatile("" ::: "memory");
+#pragma unroll
+          for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+              q[fp + m][j] = *reinterpret_cast<const uint4*>(wt + m * 2048 + wt_ld[j]);
+          asm volatile("" ::: "memory");
+        }
       }
     };
     auto load_a2 = [&](bf16x8 (&a)[MSUB][8], int c2) {
@@ -309,6 +377,7 @@ void gemm_stream_kernel(
     __builtin_amdgcn_sched_barrier(0);        \
     load_w2(Q_NEXT, KQ);                      \
     __builtin_amdgcn_sched_barrier(0);        \
+    transit(Q_CUR);                           \
     compute2(Q_CUR, a, KC);                   \
     __builtin_amdgcn_sched_barrier(0);        \
   }
@@ -326,45 +395,45 @@ void gemm_stream_kernel(
     // of each lane's row) sit at bank quad r ^ t, a function of the row alone, and
     // eight consecutive lanes storing one row's pieces hit distinct quads (the
     // tiled kernel's activation layout states the measured rule).
-    auto run_ring = [&]() __attribute__((always_inline)) {
-      constexpr int kRR = 16 * MSUB, kSlot = 32 * kRR * 16;
-      constexpr int kTpr = 16 / MSUB, kPc = 2 * MSUB;   // threads per row, pieces per thread
-      const int sr = threadIdx.x / kTpr, sp = threadIdx.x % kTpr;
-      uint32_t srow = kRsrcOutOfRange;
-      {
-        const int p = rt.p_begin + sr;
-        if (p < rt.p_end) {
-          if (kW1) {
-            const int slot = gather[p];
-            if (static_cast<unsigned>(slot) < static_cast<unsigned>(n_slots))
-              srow = static_cast<uint32_t>(slot / k_top) * static_cast<uint32_t>(K) * 2u;
-          } else {
-            srow = static_cast<uint32_t>(p) * static_cast<uint32_t>(K) * 2u;
-          }
+    constexpr int kRR = 16 * MSUB, kSlot = 32 * kRR * 16;
+    constexpr int kTpr = 16 / MSUB, kPc = 2 * MSUB;   // threads per row, pieces per thread
+    const int sr = threadIdx.x / kTpr, sp = threadIdx.x % kTpr;
+    uint32_t srow = kRsrcOutOfRange;
+    {
+      const int p = rt.p_begin + sr;
+      if (p < rt.p_end) {
+        if (kW1) {
+          const int slot = gather[p];
+          if (static_cast<unsigned>(slot) < static_cast<unsigned>(n_slots))
+            srow = static_cast<uint32_t>(slot / k_top) * static_cast<uint32_t>(K) * 2u;
+        } else {
+          srow = static_cast<uint32_t>(p) * static_cast<uint32_t>(K) * 2u;
         }
       }
-      auto stage_load = [&](uint4 (&r)[kPc], int c2) __attribute__((always_inline)) {
+    }
+    auto stage_load = [&](uint4 (&r)[kPc], int c2) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < kPc; ++i)
-          r[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                               arsrc, srow + 16 * (sp + kTpr * i), c2 * 512, 0));
-      };
-      auto stage_store = [&](const uint4 (&r)[kPc], int slot) __attribute__((always_inline)) {
-        // piece sp + kTpr * i of row sr; kTpr is a multiple of 8, so the row XOR is sp & 7
-        unsigned char* d = a_lds + slot * kSlot + (sp * kRR + (sr ^ (sp & 7))) * 16;
+      for (int i = 0; i < kPc; ++i)
+        r[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             arsrc, srow + 16 * (sp + kTpr * i), c2 * 512, 0));
+    };
+    auto stage_store = [&](const uint4 (&r)[kPc], int slot) __attribute__((always_inline)) {
+      // piece sp + kTpr * i of row sr; kTpr is a multiple of 8, so the row XOR is sp & 7
+      unsigned char* d = a_lds + slot * kSlot + (sp * kRR + (sr ^ (sp & 7))) * 16;
 #pragma unroll
-        for (int i = 0; i < kPc; ++i) *reinterpret_cast<uint4*>(d + kTpr * i * kRR * 16) = r[i];
-      };
-      auto read_a = [&](bf16x8 (&a)[MSUB][8], int c2) __attribute__((always_inline)) {
-        const unsigned char* base = a_lds + (c2 & 1) * kSlot;
+      for (int i = 0; i < kPc; ++i) *reinterpret_cast<uint4*>(d + kTpr * i * kRR * 16) = r[i];
+    };
+    auto read_a = [&](bf16x8 (&a)[MSUB][8], int c2) __attribute__((always_inline)) {
+      const unsigned char* base = a_lds + (c2 & 1) * kSlot;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const int off = ((8 * g + t) * kRR + (r16 ^ t)) * 16;   // piece 8g + t
+      for (int t = 0; t < 8; ++t) {
+        const int off = ((8 * g + t) * kRR + (r16 ^ t)) * 16;   // piece 8g + t
 #pragma unroll
-          for (int mi = 0; mi < MSUB; ++mi)
-            a[mi][t] = *reinterpret_cast<const bf16x8*>(base + off + mi * 256);
-        }
-      };
+        for (int mi = 0; mi < MSUB; ++mi)
+          a[mi][t] = *reinterpret_cast<const bf16x8*>(base + off + mi * 256);
+      }
+    };
+    auto run_ring = [&]() __attribute__((always_inline)) {
       uint4 sa[kPc];
       uint4 q0[kFrag][2], q1[kFrag][2];
       stage_load(sa, 0);
@@ -380,6 +449,7 @@ void gemm_stream_kernel(
   {                                                           \
     load_w2(Q_NEXT, KQ);                                      \
     __builtin_amdgcn_sched_barrier(0);                        \
+    transit(Q_CUR);                                           \
     bf16x8 a[MSUB][8];                                        \
     read_a(a, KC);                                            \
     compute2(Q_CUR, a, KC);                                   \
@@ -476,18 +546,20 @@ hipError_t launch_stream_t(unsigned grid, hipStream_t stream, const uint16_t* ac
   size_t a_bytes = a_rows > 0 ? static_cast<size_t>(a_rows) * K * 2 + 512 : 0;
   // the ring: two chunks of 16*MSUB padded rows, within the workgroup's share of
   // LDS
+  // 32-row tiles: the weight transit, 4 KB per wavefront, after the activations
+  const size_t wt_bytes = MSUB == 2 ? 4 * kStreamTransitBytes : 0;
   const size_t ring_bytes = 2 * 16 * MSUB * 512;
-  const size_t budget = max_lds;
+  const size_t budget = max_lds - wt_bytes;
   const int a_ring = wpt % 4 == 0 && lds + ring_bytes <= budget ? 1 : 0;
   if (a_ring && ring_bytes > a_bytes) a_bytes = ring_bytes;
   if (n_chunks % 4 == 0 && lds <= kStreamMaxScaleLds)
-    gemm_stream_kernel<kW1, MSUB, true, kFrag><<<grid, 256, lds + a_bytes, stream>>>(
+    gemm_stream_kernel<kW1, MSUB, true, kFrag><<<grid, 256, lds + a_bytes + wt_bytes, stream>>>(
         act, act_bytes, gather, k_top, n_slots, wq, wsc, tiles, n_tiles, K, n_rows, half, wpt,
-        limit, clamp, out, ld_out, a_rows, a_ring);
+        limit, clamp, out, ld_out, a_rows, a_ring, static_cast<int>(lds + a_bytes));
   else
     gemm_stream_kernel<kW1, MSUB, false, kFrag><<<grid, 256, 0, stream>>>(
         act, act_bytes, gather, k_top, n_slots, wq, wsc, tiles, n_tiles, K, n_rows, half, wpt,
-        limit, clamp, out, ld_out, 0, 0);
+        limit, clamp, out, ld_out, 0, 0, 0);
   return hipGetLastError();
 }
 
