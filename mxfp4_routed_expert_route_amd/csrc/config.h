@@ -75,7 +75,7 @@ struct RowTile {
   int32_t expert;
   int32_t p_begin;
   int32_t p_end;
-  int32_t pad;
+  int32_t multi;   // 1 when the expert's rows span more than one tile
 };
 
 }  // namespace moe

@@ -189,94 +189,106 @@ __global__ __launch_bounds__(256) void gemv_kernel(
   const int p = __builtin_amdgcn_readfirstlane(rt.p_begin);   // the tile's one row
   const int expert = __builtin_amdgcn_readfirstlane(rt.expert);
 
-  // the expert's codes and scales as buffer resources: each load below is a scalar
-  // row offset plus the lane's 32-bit offset (no 64-bit address arithmetic per lane)
-  const size_t e_rows = static_cast<size_t>(expert) * n_rows;
-  const __amdgpu_buffer_rsrc_t wrs =
-      make_rsrc(wq + e_rows * (K / 2), static_cast<uint32_t>(n_rows) * (K / 2));
-  const __amdgpu_buffer_rsrc_t srs =
-      make_rsrc(wsc + e_rows * (K / 32), static_cast<uint32_t>(n_rows) * (K / 32));
-  const int lane16 = 16 * lane;
-  const int lane_s = (lane >> 4) * (K / 32) + 4 * (lane & 15);
-  // weight row j of group g (W1: j < 4 gate rows 4 g + j, j >= 4 the matching up
-  // rows; W2: output rows 8 g + j)
-  auto wrow = [&](int g, int j) {
-    return kW1 ? (j < 4 ? 4 * g + j : half + 4 * g + (j - 4)) : kGemvRows * g + j;
-  };
-  // A group's codes: one 1 KB load per row and slice, non-temporal.  Its scales: two
-  // dwords per lane and slice (rows wrow(g, 4m + lane / 16), blocks 4 (lane % 16) ..
-  // +3 of the slice), from which each lane takes its byte (block `lane` of row j)
-  // with a lane permute when it is used.
-  auto load_group = [&](int g, uint4 (&q)[kGemvRows][kSlices], uint32_t (&sd)[2][kSlices]) {
+  // W1: an expert whose rows span several tiles (two or more rows) is read by
+  // several tiles' wavefronts at about the same time, on the same XCD (tile t's
+  // wavefront w and tile t + 1's are a multiple of 8 workgroups apart): its loads
+  // are normal ones, so that the later reads can hit the L2; all others are
+  // non-temporal.
+  auto body = [&](auto aux_c) __attribute__((always_inline)) {
+    constexpr int kAux = decltype(aux_c)::value;
+    // the expert's codes and scales as buffer resources: each load below is a scalar
+    // row offset plus the lane's 32-bit offset (no 64-bit address arithmetic per lane)
+    const size_t e_rows = static_cast<size_t>(expert) * n_rows;
+    const __amdgpu_buffer_rsrc_t wrs =
+        make_rsrc(wq + e_rows * (K / 2), static_cast<uint32_t>(n_rows) * (K / 2));
+    const __amdgpu_buffer_rsrc_t srs =
+        make_rsrc(wsc + e_rows * (K / 32), static_cast<uint32_t>(n_rows) * (K / 32));
+    const int lane16 = 16 * lane;
+    const int lane_s = (lane >> 4) * (K / 32) + 4 * (lane & 15);
+    // weight row j of group g (W1: j < 4 gate rows 4 g + j, j >= 4 the matching up
+    // rows; W2: output rows 8 g + j)
+    auto wrow = [&](int g, int j) {
+      return kW1 ? (j < 4 ? 4 * g + j : half + 4 * g + (j - 4)) : kGemvRows * g + j;
+    };
+    // A group's codes: one 1 KB load per row and slice, non-temporal.  Its scales: two
+    // dwords per lane and slice (rows wrow(g, 4m + lane / 16), blocks 4 (lane % 16) ..
+    // +3 of the slice), from which each lane takes its byte (block `lane` of row j)
+    // with a lane permute when it is used.
+    auto load_group = [&](int g, uint4 (&q)[kGemvRows][kSlices], uint32_t (&sd)[2][kSlices]) {
 #pragma unroll
-    for (int i = 0; i < kSlices; ++i)
+      for (int i = 0; i < kSlices; ++i)
 #pragma unroll
-      for (int m = 0; m < 2; ++m)
-        sd[m][i] = __builtin_amdgcn_raw_buffer_load_b32(
-            srs, lane_s + 64 * i, __builtin_amdgcn_readfirstlane(wrow(g, 4 * m) * (K / 32)), 0);
+        for (int m = 0; m < 2; ++m)
+          sd[m][i] = __builtin_amdgcn_raw_buffer_load_b32(
+              srs, lane_s + 64 * i, __builtin_amdgcn_readfirstlane(wrow(g, 4 * m) * (K / 32)), 0);
 #pragma unroll
-    for (int i = 0; i < kSlices; ++i)
+      for (int i = 0; i < kSlices; ++i)
 #pragma unroll
-      for (int j = 0; j < kGemvRows; ++j)
-        q[j][i] = __builtin_bit_cast(
-            uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                       wrs, lane16 + 1024 * i,
-                       __builtin_amdgcn_readfirstlane(wrow(g, j) * (K / 2)), kGemvNt));
-    // keep the loads where they stand: hoisted into the previous group's products
-    // they would hold a third register set
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  uint4 a[kSlices][4];   // the lane's activations (filled below)
-  const int idx = (lane >> 2) & 7;   // the row whose sum a lane holds after the reduction
-  // group g from q / sd: products, reduction over the lanes, epilogue
-  auto finish_group = [&](int g, const uint4 (&q)[kGemvRows][kSlices],
-                          const uint32_t (&sd)[2][kSlices]) {
-    float v[kGemvRows];
-    gemv_dot8<kSlices>(q, [&](int j, int i) { return gemv_scale_byte(sd[j >> 2][i], j, lane); },
-                       a, v);
-    const float sum = gemv_reduce8(v, lane);
-    if (kW1) {
-      // gate rows are rows 0..3 (lane bit 4 clear), their up rows 4..7 (lane ^ 16)
-      const float up = swz_xor16(sum);
-      if ((lane & 0x33) == 0)   // one lane per gate row
-        out[static_cast<int64_t>(p) * ld_out + 4 * g + idx] =
-            f32_to_bf16_bits(swiglu(sum, up, limit, clamp != 0));
-    } else if ((lane & 0x23) == 0) {   // one lane per row
-      out[static_cast<int64_t>(p) * ld_out + kGemvRows * g + idx] = f32_to_bf16_bits(sum);
-    }
-  };
+        for (int j = 0; j < kGemvRows; ++j)
+          q[j][i] = __builtin_bit_cast(
+              uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                         wrs, lane16 + 1024 * i,
+                         __builtin_amdgcn_readfirstlane(wrow(g, j) * (K / 2)), kAux));
+      // keep the loads where they stand: hoisted into the previous group's products
+      // they would hold a third register set
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    uint4 a[kSlices][4];   // the lane's activations (filled below)
+    const int idx = (lane >> 2) & 7;   // the row whose sum a lane holds after the reduction
+    // group g from q / sd: products, reduction over the lanes, epilogue
+    auto finish_group = [&](int g, const uint4 (&q)[kGemvRows][kSlices],
+                            const uint32_t (&sd)[2][kSlices]) {
+      float v[kGemvRows];
+      gemv_dot8<kSlices>(q, [&](int j, int i) { return gemv_scale_byte(sd[j >> 2][i], j, lane); },
+                         a, v);
+      const float sum = gemv_reduce8(v, lane);
+      if (kW1) {
+        // gate rows are rows 0..3 (lane bit 4 clear), their up rows 4..7 (lane ^ 16)
+        const float up = swz_xor16(sum);
+        if ((lane & 0x33) == 0)   // one lane per gate row
+          out[static_cast<int64_t>(p) * ld_out + 4 * g + idx] =
+              f32_to_bf16_bits(swiglu(sum, up, limit, clamp != 0));
+      } else if ((lane & 0x23) == 0) {   // one lane per row
+        out[static_cast<int64_t>(p) * ld_out + kGemvRows * g + idx] = f32_to_bf16_bits(sum);
+      }
+    };
 
-  // Two register sets: the next group's loads are issued before the current group
-  // is computed.  The wavefront's groups are w_in + r wpt, r < groups / wpt (an even
-  // count), so every load is issued on every path (no load sits under a branch,
-  // which would make the compiler's later waits count as if it had not been taken)
-  // and each wait counts only older loads.  The first group's loads go out before
-  // the activation row's (which wait on the gather index).
-  uint4 qa[kGemvRows][kSlices], qb[kGemvRows][kSlices];
-  uint32_t sa[2][kSlices], sbb[2][kSlices];
-  int g = w_in;
-  load_group(g, qa, sa);
-  {
-    // W1: the tile row's token.  gather comes from moe_expert_offsets; an entry out
-    // of range (outside that contract) reads token 0 instead, so that the loads stay
-    // in bounds and unconditional (its h row is then unspecified).
-    int64_t row = p;
-    if (kW1) {
-      const int slot = __builtin_amdgcn_readfirstlane(gather[p]);
-      row = static_cast<unsigned>(slot) < static_cast<unsigned>(n_slots) ? slot / k_top : 0;
+    // Two register sets: the next group's loads are issued before the current group
+    // is computed.  The wavefront's groups are w_in + r wpt, r < groups / wpt (an even
+    // count), so every load is issued on every path (no load sits under a branch,
+    // which would make the compiler's later waits count as if it had not been taken)
+    // and each wait counts only older loads.  The first group's loads go out before
+    // the activation row's (which wait on the gather index).
+    uint4 qa[kGemvRows][kSlices], qb[kGemvRows][kSlices];
+    uint32_t sa[2][kSlices], sbb[2][kSlices];
+    int g = w_in;
+    load_group(g, qa, sa);
+    {
+      // W1: the tile row's token.  gather comes from moe_expert_offsets; an entry out
+      // of range (outside that contract) reads token 0 instead, so that the loads stay
+      // in bounds and unconditional (its h row is then unspecified).
+      int64_t row = p;
+      if (kW1) {
+        const int slot = __builtin_amdgcn_readfirstlane(gather[p]);
+        row = static_cast<unsigned>(slot) < static_cast<unsigned>(n_slots) ? slot / k_top : 0;
+      }
+      gemv_load_act<kSlices>(act + row * K, lane, a);
     }
-    gemv_load_act<kSlices>(act + row * K, lane, a);
-  }
 #pragma unroll 1
-  for (;;) {
-    load_group(g + wpt, qb, sbb);
-    finish_group(g, qa, sa);
-    if (g + 2 * wpt >= groups) break;
-    load_group(g + 2 * wpt, qa, sa);
+    for (;;) {
+      load_group(g + wpt, qb, sbb);
+      finish_group(g, qa, sa);
+      if (g + 2 * wpt >= groups) break;
+      load_group(g + 2 * wpt, qa, sa);
+      finish_group(g + wpt, qb, sbb);
+      g += 2 * wpt;
+    }
     finish_group(g + wpt, qb, sbb);
-    g += 2 * wpt;
-  }
-  finish_group(g + wpt, qb, sbb);
+  };
+  if (kW1 && __builtin_amdgcn_readfirstlane(rt.multi) != 0)
+    body(std::integral_constant<int, 0>{});
+  else
+    body(std::integral_constant<int, kGemvNt>{});
 }
 
 // gemv_dot8 with the lane's activations fetched half a slice at a time (act(i, c):

@@ -122,7 +122,7 @@ __global__ __launch_bounds__(1024) void frontend_small_kernel(
         rt.expert = lane * EPL + i;
         rt.p_begin = off + t * tile_rows;
         rt.p_end = (t + 1) * tile_rows < c[i] ? off + (t + 1) * tile_rows : off + c[i];
-        rt.pad = 0;
+        rt.multi = c[i] > tile_rows ? 1 : 0;
         tiles[slot] = rt;
       }
       off += c[i];

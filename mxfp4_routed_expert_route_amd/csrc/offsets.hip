@@ -75,7 +75,7 @@ __device__ __forceinline__ void write_tile_plan_pairs(int e0, int E, const int (
       rt.expert = e0 + q;
       rt.p_begin = off[q] + i * tile_rows;
       rt.p_end = (i + 1) * tile_rows < c[q] ? off[q] + (i + 1) * tile_rows : off[q] + c[q];
-      rt.pad = 0;
+      rt.multi = c[q] > tile_rows ? 1 : 0;
       tiles[slot] = rt;
     }
     slot0 += nt[q];

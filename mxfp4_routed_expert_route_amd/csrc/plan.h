@@ -34,7 +34,7 @@ __device__ __forceinline__ void write_tile_plan(int e, int E, int count, int beg
     rt.expert = e;
     rt.p_begin = begin + i * tile_rows;
     rt.p_end = (i + 1) * tile_rows < count ? begin + (i + 1) * tile_rows : begin + count;
-    rt.pad = 0;
+    rt.multi = count > tile_rows ? 1 : 0;
     tiles[slot] = rt;
   }
   if (threadIdx.x == blockDim.x - 1) {

@@ -126,17 +126,24 @@ __device__ __forceinline__ void collect_word(uint32_t word, uint32_t& lo, uint32
   }
 }
 
+// masks[e] for the 64 experts of bit-matrix words w0, w0+1 (this lane's token's
+// words word0, word1).
+__device__ __forceinline__ void column_masks_words(uint32_t word0, uint32_t word1, int E,
+                                                   int lane, uint64_t* masks, int w0) {
+  uint32_t lo = 0u, hi = 0u;
+  collect_word<0>(word0, lo, hi);
+  collect_word<32>(word1, lo, hi);
+  const int e = w0 * 32 + lane;
+  if (e < E) masks[e] = (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
 // masks[e] for the 64 experts of bit-matrix words w0, w0+1, for the token of this
 // lane (t, valid = t < T).
 __device__ __forceinline__ void column_masks_64(const uint32_t* bm, int64_t t, bool valid, int E,
                                                 int words, int lane, uint64_t* masks, int w0) {
   const uint32_t word0 = valid ? bm[t * words + w0] : 0u;
   const uint32_t word1 = (valid && w0 + 1 < words) ? bm[t * words + w0 + 1] : 0u;
-  uint32_t lo = 0u, hi = 0u;
-  collect_word<0>(word0, lo, hi);
-  collect_word<32>(word1, lo, hi);
-  const int e = w0 * 32 + lane;
-  if (e < E) masks[e] = (static_cast<uint64_t>(hi) << 32) | lo;
+  column_masks_words(word0, word1, E, lane, masks, w0);
 }
 
 // masks[e] <- column mask of expert e over rows[t0 .. t0+63] (rows past T are empty).
@@ -147,6 +154,17 @@ __device__ __forceinline__ void wave_column_masks(const uint32_t* bm, int64_t t0
   const bool valid = t < T;
   if (t0 >= T) {   // no token in this wavefront
     for (int e = lane; e < E; e += 64) masks[e] = 0ull;
+    return;
+  }
+  if (words <= 8) {
+    // up to 256 experts: the token's words are loaded together (one memory
+    // latency, not one per pair of words)
+    uint32_t wd[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) wd[i] = valid && i < words ? bm[t * words + i] : 0u;
+#pragma unroll
+    for (int w0 = 0; w0 < 8; w0 += 2)
+      if (w0 < words) column_masks_words(wd[w0], wd[w0 + 1], E, lane, masks, w0);
     return;
   }
   for (int w0 = 0; w0 < words; w0 += 2) column_masks_64(bm, t, valid, E, words, lane, masks, w0);
