@@ -451,8 +451,10 @@ def markers(mib: int):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    # the clocks settle over the first few ms of steady work (verify layer: ~112 us
+    # per step over the first 100 steps after setup, ~105.5 after)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workloads", default="1,2,3,4",
                     help="comma-separated workload indices 0..4 (default: the four full-size ones)")
     ap.add_argument("--workload", type=int, default=None,
