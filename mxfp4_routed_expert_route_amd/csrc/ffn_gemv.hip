@@ -19,11 +19,13 @@
 // with their E8M0 scale (the gfx950 scaled convert; exact) and multiplied by the
 // lane's 32 activations with two-element dot products into fp32.  Each group's 8
 // sums are reduced over the 64 lanes with lane exchanges, and W1 applies the
-// clamped SwiGLU.  A tile is one row: an expert with several rows gets several
-// tiles, whose wavefronts read its weights at about the same time (the second read
-// mostly from cache); one activation row keeps the registers for two groups of
-// weights in flight.  No LDS, no workgroup barrier: every wavefront runs on its
-// own.  In the one-call layer, W2 runs with the weighted combine folded in
+// clamped SwiGLU.  A group's E8M0 scales come as two dwords per lane and slice and
+// reach their lanes by lane permutes.  A tile is one row: an expert with several
+// rows gets several tiles, whose wavefronts read its weights at about the same time
+// on the same XCD (W1 reads such experts with normal loads, so the later reads hit
+// the L2); one activation row keeps the registers for two groups of weights in
+// flight.  No LDS, no workgroup barrier: every wavefront runs on its own.  In the
+// one-call layer, W2 runs with the weighted combine folded in
 // (gemv_w2_combine_kernel, one workgroup per token and 32 output columns).
 #include <type_traits>
 
