@@ -395,45 +395,45 @@ void gemm_stream_kernel(
     // of each lane's row) sit at bank quad r ^ t, a function of the row alone, and
     // eight consecutive lanes storing one row's pieces hit distinct quads (the
     // tiled kernel's activation layout states the measured rule).
-    constexpr int kRR = 16 * MSUB, kSlot = 32 * kRR * 16;
-    constexpr int kTpr = 16 / MSUB, kPc = 2 * MSUB;   // threads per row, pieces per thread
-    const int sr = threadIdx.x / kTpr, sp = threadIdx.x % kTpr;
-    uint32_t srow = kRsrcOutOfRange;
-    {
-      const int p = rt.p_begin + sr;
-      if (p < rt.p_end) {
-        if (kW1) {
-          const int slot = gather[p];
-          if (static_cast<unsigned>(slot) < static_cast<unsigned>(n_slots))
-            srow = static_cast<uint32_t>(slot / k_top) * static_cast<uint32_t>(K) * 2u;
-        } else {
-          srow = static_cast<uint32_t>(p) * static_cast<uint32_t>(K) * 2u;
+    auto run_ring = [&]() __attribute__((always_inline)) {
+      constexpr int kRR = 16 * MSUB, kSlot = 32 * kRR * 16;
+      constexpr int kTpr = 16 / MSUB, kPc = 2 * MSUB;   // threads per row, pieces per thread
+      const int sr = threadIdx.x / kTpr, sp = threadIdx.x % kTpr;
+      uint32_t srow = kRsrcOutOfRange;
+      {
+        const int p = rt.p_begin + sr;
+        if (p < rt.p_end) {
+          if (kW1) {
+            const int slot = gather[p];
+            if (static_cast<unsigned>(slot) < static_cast<unsigned>(n_slots))
+              srow = static_cast<uint32_t>(slot / k_top) * static_cast<uint32_t>(K) * 2u;
+          } else {
+            srow = static_cast<uint32_t>(p) * static_cast<uint32_t>(K) * 2u;
+          }
         }
       }
-    }
-    auto stage_load = [&](uint4 (&r)[kPc], int c2) __attribute__((always_inline)) {
+      auto stage_load = [&](uint4 (&r)[kPc], int c2) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < kPc; ++i)
-        r[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                             arsrc, srow + 16 * (sp + kTpr * i), c2 * 512, 0));
-    };
-    auto stage_store = [&](const uint4 (&r)[kPc], int slot) __attribute__((always_inline)) {
-      // piece sp + kTpr * i of row sr; kTpr is a multiple of 8, so the row XOR is sp & 7
-      unsigned char* d = a_lds + slot * kSlot + (sp * kRR + (sr ^ (sp & 7))) * 16;
+        for (int i = 0; i < kPc; ++i)
+          r[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                               arsrc, srow + 16 * (sp + kTpr * i), c2 * 512, 0));
+      };
+      auto stage_store = [&](const uint4 (&r)[kPc], int slot) __attribute__((always_inline)) {
+        // piece sp + kTpr * i of row sr; kTpr is a multiple of 8, so the row XOR is sp & 7
+        unsigned char* d = a_lds + slot * kSlot + (sp * kRR + (sr ^ (sp & 7))) * 16;
 #pragma unroll
-      for (int i = 0; i < kPc; ++i) *reinterpret_cast<uint4*>(d + kTpr * i * kRR * 16) = r[i];
-    };
-    auto read_a = [&](bf16x8 (&a)[MSUB][8], int c2) __attribute__((always_inline)) {
-      const unsigned char* base = a_lds + (c2 & 1) * kSlot;
+        for (int i = 0; i < kPc; ++i) *reinterpret_cast<uint4*>(d + kTpr * i * kRR * 16) = r[i];
+      };
+      auto read_a = [&](bf16x8 (&a)[MSUB][8], int c2) __attribute__((always_inline)) {
+        const unsigned char* base = a_lds + (c2 & 1) * kSlot;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int off = ((8 * g + t) * kRR + (r16 ^ t)) * 16;   // piece 8g + t
+        for (int t = 0; t < 8; ++t) {
+          const int off = ((8 * g + t) * kRR + (r16 ^ t)) * 16;   // piece 8g + t
 #pragma unroll
-        for (int mi = 0; mi < MSUB; ++mi)
-          a[mi][t] = *reinterpret_cast<const bf16x8*>(base + off + mi * 256);
-      }
-    };
-    auto run_ring = [&]() __attribute__((always_inline)) {
+          for (int mi = 0; mi < MSUB; ++mi)
+            a[mi][t] = *reinterpret_cast<const bf16x8*>(base + off + mi * 256);
+        }
+      };
       uint4 sa[kPc];
       uint4 q0[kFrag][2], q1[kFrag][2];
       stage_load(sa, 0);
