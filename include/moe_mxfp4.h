@@ -201,9 +201,12 @@ moe_status moe_route_and_group(const float* logits, int64_t T, int32_t E, int32_
  * and citation).  The FFN's row-tile plan is written by the routing side where
  * it holds the counts in one workgroup -- the one-launch front-end for T <= 64,
  * the expert-offsets kernel for 64 < T <= 512, the expert-offsets scan above --
- * which saves the FFN its plan launch.  ws is
- * the workspace of those calls (moe_workspace_bytes).  T = 0 writes zeros to
- * counts and offsets and nothing else.
+ * which saves the FFN its plan launch.  On the decode GEMV path (T*k < E, H and
+ * I each 2048 or 4096) the W2 launch also computes y, with the combine's
+ * arithmetic (fp32 sum in slot order, one bf16 rounding), which saves the combine
+ * launch; the outputs are the same bits.  ws is the workspace of those calls
+ * (moe_workspace_bytes).  T = 0 writes zeros to counts and offsets and nothing
+ * else.
  */
 moe_status moe_forward_mxfp4(const float* logits, const uint16_t* x, int64_t T, int32_t H,
                              int32_t I, int32_t E, int32_t k, const uint8_t* w1,
