@@ -83,6 +83,7 @@ def test_forward_matches_separate_calls_workloads(index):
     (1, 16, 8, 2048, 2048, 58),      # GEMV path, k = 8 (the maximum)
     (3, 16, 3, 2048, 4096, 59),      # GEMV path, W2 over K = 4096 (two slices), k odd
     (2, 16, 5, 4096, 2048, 60),      # GEMV path, H = 4096
+    (1, 16, 8, 2048, 4096, 61),      # GEMV path, W2 K = 4096 and k = 8: 64 KB of h in LDS
 ])
 def test_forward_matches_separate_calls(T, E, k, H, I, seed):
     if not torch.cuda.is_available():
