@@ -82,22 +82,29 @@ constexpr int kXcds = 8;
 
 template <int kMSub>
 constexpr int a_buf_bytes() { return kMSub * 16 * kAPieces * 16; }
-// LDS of the staged E8M0 scales: per wavefront, one dword per (128-element chunk,
-// weight row) of its 64 rows
+// LDS a wavefront's weights pass through (kR8): one pair of chunks of its four
+// fragments (4 x 16 rows x 128 bytes of codes) and the scale dwords of two pairs
+// (4 chunks x 16 rows x 4 fragments)
+constexpr int kTileTransitBytes = 4 * 2048 + 4 * 16 * 4 * 4;
+// LDS of the staged E8M0 scales (without kR8): per wavefront, one dword per
+// (128-element chunk, weight row) of its 64 rows
 inline size_t tile_scale_lds_bytes(int K, int waves) {
   return static_cast<size_t>(waves) * (K / kFfnKChunk) * 64 * sizeof(uint32_t);
 }
 constexpr size_t kTileLdsPerWorkgroup = 80 * 1024;   // two workgroups per CU
 constexpr size_t kCuLds = 160 * 1024;                 // one workgroup per CU
-// LDS of a workgroup: two activation buffers, a scale dword per thread for each
-// (the rows' block scales), and the staged weight scales (when they are staged)
-inline size_t tile_lds_bytes(int msub, int K, int waves, bool lds_scales, bool tile_ascales) {
+// LDS of a workgroup: two activation buffers, the rows' block scales (a dword per
+// thread for each buffer, or with tile_ascales all of K for each row), and the
+// wavefronts' weight transit areas (r8) or staged weight scales (lds_scales)
+inline size_t tile_lds_bytes(int msub, int K, int waves, bool r8, bool lds_scales, bool tile_ascales) {
   const size_t rows = static_cast<size_t>(msub) * 16;
   const size_t ascales = tile_ascales ? rows * (K / 128 + 1) * 4 : 2 * static_cast<size_t>(64 * waves) * 4;
-  return 2 * rows * kAPieces * 16 + ascales + (lds_scales ? tile_scale_lds_bytes(K, waves) : 0);
+  const size_t weights = r8 ? static_cast<size_t>(waves) * kTileTransitBytes
+                            : (lds_scales ? tile_scale_lds_bytes(K, waves) : 0);
+  return 2 * rows * kAPieces * 16 + ascales + weights;
 }
 
-template <bool kW1, int kMSub, int kFrag, int kWaves, bool kLdsScales, bool kTileAScales>
+template <bool kW1, int kMSub, int kFrag, int kWaves, bool kR8, bool kLdsScales, bool kTileAScales>
 __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
     const uint8_t* __restrict__ act, uint32_t act_bytes, const uint8_t* __restrict__ asc,
     uint32_t asc_bytes, const int32_t* __restrict__ gather, int k_top, int n_slots,
@@ -247,15 +254,91 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
                : cg * (16 * kFrag) + (c16 >> 2) * (4 * kFrag) + f * 4 + (c16 & 3);
   };
   const size_t row_q = static_cast<size_t>(K / 2), row_s = static_cast<size_t>(K / 32);
-  const size_t e_rows = static_cast<size_t>(rt.expert) * n_rows;
-  // weight and scale addresses: a wave-uniform base (the expert's slab and the
-  // fragment's first row) plus one 32-bit lane offset within the slab, so each
-  // load takes the scalar-base form and costs the wavefront one VGPR of address
+  // The wavefront reads its rows 256 K elements at a time (a pair of 128-element
+  // chunks: 128 bytes of codes and 8 scale bytes per row).  Each load instruction
+  // covers 8 rows x 128 contiguous bytes -- lane l takes row 8h + l/8 of a
+  // fragment (h = 0, 1), bytes 16 (l % 8) .. +15 -- the read shape that streams
+  // fastest on MI355X (the FP4 operand's own shape, 16 rows x 64 bytes, reads
+  // ~20% slower).  The pair reaches the operand layout through kTileTransitBytes
+  // of LDS per wavefront: lane (r16, g) reads row r16's 16-byte block 4j + g for
+  // chunk j of the pair.  Row r's block b sits in 256-byte line r/2 at 16-byte
+  // quad 8 (r % 2) + (b ^ r/2) of its fragment's 2 KB, so the stores (8 lanes at
+  // a time) and the reads (16 lanes at a time) each meet 8 or 16 different quads.
+  // Lane l loads the 8 scale bytes of row (fragment l/16, row l%16), kept as
+  // [j][16][kFrag] dwords: one 16-byte read gives a lane its fragments' scale
+  // dwords for chunk j.  The transit area is the wavefront's own and its LDS
+  // operations run in order, so a pair is stored right after the reads of the
+  // one before, with no barrier.  Loads go through a buffer resource on the
+  // expert's slab: with an odd chunk count the last pair's second half reads the
+  // next row's codes, or zeros past the slab, which no product uses.
+  const int expert_u = __builtin_amdgcn_readfirstlane(rt.expert);
+  const size_t e_rows = static_cast<size_t>(expert_u) * n_rows;
+  const __amdgpu_buffer_rsrc_t wrs =
+      make_rsrc(wq + e_rows * row_q, static_cast<uint32_t>(static_cast<size_t>(n_rows) * row_q));
+  const __amdgpu_buffer_rsrc_t srs =
+      make_rsrc(wsc + e_rows * row_s, static_cast<uint32_t>(static_cast<size_t>(n_rows) * row_s));
+  // fragment f's rows are wrow(f, 0) + (wrow(0, c) - wrow(0, 0)): a wave-uniform
+  // fragment base plus a lane offset shared by all fragments
+  const int row0 = wrow(0, 0);
+  uint32_t fq[kFrag];
+#pragma unroll
+  for (int f = 0; f < kFrag; ++f)
+    fq[f] = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(wrow(f, 0))) * static_cast<uint32_t>(row_q);
+  const uint32_t vq0 = static_cast<uint32_t>((wrow(0, lane >> 3) - row0) * row_q) + 16u * (lane & 7);
+  const uint32_t vq1 = static_cast<uint32_t>((wrow(0, 8 + (lane >> 3)) - row0) * row_q) + 16u * (lane & 7);
+  const uint32_t vs = static_cast<uint32_t>(wrow(lane >> 4, r16) * row_s);
+  const int last_pair = (n_chunks - 1) >> 1;
+  uint4 wr[kFrag][2];
+  uint4 sr;
+  // pair p's codes into wr; for even pairs (with_scales) also the scales of pairs
+  // p and p + 1 into sr (16 bytes a row: half the scale-line visits of one load
+  // per pair).  The K loop advances two pairs per iteration, so which pairs carry
+  // scales is fixed at compile time (a branch inside the loop would split its body
+  // and spill the accumulators).
+  auto load_pair = [&](int p, auto with_scales) {
+#pragma unroll
+    for (int f = 0; f < kFrag; ++f)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        wr[f][h] = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(wrs, h ? vq1 : vq0, fq[f] + 128u * p, 0));
+    if constexpr (decltype(with_scales)::value)
+      sr = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(srs, vs, 8u * p, 0));
+  };
+  const size_t a_scl_bytes =
+      kTileAScales ? static_cast<size_t>(kRows) * (K / 128 + 1) * 4 : 2 * static_cast<size_t>(kThreads) * 4;
+  unsigned char* wt = tile_lds + 2 * kABuf + a_scl_bytes + wave * kTileTransitBytes;
+  uint32_t* wts = reinterpret_cast<uint32_t*>(wt + kFrag * 2048);   // [chunk % 4][16][kFrag]
+  auto put_pair = [&](auto with_scales) {
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int f = 0; f < kFrag; ++f)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = 8 * h + (lane >> 3), b = lane & 7;
+        *reinterpret_cast<uint4*>(wt + f * 2048 + (r >> 1) * 256 + ((r & 1) * 8 + (b ^ (r >> 1))) * 16) =
+            wr[f][h];
+      }
+    if constexpr (decltype(with_scales)::value) {
+      wts[r16 * kFrag + (lane >> 4)] = sr.x;
+      wts[(16 + r16) * kFrag + (lane >> 4)] = sr.y;
+      wts[(32 + r16) * kFrag + (lane >> 4)] = sr.z;
+      wts[(48 + r16) * kFrag + (lane >> 4)] = sr.w;
+    }
+    asm volatile("" ::: "memory");
+  };
+
+  // Without kR8 (128-row tiles): each fragment row is loaded in the FP4 operand's
+  // own layout, 64 bytes per chunk, two chunks ahead; the weight scales are staged
+  // in LDS for all of K (kLdsScales) or come with the weights.  Addresses: a
+  // wave-uniform base (the expert's slab and the fragment's first row) plus one
+  // 32-bit lane offset within the slab, so each load takes the scalar-base form
+  // and costs the wavefront one VGPR of address.
   const uint8_t* wbase = wq + e_rows * row_q;
   const uint8_t* sbase = wsc + e_rows * row_s;
-  const int row0 = wrow(0, r16);
-  const uint32_t lane_q = static_cast<uint32_t>(row0 * row_q) + 16u * g;
-  const uint32_t lane_s = static_cast<uint32_t>(row0 * row_s);
+  const int lane_row0 = wrow(0, r16);
+  const uint32_t lane_q = static_cast<uint32_t>(lane_row0 * row_q) + 16u * g;
+  const uint32_t lane_s = static_cast<uint32_t>(lane_row0 * row_s);
   size_t dq[kFrag], ds[kFrag];   // fragment f's rows start wrow(f) - wrow(0) rows further on
 #pragma unroll
   for (int f = 0; f < kFrag; ++f) {
@@ -280,7 +363,7 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
       reinterpret_cast<uint32_t*>(tile_lds + 2 * kABuf +
                                   (kTileAScales ? kRows * (K / 128 + 1) : 2 * kThreads) * 4) +
       wave * (n_chunks * 64);
-  if constexpr (kLdsScales) {
+  if constexpr (!kR8 && kLdsScales) {
     const int f = lane >> 4;
     const uint8_t* srow = wsc + (e_rows + wrow(f, r16)) * row_s;
     // eight 16-byte loads in flight before their stores: a load-then-store loop
@@ -311,31 +394,45 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
     for (int f = 0; f < kFrag; ++f) acc[mi][f] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   // one chunk: activations (two-part FP8) and their block scales from LDS buffer
-  // `buf`, weights (FP4 codes) in q, weight scale dwords in sd; subtiles 0 .. NS-1
+  // `buf`, weights (FP4 codes) and their scale dwords from the transit area (chunk
+  // kc is half kc % 2 of the pair stored there); subtiles 0 .. NS-1
   // (NS = kMSub, or fewer when the tile's rows end earlier).  Per subtile and
   // fragment two block-scaled MFMAs (16 x 16 x 128: FP4 weights x FP8 activations),
   // one on the hi parts and one on the lo parts.  The MFMA takes lane 16b + c's
   // scale for row / column c and 32-element block b: a lane of group g passes the
   // scales of block g.
   typedef int v8i __attribute__((ext_vector_type(8)));
-  auto compute = [&](auto ns_c, const uint4 (&q)[kFrag], const uint32_t (&sd)[kFrag], int kc,
-                     int buf) {
+  auto compute = [&](auto ns_c, int kc, int buf, const uint4 (&q)[kFrag], const uint32_t (&sd)[kFrag]) {
     constexpr int NS = decltype(ns_c)::value;
-    uint32_t dw[kFrag];
-    if constexpr (kLdsScales) {
-      const uint4 d = *reinterpret_cast<const uint4*>(my_scales + (kc * 16 + r16) * 4);
-      dw[0] = d.x; dw[1] = d.y; dw[2] = d.z; dw[3] = d.w;
-    } else {
-#pragma unroll
-      for (int f = 0; f < kFrag; ++f) dw[f] = sd[f];
-    }
     int wsc_g[kFrag];   // byte 0: the scale of this lane's weight row, block g
     v8i wb[kFrag];      // 32 FP4 codes of this lane's weight row: elements 32g .. 32g+31
+    if constexpr (kR8) {
+      const int j = kc & 1, bj = 4 * j + g;
+      const int off = (r16 >> 1) * 256 + ((r16 & 1) * 8 + (bj ^ (r16 >> 1))) * 16;
+      const uint4 d = *reinterpret_cast<const uint4*>(wts + (16 * (kc & 3) + r16) * kFrag);
+      const uint32_t dw[4] = {d.x, d.y, d.z, d.w};
 #pragma unroll
-    for (int f = 0; f < kFrag; ++f) {
-      wsc_g[f] = static_cast<int>(dw[f] >> (8 * g));
-      wb[f] = v8i{static_cast<int>(q[f].x), static_cast<int>(q[f].y), static_cast<int>(q[f].z),
-                  static_cast<int>(q[f].w), 0, 0, 0, 0};
+      for (int f = 0; f < kFrag; ++f) {
+        const uint4 w = *reinterpret_cast<const uint4*>(wt + f * 2048 + off);
+        wsc_g[f] = static_cast<int>(dw[f] >> (8 * g));
+        wb[f] = v8i{static_cast<int>(w.x), static_cast<int>(w.y), static_cast<int>(w.z),
+                    static_cast<int>(w.w), 0, 0, 0, 0};
+      }
+    } else {
+      uint32_t dw[kFrag];
+      if constexpr (kLdsScales) {
+        const uint4 d = *reinterpret_cast<const uint4*>(my_scales + (kc * 16 + r16) * 4);
+        dw[0] = d.x; dw[1] = d.y; dw[2] = d.z; dw[3] = d.w;
+      } else {
+#pragma unroll
+        for (int f = 0; f < kFrag; ++f) dw[f] = sd[f];
+      }
+#pragma unroll
+      for (int f = 0; f < kFrag; ++f) {
+        wsc_g[f] = static_cast<int>(dw[f] >> (8 * g));
+        wb[f] = v8i{static_cast<int>(q[f].x), static_cast<int>(q[f].y), static_cast<int>(q[f].z),
+                    static_cast<int>(q[f].w), 0, 0, 0, 0};
+      }
     }
     const unsigned char* abase = a_lds + buf * kABuf;
     const uint32_t* ascl = kTileAScales ? a_scl + kc : a_scl + buf * kThreads;
@@ -363,7 +460,7 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
     // of all fragments go before the lo ones, so no MFMA waits on the one before it.
     // (Not in the 128-row kernel that loads the weight scales with the weights:
     // there the second register set does not fit beside its other registers.)
-    constexpr bool kTwoSets = !(kMSub == 8 && !kLdsScales);
+    constexpr bool kTwoSets = kR8 ? false : !(kMSub == 8 && !kLdsScales);
     v8i ah0, al0, ah1, al1;
     int as0 = 0, as1 = 0;
     read_sub(0, ah0, al0, as0);
@@ -399,83 +496,172 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
   };
 
   const int last = n_chunks - 1;
-  uint4 q0[kFrag], q1[kFrag];
-  uint32_t s0[kFrag], s1[kFrag];
   int kc = 0;
-  if constexpr (kWaves == 4) {
-    // activations two chunks ahead in registers (ra0/ra1), one chunk ahead in LDS.
-    // The K loop is instantiated for 2 .. 5 subtiles; the tile takes the smallest
-    // that covers its rows (a uniform branch outside the loop)
-    auto run = [&](auto ns_c) {
-      constexpr int NS = decltype(ns_c)::value;
-      constexpr int NP = (NS * 16 + kRowStride - 1) / kRowStride;   // pieces in use
-      uint4 ra0[kPieces], ra1[kPieces];
-      uint32_t rs0 = 0, rs1 = 0;
-      load_a(ra0, rs0, 0, NP);
-      load_w(q0, s0, 0);
-      load_w(q1, s1, last >= 1 ? 1 : 0);
-      load_a(ra1, rs1, last >= 1 ? 1 : 0, NP);
-      store_a(ra0, rs0, 0, NP);
+  // Activations one chunk ahead (registers ra, then LDS), weights one pair ahead
+  // (registers wr, then the transit area).  The K loop is instantiated per
+  // subtile count -- 80-row tiles: 2 .. 5; 128-row tiles: 2, 4, 8 -- and the tile
+  // takes the smallest that covers its rows (a uniform branch outside the loop):
+  // the last tile of an expert, and every tile of an expert with few rows, runs
+  // only the MFMAs of its rows.
+  auto run = [&](auto ns_c) {
+    constexpr int NS = decltype(ns_c)::value;
+    constexpr int NP = (NS * 16 + kRowStride - 1) / kRowStride;   // pieces in use
+    const std::true_type sc{};
+    const std::false_type no_sc{};
+    uint4 ra[kPieces];
+    uint32_t rs = 0;
+    const uint4 qd[kFrag] = {};
+    const uint32_t sdd[kFrag] = {};
+    load_pair(0, sc);
+    load_a(ra, rs, 0, NP);
+    put_pair(sc);
+    load_pair(last_pair >= 1 ? 1 : 0, no_sc);
+    store_a(ra, rs, 0, NP);
+    __syncthreads();
+    // four chunks (pairs P, P + 1) per iteration; each pair is stored after the
+    // last reads of the one before.  Past the last pair the loads repeat it; what
+    // they store is never read.
+    for (; kc + 4 <= n_chunks; kc += 4) {
+      const int P = kc >> 1;
+      load_a(ra, rs, kc + 1, NP);
+      compute(ns_c, kc, 0, qd, sdd);
+      store_a(ra, rs, 1, NP);
       __syncthreads();
-      for (; kc + 2 <= n_chunks; kc += 2) {
-        load_a(ra0, rs0, kc + 2 <= last ? kc + 2 : last, NP);
-        compute(ns_c, q0, s0, kc, 0);
-        load_w(q0, s0, kc + 2 <= last ? kc + 2 : last);
-        store_a(ra1, rs1, 1, NP);
-        __syncthreads();
-        load_a(ra1, rs1, kc + 3 <= last ? kc + 3 : last, NP);
-        compute(ns_c, q1, s1, kc + 1, 1);
-        load_w(q1, s1, kc + 3 <= last ? kc + 3 : last);
-        store_a(ra0, rs0, 0, NP);
-        __syncthreads();
-      }
-      if (kc < n_chunks) compute(ns_c, q0, s0, kc, 0);   // odd chunk count: last chunk in q0
-    };
-    if (msub > 4) {
-      run(std::integral_constant<int, 5>{});
-    } else if (msub > 3) {
-      run(std::integral_constant<int, 4>{});
-    } else if (msub > 2) {
-      run(std::integral_constant<int, 3>{});
-    } else {
-      run(std::integral_constant<int, 2>{});
-    }
-  } else {
-    // activations one chunk ahead (registers ra, then LDS).  The K loop is
-    // instantiated for 2, 4 and 8 subtiles and the tile takes the smallest that
-    // covers its rows (a uniform branch outside the loop): the last tile of an
-    // expert, and every tile of an expert with few rows, runs only the MFMAs of
-    // its rows
-    auto run = [&](auto ns_c) {
-      constexpr int NS = decltype(ns_c)::value;
-      constexpr int NP = (NS * 16 + kRowStride - 1) / kRowStride;   // pieces in use
-      uint4 ra[kPieces];
-      uint32_t rs = 0;
-      load_a(ra, rs, 0, NP);
-      load_w(q0, s0, 0);
-      load_w(q1, s1, last >= 1 ? 1 : 0);
+      load_a(ra, rs, kc + 2, NP);
+      compute(ns_c, kc + 1, 1, qd, sdd);
+      put_pair(no_sc);   // pair P + 1 (its scales came with pair P)
+      load_pair(P + 2 <= last_pair ? P + 2 : last_pair, sc);
       store_a(ra, rs, 0, NP);
       __syncthreads();
-      for (; kc + 2 <= n_chunks; kc += 2) {
-        load_a(ra, rs, kc + 1, NP);
-        compute(ns_c, q0, s0, kc, 0);
-        load_w(q0, s0, kc + 2 <= last ? kc + 2 : last);
+      load_a(ra, rs, kc + 3, NP);
+      compute(ns_c, kc + 2, 0, qd, sdd);
+      store_a(ra, rs, 1, NP);
+      __syncthreads();
+      load_a(ra, rs, kc + 4 <= last ? kc + 4 : last, NP);
+      compute(ns_c, kc + 3, 1, qd, sdd);
+      put_pair(sc);      // pair P + 2 and the scales of P + 2, P + 3
+      load_pair(P + 3 <= last_pair ? P + 3 : last_pair, no_sc);
+      store_a(ra, rs, 0, NP);
+      __syncthreads();
+    }
+    // the last one to three chunks: pair P (stored, with the scales of P + 1) and
+    // pair P + 1 (in wr)
+    if (kc < n_chunks) {
+      const bool c1 = kc + 1 < n_chunks, c2 = kc + 2 < n_chunks;
+      load_a(ra, rs, c1 ? kc + 1 : last, NP);
+      compute(ns_c, kc, 0, qd, sdd);
+      if (c1) {
         store_a(ra, rs, 1, NP);
         __syncthreads();
-        load_a(ra, rs, kc + 2 <= last ? kc + 2 : last, NP);
-        compute(ns_c, q1, s1, kc + 1, 1);
-        load_w(q1, s1, kc + 3 <= last ? kc + 3 : last);
+        load_a(ra, rs, c2 ? kc + 2 : last, NP);
+        compute(ns_c, kc + 1, 1, qd, sdd);
+        if (c2) {
+          put_pair(no_sc);
+          store_a(ra, rs, 0, NP);
+          __syncthreads();
+          compute(ns_c, kc + 2, 0, qd, sdd);
+        }
+      }
+    }
+  };
+  if constexpr (kR8) {
+    if constexpr (kMSub == 5) {
+      if (msub > 4) {
+        run(std::integral_constant<int, 5>{});
+      } else if (msub > 3) {
+        run(std::integral_constant<int, 4>{});
+      } else if (msub > 2) {
+        run(std::integral_constant<int, 3>{});
+      } else {
+        run(std::integral_constant<int, 2>{});
+      }
+    } else {
+      if (msub > kMSub / 2) {
+        run(std::integral_constant<int, kMSub>{});
+      } else if (msub > kMSub / 4) {
+        run(std::integral_constant<int, kMSub / 2>{});
+      } else {
+        run(std::integral_constant<int, kMSub / 4>{});
+      }
+    }
+  } else {
+    uint4 q0[kFrag], q1[kFrag];
+    uint32_t s0[kFrag], s1[kFrag];
+    if constexpr (kWaves == 4) {
+      // activations two chunks ahead in registers (ra0/ra1), one chunk ahead in LDS.
+      // The K loop is instantiated for 2 .. 5 subtiles; the tile takes the smallest
+      // that covers its rows (a uniform branch outside the loop)
+      auto run = [&](auto ns_c) {
+        constexpr int NS = decltype(ns_c)::value;
+        constexpr int NP = (NS * 16 + kRowStride - 1) / kRowStride;   // pieces in use
+        uint4 ra0[kPieces], ra1[kPieces];
+        uint32_t rs0 = 0, rs1 = 0;
+        load_a(ra0, rs0, 0, NP);
+        load_w(q0, s0, 0);
+        load_w(q1, s1, last >= 1 ? 1 : 0);
+        load_a(ra1, rs1, last >= 1 ? 1 : 0, NP);
+        store_a(ra0, rs0, 0, NP);
+        __syncthreads();
+        for (; kc + 2 <= n_chunks; kc += 2) {
+          load_a(ra0, rs0, kc + 2 <= last ? kc + 2 : last, NP);
+          compute(ns_c, kc, 0, q0, s0);
+          load_w(q0, s0, kc + 2 <= last ? kc + 2 : last);
+          store_a(ra1, rs1, 1, NP);
+          __syncthreads();
+          load_a(ra1, rs1, kc + 3 <= last ? kc + 3 : last, NP);
+          compute(ns_c, kc + 1, 1, q1, s1);
+          load_w(q1, s1, kc + 3 <= last ? kc + 3 : last);
+          store_a(ra0, rs0, 0, NP);
+          __syncthreads();
+        }
+        if (kc < n_chunks) compute(ns_c, kc, 0, q0, s0);   // odd chunk count: last chunk in q0
+      };
+      if (msub > 4) {
+        run(std::integral_constant<int, 5>{});
+      } else if (msub > 3) {
+        run(std::integral_constant<int, 4>{});
+      } else if (msub > 2) {
+        run(std::integral_constant<int, 3>{});
+      } else {
+        run(std::integral_constant<int, 2>{});
+      }
+    } else {
+      // activations one chunk ahead (registers ra, then LDS).  The K loop is
+      // instantiated for 2, 4 and 8 subtiles and the tile takes the smallest that
+      // covers its rows (a uniform branch outside the loop): the last tile of an
+      // expert, and every tile of an expert with few rows, runs only the MFMAs of
+      // its rows
+      auto run = [&](auto ns_c) {
+        constexpr int NS = decltype(ns_c)::value;
+        constexpr int NP = (NS * 16 + kRowStride - 1) / kRowStride;   // pieces in use
+        uint4 ra[kPieces];
+        uint32_t rs = 0;
+        load_a(ra, rs, 0, NP);
+        load_w(q0, s0, 0);
+        load_w(q1, s1, last >= 1 ? 1 : 0);
         store_a(ra, rs, 0, NP);
         __syncthreads();
+        for (; kc + 2 <= n_chunks; kc += 2) {
+          load_a(ra, rs, kc + 1, NP);
+          compute(ns_c, kc, 0, q0, s0);
+          load_w(q0, s0, kc + 2 <= last ? kc + 2 : last);
+          store_a(ra, rs, 1, NP);
+          __syncthreads();
+          load_a(ra, rs, kc + 2 <= last ? kc + 2 : last, NP);
+          compute(ns_c, kc + 1, 1, q1, s1);
+          load_w(q1, s1, kc + 3 <= last ? kc + 3 : last);
+          store_a(ra, rs, 0, NP);
+          __syncthreads();
+        }
+        if (kc < n_chunks) compute(ns_c, kc, 0, q0, s0);   // odd chunk count
+      };
+      if (msub > kMSub / 2) {
+        run(std::integral_constant<int, kMSub>{});
+      } else if (msub > kMSub / 4) {
+        run(std::integral_constant<int, kMSub / 2>{});
+      } else {
+        run(std::integral_constant<int, kMSub / 4>{});
       }
-      if (kc < n_chunks) compute(ns_c, q0, s0, kc, 0);   // odd chunk count
-    };
-    if (msub > kMSub / 2) {
-      run(std::integral_constant<int, kMSub>{});
-    } else if (msub > kMSub / 4) {
-      run(std::integral_constant<int, kMSub / 2>{});
-    } else {
-      run(std::integral_constant<int, kMSub / 4>{});
     }
   }
 
@@ -537,19 +723,19 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
   }
 }
 
-template <bool kW1, int kMSub, int kFrag, int kWaves, bool kLdsScales, bool kTileAScales>
+template <bool kW1, int kMSub, int kFrag, int kWaves, bool kR8, bool kLdsScales, bool kTileAScales>
 hipError_t launch_tile_t(const TileArgs& t, hipStream_t stream) {
   // wavefronts per row tile: W1 pairs `half` gate rows with as many up rows, 16 *
   // kFrag/2 of each per wavefront; W2 covers n_rows output rows, 16 * kFrag each
   const int wpt = kW1 ? t.half / (8 * kFrag) : t.n_rows / (16 * kFrag);
   const int bpt = (wpt + kWaves - 1) / kWaves;
-  size_t lds = tile_lds_bytes(kMSub, t.K, kWaves, kLdsScales, kTileAScales);
+  size_t lds = tile_lds_bytes(kMSub, t.K, kWaves, kR8, kLdsScales, kTileAScales);
   // whole tiles per XCD cover row tiles in groups of 8, the column-block/XCD split
   // in pairs: round up to whole groups
   const int64_t blocks = t.whole_tiles               ? (t.tile_bound + 7) / 8 * 8 * bpt
                          : (bpt == 16 || bpt == 8) ? (t.tile_bound + 1) / 2 * 2 * bpt
                                                    : t.tile_bound * bpt;
-  gemm_tile_kernel<kW1, kMSub, kFrag, kWaves, kLdsScales, kTileAScales>
+  gemm_tile_kernel<kW1, kMSub, kFrag, kWaves, kR8, kLdsScales, kTileAScales>
       <<<static_cast<unsigned>(blocks), 64 * kWaves, lds, stream>>>(
       t.act, t.act_bytes, t.asc, t.asc_bytes, t.gather, t.k_top, t.n_slots, t.wq, t.wsc, t.tiles,
       t.n_tiles, t.K, t.n_rows, t.half, wpt, bpt, t.limit, t.clamp, t.out, t.out_sc, t.ld_out,
@@ -560,24 +746,21 @@ hipError_t launch_tile_t(const TileArgs& t, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_tile(bool w1, int tile_rows, const TileArgs& t, hipStream_t stream) {
-  // The E8M0 weight scales are staged in LDS while they fit beside the activation
-  // buffers: in the CU's 160 KB for 128-row tiles (one workgroup per CU), in half
-  // of it for 80-row tiles (two per CU); K <= 4096 either way.  Otherwise they come
-  // with the weights.  128-row tiles also stage the activations' block scales for
-  // all of K when those fit too (K a multiple of 2048 up to 4096: each thread
-  // stages whole 16-byte groups); 80-row tiles stage them per chunk.
+  // 128-row tiles: the E8M0 weight scales are staged in LDS while they fit beside
+  // the activation buffers in the CU's 160 KB (K <= 4096), otherwise they come with
+  // the weights; the activations' block scales are staged for all of K when those
+  // fit too (K a multiple of 2048 up to 4096: each thread stages whole 16-byte
+  // groups).  80-row tiles (two workgroups per CU, 78 KB each) read the weights
+  // through the transit areas and stage the activation scales per chunk.
   if (tile_rows == 128) {
-    if (t.K % 2048 == 0 && tile_lds_bytes(8, t.K, 8, true, true) <= kCuLds)
-      return w1 ? launch_tile_t<true, 8, 4, 8, true, true>(t, stream)
-                : launch_tile_t<false, 8, 4, 8, true, true>(t, stream);
-    return w1 ? launch_tile_t<true, 8, 4, 8, false, false>(t, stream)
-              : launch_tile_t<false, 8, 4, 8, false, false>(t, stream);
+    if (t.K % 2048 == 0 && tile_lds_bytes(8, t.K, 8, false, true, true) <= kCuLds)
+      return w1 ? launch_tile_t<true, 8, 4, 8, false, true, true>(t, stream)
+                : launch_tile_t<false, 8, 4, 8, false, true, true>(t, stream);
+    return w1 ? launch_tile_t<true, 8, 4, 8, false, false, false>(t, stream)
+              : launch_tile_t<false, 8, 4, 8, false, false, false>(t, stream);
   }
-  if (tile_lds_bytes(5, t.K, 4, true, false) <= kTileLdsPerWorkgroup)
-    return w1 ? launch_tile_t<true, 5, 4, 4, true, false>(t, stream)
-              : launch_tile_t<false, 5, 4, 4, true, false>(t, stream);
-  return w1 ? launch_tile_t<true, 5, 4, 4, false, false>(t, stream)
-            : launch_tile_t<false, 5, 4, 4, false, false>(t, stream);
+  return w1 ? launch_tile_t<true, 5, 4, 4, true, false, false>(t, stream)
+            : launch_tile_t<false, 5, 4, 4, true, false, false>(t, stream);
 }
 
 }  // namespace moe

@@ -146,6 +146,9 @@ def test_workload0_whole_layer(limit):
     (300, 8, 3, 384, 640, 17),       # 128-row tiles (112 rows per expert): W1 3 chunks, 20
                                      # wavefronts per tile (last workgroup part-idle); W2 5
                                      # chunks, 6 wavefronts per tile
+    (300, 16, 3, 640, 896, 21),      # 80-row tiles: W1 5 chunks, W2 7 (the weight pairs' loop
+                                     # of four chunks, then one or three more)
+    (250, 8, 2, 768, 128, 22),       # 80-row tiles: W1 6 chunks (loop, then two), W2 1 chunk
 ])
 @pytest.mark.parametrize("limit", [10.0, None])
 def test_ragged_shapes_whole_layer(T, E, k, H, I, seed, limit):
