@@ -95,14 +95,23 @@ constexpr size_t kTileLdsPerWorkgroup = 80 * 1024;   // two workgroups per CU
 constexpr size_t kCuLds = 160 * 1024;                 // one workgroup per CU
 // LDS of a workgroup: two activation buffers, the rows' block scales (a dword per
 // thread for each buffer, or with tile_ascales all of K for each row), and the
-// wavefronts' weight transit areas (r8) or staged weight scales (lds_scales)
+// wavefronts' weight transit areas (r8) and/or staged weight scales (lds_scales)
 inline size_t tile_lds_bytes(int msub, int K, int waves, bool r8, bool lds_scales, bool tile_ascales) {
   const size_t rows = static_cast<size_t>(msub) * 16;
   const size_t ascales = tile_ascales ? rows * (K / 128 + 1) * 4 : 2 * static_cast<size_t>(64 * waves) * 4;
-  const size_t weights = r8 ? static_cast<size_t>(waves) * kTileTransitBytes
-                            : (lds_scales ? tile_scale_lds_bytes(K, waves) : 0);
+  // transit areas and staged weight scales share one region (a tile uses one)
+  const size_t transit = r8 ? static_cast<size_t>(waves) * kTileTransitBytes : 0;
+  const size_t staged = lds_scales ? tile_scale_lds_bytes(K, waves) : 0;
+  const size_t weights = transit > staged ? transit : staged;
   return 2 * rows * kAPieces * 16 + ascales + weights;
 }
+
+// Which K loop a tile with NS subtiles runs: the weight transit (kR8) for every
+// 80-row tile and for 128-row tiles with at most four subtiles; 128-row tiles with
+// eight subtiles keep the operand-layout loads (their 128 accumulators leave no
+// registers for a pair in flight beside the transit's operands).
+template <bool kR8, int kMSub, int NS>
+constexpr bool tile_r8_path() { return kR8 && (kMSub == 5 || NS < kMSub); }
 
 template <bool kW1, int kMSub, int kFrag, int kWaves, bool kR8, bool kLdsScales, bool kTileAScales>
 __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
@@ -357,13 +366,11 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
     }
   };
 
-  // --- 80-row tiles: scales of the wavefront's 64 weight rows, staged as
-  // [chunk][16][4] dwords
+  // staged scales of the wavefront's 64 weight rows, [chunk][16][4] dwords (in the
+  // region the transit areas use on the other path)
   uint32_t* my_scales =
-      reinterpret_cast<uint32_t*>(tile_lds + 2 * kABuf +
-                                  (kTileAScales ? kRows * (K / 128 + 1) : 2 * kThreads) * 4) +
-      wave * (n_chunks * 64);
-  if constexpr (!kR8 && kLdsScales) {
+      reinterpret_cast<uint32_t*>(tile_lds + 2 * kABuf + a_scl_bytes) + wave * (n_chunks * 64);
+  auto stage_scales = [&]() {
     const int f = lane >> 4;
     const uint8_t* srow = wsc + (e_rows + wrow(f, r16)) * row_s;
     // eight 16-byte loads in flight before their stores: a load-then-store loop
@@ -385,7 +392,7 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
     for (; c + 4 <= n_chunks; c += 4) put(c, *reinterpret_cast<const uint4*>(srow + c * 4));
     for (; c < n_chunks; ++c)
       my_scales[(c * 16 + r16) * 4 + f] = *reinterpret_cast<const uint32_t*>(srow + c * 4);
-  }
+  };
 
   floatx4 acc[kMSub][kFrag];
 #pragma unroll
@@ -406,7 +413,7 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
     constexpr int NS = decltype(ns_c)::value;
     int wsc_g[kFrag];   // byte 0: the scale of this lane's weight row, block g
     v8i wb[kFrag];      // 32 FP4 codes of this lane's weight row: elements 32g .. 32g+31
-    if constexpr (kR8) {
+    if constexpr (tile_r8_path<kR8, kMSub, NS>()) {
       const int j = kc & 1, bj = 4 * j + g;
       const int off = (r16 >> 1) * 256 + ((r16 & 1) * 8 + (bj ^ (r16 >> 1))) * 16;
       const uint4 d = *reinterpret_cast<const uint4*>(wts + (16 * (kc & 3) + r16) * kFrag);
@@ -460,7 +467,8 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
     // of all fragments go before the lo ones, so no MFMA waits on the one before it.
     // (Not in the 128-row kernel that loads the weight scales with the weights:
     // there the second register set does not fit beside its other registers.)
-    constexpr bool kTwoSets = kR8 ? false : !(kMSub == 8 && !kLdsScales);
+    constexpr bool kTwoSets =
+        tile_r8_path<kR8, kMSub, NS>() ? NS <= 4 : !(kMSub == 8 && !kLdsScales);
     v8i ah0, al0, ah1, al1;
     int as0 = 0, as1 = 0;
     read_sub(0, ah0, al0, as0);
@@ -497,103 +505,142 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
 
   const int last = n_chunks - 1;
   int kc = 0;
-  // Activations one chunk ahead (registers ra, then LDS), weights one pair ahead
-  // (registers wr, then the transit area).  The K loop is instantiated per
-  // subtile count -- 80-row tiles: 2 .. 5; 128-row tiles: 2, 4, 8 -- and the tile
-  // takes the smallest that covers its rows (a uniform branch outside the loop):
-  // the last tile of an expert, and every tile of an expert with few rows, runs
-  // only the MFMAs of its rows.
-  auto run = [&](auto ns_c) {
+  // D of the tile's subtiles 0 .. NS-1 to the output (the accumulators of
+  // subtiles past NS are never touched on that path)
+  auto epilogue = [&](auto ns_c) {
     constexpr int NS = decltype(ns_c)::value;
-    constexpr int NP = (NS * 16 + kRowStride - 1) / kRowStride;   // pieces in use
-    const std::true_type sc{};
-    const std::false_type no_sc{};
-    uint4 ra[kPieces];
-    uint32_t rs = 0;
-    const uint4 qd[kFrag] = {};
-    const uint32_t sdd[kFrag] = {};
-    load_pair(0, sc);
-    load_a(ra, rs, 0, NP);
-    put_pair(sc);
-    load_pair(last_pair >= 1 ? 1 : 0, no_sc);
-    store_a(ra, rs, 0, NP);
-    __syncthreads();
-    // four chunks (pairs P, P + 1) per iteration; each pair is stored after the
-    // last reads of the one before.  Past the last pair the loads repeat it; what
-    // they store is never read.
-    for (; kc + 4 <= n_chunks; kc += 4) {
-      const int P = kc >> 1;
-      load_a(ra, rs, kc + 1, NP);
-      compute(ns_c, kc, 0, qd, sdd);
-      store_a(ra, rs, 1, NP);
-      __syncthreads();
-      load_a(ra, rs, kc + 2, NP);
-      compute(ns_c, kc + 1, 1, qd, sdd);
-      put_pair(no_sc);   // pair P + 1 (its scales came with pair P)
-      load_pair(P + 2 <= last_pair ? P + 2 : last_pair, sc);
-      store_a(ra, rs, 0, NP);
-      __syncthreads();
-      load_a(ra, rs, kc + 3, NP);
-      compute(ns_c, kc + 2, 0, qd, sdd);
-      store_a(ra, rs, 1, NP);
-      __syncthreads();
-      load_a(ra, rs, kc + 4 <= last ? kc + 4 : last, NP);
-      compute(ns_c, kc + 3, 1, qd, sdd);
-      put_pair(sc);      // pair P + 2 and the scales of P + 2, P + 3
-      load_pair(P + 3 <= last_pair ? P + 3 : last_pair, no_sc);
-      store_a(ra, rs, 0, NP);
-      __syncthreads();
-    }
-    // the last one to three chunks: pair P (stored, with the scales of P + 1) and
-    // pair P + 1 (in wr)
-    if (kc < n_chunks) {
-      const bool c1 = kc + 1 < n_chunks, c2 = kc + 2 < n_chunks;
-      load_a(ra, rs, c1 ? kc + 1 : last, NP);
-      compute(ns_c, kc, 0, qd, sdd);
-      if (c1) {
-        store_a(ra, rs, 1, NP);
-        __syncthreads();
-        load_a(ra, rs, c2 ? kc + 2 : last, NP);
-        compute(ns_c, kc + 1, 1, qd, sdd);
-        if (c2) {
-          put_pair(no_sc);
-          store_a(ra, rs, 0, NP);
-          __syncthreads();
-          compute(ns_c, kc + 2, 0, qd, sdd);
-        }
+    if (!store_cols) return;
+    // D of fragment f, lane (r16, g), element i: activation row 16 mi + r16, output
+    // column wrow(f, 4g + i); per lane these are consecutive from column wrow(0, 4g)
+    const bool do_clamp = clamp != 0;
+    const int col0 = wrow(0, 4 * g);
+#pragma unroll
+    for (int mi = 0; mi < NS; ++mi) {
+      if (mi >= msub) continue;   // uniform over the workgroup
+      const int p = rt.p_begin + mi * 16 + r16;
+      if constexpr (kW1) {
+        // h in two-part FP8: the wavefront's 32 gate columns cg*32 .. cg*32+31 are one
+        // 32-element block of h's row, held by the four lanes r16 + 16g (8 each); the
+        // block's largest magnitude comes from two lane exchanges, which every lane
+        // takes part in
+        float hv[8];
+        uint32_t m = 0;
+#pragma unroll
+        for (int f = 0; f < kGate; ++f)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            hv[4 * f + i] = swiglu(acc[mi][f][i], acc[mi][f + kGate][i], limit, do_clamp);
+            const uint32_t a = __float_as_uint(hv[4 * f + i]) & 0x7FFFFFFFu;
+            m = a > m ? a : m;
+          }
+        uint32_t o = static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 16, 64));
+        m = o > m ? o : m;
+        o = static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 32, 64));
+        m = o > m ? o : m;
+        const uint32_t s = a8_scale_byte(m);
+        const float inv = a8_inv_scale(s);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) hv[i] *= inv;
+        uint2 hi, lo;
+        a8_split8(hv, hi, lo);
+        if (p >= rt.p_end) continue;
+        // block cg = chunk cg / 4, block cg % 4 of it; this lane's 8 elements are
+        // elements 8g .. 8g+7 of the block
+        uint8_t* orow = static_cast<uint8_t*>(out) + static_cast<int64_t>(p) * (2 * ld_out) +
+                        (cg / 4) * 256;
+        const int pos = a8_pos(32 * (cg % 4) + 16 * (g >> 1)) + 8 * (g & 1);
+        *reinterpret_cast<uint2*>(orow + pos) = hi;
+        *reinterpret_cast<uint2*>(orow + 128 + pos) = lo;
+        if (g == 0) out_sc[static_cast<int64_t>(p) * (ld_out / 32) + cg] = static_cast<uint8_t>(s);
+      } else {
+        if (p >= rt.p_end) continue;
+        uint16_t* orow = static_cast<uint16_t*>(out) + static_cast<int64_t>(p) * ld_out + col0;
+        uint32_t w[2 * kFrag];
+#pragma unroll
+        for (int f = 0; f < kFrag; ++f)
+#pragma unroll
+          for (int i = 0; i < 4; i += 2)
+            w[2 * f + i / 2] = pack_bf16x2(acc[mi][f][i], acc[mi][f][i + 1]);
+        *reinterpret_cast<uint4*>(orow) = make_uint4(w[0], w[1], w[2], w[3]);
+        *reinterpret_cast<uint4*>(orow + 8) = make_uint4(w[4], w[5], w[6], w[7]);
       }
     }
   };
-  if constexpr (kR8) {
-    if constexpr (kMSub == 5) {
-      if (msub > 4) {
-        run(std::integral_constant<int, 5>{});
-      } else if (msub > 3) {
-        run(std::integral_constant<int, 4>{});
-      } else if (msub > 2) {
-        run(std::integral_constant<int, 3>{});
-      } else {
-        run(std::integral_constant<int, 2>{});
+
+  // Activations one chunk ahead (registers ra, then LDS).  Weights one pair ahead
+  // (registers wr, then the transit area), or, on the operand-layout path, two
+  // chunks ahead in registers.  The K loop is instantiated per subtile count --
+  // 80-row tiles: 2 .. 5; 128-row tiles: 2, 4, 8 -- and the tile takes the
+  // smallest that covers its rows (a uniform branch outside the loop): the last
+  // tile of an expert, and every tile of an expert with few rows, runs only the
+  // MFMAs of its rows.
+  auto run = [&](auto ns_c) {
+    constexpr int NS = decltype(ns_c)::value;
+    constexpr int NP = (NS * 16 + kRowStride - 1) / kRowStride;   // pieces in use
+    if constexpr (tile_r8_path<kR8, kMSub, NS>()) {
+      const std::true_type sc{};
+      const std::false_type no_sc{};
+      uint4 ra[kPieces];
+      uint32_t rs = 0;
+      const uint4 qd[kFrag] = {};
+      const uint32_t sdd[kFrag] = {};
+      load_pair(0, sc);
+      load_a(ra, rs, 0, NP);
+      put_pair(sc);
+      load_pair(last_pair >= 1 ? 1 : 0, no_sc);
+      store_a(ra, rs, 0, NP);
+      __syncthreads();
+      // four chunks (pairs P, P + 1) per iteration; each pair is stored after the
+      // last reads of the one before.  Past the last pair the loads repeat it; what
+      // they store is never read.
+      for (; kc + 4 <= n_chunks; kc += 4) {
+        const int P = kc >> 1;
+        load_a(ra, rs, kc + 1, NP);
+        compute(ns_c, kc, 0, qd, sdd);
+        store_a(ra, rs, 1, NP);
+        __syncthreads();
+        load_a(ra, rs, kc + 2, NP);
+        compute(ns_c, kc + 1, 1, qd, sdd);
+        put_pair(no_sc);   // pair P + 1 (its scales came with pair P)
+        load_pair(P + 2 <= last_pair ? P + 2 : last_pair, sc);
+        store_a(ra, rs, 0, NP);
+        __syncthreads();
+        load_a(ra, rs, kc + 3, NP);
+        compute(ns_c, kc + 2, 0, qd, sdd);
+        store_a(ra, rs, 1, NP);
+        __syncthreads();
+        load_a(ra, rs, kc + 4 <= last ? kc + 4 : last, NP);
+        compute(ns_c, kc + 3, 1, qd, sdd);
+        put_pair(sc);      // pair P + 2 and the scales of P + 2, P + 3
+        load_pair(P + 3 <= last_pair ? P + 3 : last_pair, no_sc);
+        store_a(ra, rs, 0, NP);
+        __syncthreads();
+      }
+      // the last one to three chunks: pair P (stored, with the scales of P + 1) and
+      // pair P + 1 (in wr)
+      if (kc < n_chunks) {
+        const bool c1 = kc + 1 < n_chunks, c2 = kc + 2 < n_chunks;
+        load_a(ra, rs, c1 ? kc + 1 : last, NP);
+        compute(ns_c, kc, 0, qd, sdd);
+        if (c1) {
+          store_a(ra, rs, 1, NP);
+          __syncthreads();
+          load_a(ra, rs, c2 ? kc + 2 : last, NP);
+          compute(ns_c, kc + 1, 1, qd, sdd);
+          if (c2) {
+            put_pair(no_sc);
+            store_a(ra, rs, 0, NP);
+            __syncthreads();
+            compute(ns_c, kc + 2, 0, qd, sdd);
+          }
+        }
       }
     } else {
-      if (msub > kMSub / 2) {
-        run(std::integral_constant<int, kMSub>{});
-      } else if (msub > kMSub / 4) {
-        run(std::integral_constant<int, kMSub / 2>{});
-      } else {
-        run(std::integral_constant<int, kMSub / 4>{});
-      }
-    }
-  } else {
-    uint4 q0[kFrag], q1[kFrag];
-    uint32_t s0[kFrag], s1[kFrag];
-    if constexpr (kWaves == 4) {
-      // activations two chunks ahead in registers (ra0/ra1), one chunk ahead in LDS.
-      // The K loop is instantiated for 2 .. 5 subtiles; the tile takes the smallest
-      // that covers its rows (a uniform branch outside the loop)
-      auto run = [&](auto ns_c) {
-        constexpr int NS = decltype(ns_c)::value;
-        constexpr int NP = (NS * 16 + kRowStride - 1) / kRowStride;   // pieces in use
+      uint4 q0[kFrag], q1[kFrag];
+      uint32_t s0[kFrag], s1[kFrag];
+      if constexpr (kLdsScales) stage_scales();
+      if constexpr (kWaves == 4) {
+        // 80-row tiles: activations two chunks ahead in registers, one in LDS
         uint4 ra0[kPieces], ra1[kPieces];
         uint32_t rs0 = 0, rs1 = 0;
         load_a(ra0, rs0, 0, NP);
@@ -614,26 +661,7 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
           store_a(ra0, rs0, 0, NP);
           __syncthreads();
         }
-        if (kc < n_chunks) compute(ns_c, kc, 0, q0, s0);   // odd chunk count: last chunk in q0
-      };
-      if (msub > 4) {
-        run(std::integral_constant<int, 5>{});
-      } else if (msub > 3) {
-        run(std::integral_constant<int, 4>{});
-      } else if (msub > 2) {
-        run(std::integral_constant<int, 3>{});
       } else {
-        run(std::integral_constant<int, 2>{});
-      }
-    } else {
-      // activations one chunk ahead (registers ra, then LDS).  The K loop is
-      // instantiated for 2, 4 and 8 subtiles and the tile takes the smallest that
-      // covers its rows (a uniform branch outside the loop): the last tile of an
-      // expert, and every tile of an expert with few rows, runs only the MFMAs of
-      // its rows
-      auto run = [&](auto ns_c) {
-        constexpr int NS = decltype(ns_c)::value;
-        constexpr int NP = (NS * 16 + kRowStride - 1) / kRowStride;   // pieces in use
         uint4 ra[kPieces];
         uint32_t rs = 0;
         load_a(ra, rs, 0, NP);
@@ -653,72 +681,28 @@ __global__ __launch_bounds__(64 * kWaves, 8 / kWaves) void gemm_tile_kernel(
           store_a(ra, rs, 0, NP);
           __syncthreads();
         }
-        if (kc < n_chunks) compute(ns_c, kc, 0, q0, s0);   // odd chunk count
-      };
-      if (msub > kMSub / 2) {
-        run(std::integral_constant<int, kMSub>{});
-      } else if (msub > kMSub / 4) {
-        run(std::integral_constant<int, kMSub / 2>{});
-      } else {
-        run(std::integral_constant<int, kMSub / 4>{});
       }
+      if (kc < n_chunks) compute(ns_c, kc, 0, q0, s0);   // odd chunk count: last chunk in q0
     }
-  }
-
-  if (!store_cols) return;
-  // D of fragment f, lane (r16, g), element i: activation row 16 mi + r16, output
-  // column wrow(f, 4g + i); per lane these are consecutive from column wrow(0, 4g)
-  const bool do_clamp = clamp != 0;
-  const int col0 = wrow(0, 4 * g);
-#pragma unroll
-  for (int mi = 0; mi < kMSub; ++mi) {
-    if (mi >= msub) continue;   // uniform over the workgroup
-    const int p = rt.p_begin + mi * 16 + r16;
-    if constexpr (kW1) {
-      // h in two-part FP8: the wavefront's 32 gate columns cg*32 .. cg*32+31 are one
-      // 32-element block of h's row, held by the four lanes r16 + 16g (8 each); the
-      // block's largest magnitude comes from two lane exchanges, which every lane
-      // takes part in
-      float hv[8];
-      uint32_t m = 0;
-#pragma unroll
-      for (int f = 0; f < kGate; ++f)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          hv[4 * f + i] = swiglu(acc[mi][f][i], acc[mi][f + kGate][i], limit, do_clamp);
-          const uint32_t a = __float_as_uint(hv[4 * f + i]) & 0x7FFFFFFFu;
-          m = a > m ? a : m;
-        }
-      uint32_t o = static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 16, 64));
-      m = o > m ? o : m;
-      o = static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), 32, 64));
-      m = o > m ? o : m;
-      const uint32_t s = a8_scale_byte(m);
-      const float inv = a8_inv_scale(s);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) hv[i] *= inv;
-      uint2 hi, lo;
-      a8_split8(hv, hi, lo);
-      if (p >= rt.p_end) continue;
-      // block cg = chunk cg / 4, block cg % 4 of it; this lane's 8 elements are
-      // elements 8g .. 8g+7 of the block
-      uint8_t* orow = static_cast<uint8_t*>(out) + static_cast<int64_t>(p) * (2 * ld_out) +
-                      (cg / 4) * 256;
-      const int pos = a8_pos(32 * (cg % 4) + 16 * (g >> 1)) + 8 * (g & 1);
-      *reinterpret_cast<uint2*>(orow + pos) = hi;
-      *reinterpret_cast<uint2*>(orow + 128 + pos) = lo;
-      if (g == 0) out_sc[static_cast<int64_t>(p) * (ld_out / 32) + cg] = static_cast<uint8_t>(s);
+    epilogue(ns_c);
+  };
+  if constexpr (kMSub == 5) {
+    if (msub > 4) {
+      run(std::integral_constant<int, 5>{});
+    } else if (msub > 3) {
+      run(std::integral_constant<int, 4>{});
+    } else if (msub > 2) {
+      run(std::integral_constant<int, 3>{});
     } else {
-      if (p >= rt.p_end) continue;
-      uint16_t* orow = static_cast<uint16_t*>(out) + static_cast<int64_t>(p) * ld_out + col0;
-      uint32_t w[2 * kFrag];
-#pragma unroll
-      for (int f = 0; f < kFrag; ++f)
-#pragma unroll
-        for (int i = 0; i < 4; i += 2)
-          w[2 * f + i / 2] = pack_bf16x2(acc[mi][f][i], acc[mi][f][i + 1]);
-      *reinterpret_cast<uint4*>(orow) = make_uint4(w[0], w[1], w[2], w[3]);
-      *reinterpret_cast<uint4*>(orow + 8) = make_uint4(w[4], w[5], w[6], w[7]);
+      run(std::integral_constant<int, 2>{});
+    }
+  } else {
+    if (msub > kMSub / 2) {
+      run(std::integral_constant<int, kMSub>{});
+    } else if (msub > kMSub / 4) {
+      run(std::integral_constant<int, kMSub / 2>{});
+    } else {
+      run(std::integral_constant<int, kMSub / 4>{});
     }
   }
 }
@@ -746,21 +730,26 @@ hipError_t launch_tile_t(const TileArgs& t, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_tile(bool w1, int tile_rows, const TileArgs& t, hipStream_t stream) {
-  // 128-row tiles: the E8M0 weight scales are staged in LDS while they fit beside
-  // the activation buffers in the CU's 160 KB (K <= 4096), otherwise they come with
-  // the weights; the activations' block scales are staged for all of K when those
-  // fit too (K a multiple of 2048 up to 4096: each thread stages whole 16-byte
-  // groups).  80-row tiles (two workgroups per CU, 78 KB each) read the weights
-  // through the transit areas and stage the activation scales per chunk.
+  // W1: operand-layout loads; the E8M0 weight scales are staged in LDS while they
+  // fit beside the activation buffers (in the CU's 160 KB for 128-row tiles, one
+  // workgroup per CU; in half of it for 80-row tiles, two per CU; K <= 4096 either
+  // way), otherwise they come with the weights.  W2: the weight transit (for
+  // 128-row tiles, on tiles with fewer than eight subtiles).  128-row tiles stage
+  // the activations' block scales for all of K when they fit too (K a multiple of
+  // 2048 up to 4096: each thread stages whole 16-byte groups); 80-row tiles stage
+  // them per chunk.
   if (tile_rows == 128) {
-    if (t.K % 2048 == 0 && tile_lds_bytes(8, t.K, 8, false, true, true) <= kCuLds)
-      return w1 ? launch_tile_t<true, 8, 4, 8, false, true, true>(t, stream)
-                : launch_tile_t<false, 8, 4, 8, false, true, true>(t, stream);
-    return w1 ? launch_tile_t<true, 8, 4, 8, false, false, false>(t, stream)
-              : launch_tile_t<false, 8, 4, 8, false, false, false>(t, stream);
+    const bool tile_as = t.K % 2048 == 0 && tile_lds_bytes(8, t.K, 8, !w1, true, true) <= kCuLds;
+    if (w1)
+      return tile_as ? launch_tile_t<true, 8, 4, 8, false, true, true>(t, stream)
+                     : launch_tile_t<true, 8, 4, 8, false, false, false>(t, stream);
+    return tile_as ? launch_tile_t<false, 8, 4, 8, true, true, true>(t, stream)
+                   : launch_tile_t<false, 8, 4, 8, true, false, false>(t, stream);
   }
-  return w1 ? launch_tile_t<true, 5, 4, 4, true, false, false>(t, stream)
-            : launch_tile_t<false, 5, 4, 4, true, false, false>(t, stream);
+  if (!w1) return launch_tile_t<false, 5, 4, 4, true, false, false>(t, stream);
+  if (tile_lds_bytes(5, t.K, 4, false, true, false) <= kTileLdsPerWorkgroup)
+    return launch_tile_t<true, 5, 4, 4, false, true, false>(t, stream);
+  return launch_tile_t<true, 5, 4, 4, false, false, false>(t, stream);
 }
 
 }  // namespace moe

@@ -235,6 +235,19 @@ def test_streaming_activation_paths(T, E, k, H, I, seed, limit):
     whole_layer_parity(tiny(T, E, k, H, I, seed, skew=True), limit)
 
 
+@pytest.mark.parametrize("T,E,k,H,I,seed", [
+    # 150 rows per expert on average, skewed (6 to 580 rows): 128-row tiles with 8
+    # subtiles (operand-layout loads) next to tiles with 2 and 4 subtiles (weight
+    # transit); W1 5 chunks (one loop of four, then one), W2 3 chunks
+    (600, 8, 2, 640, 384, 27),
+    # the same routing, W1 8 chunks (two loops), W2 6 chunks (one loop, then two)
+    (600, 8, 2, 1024, 768, 27),
+])
+@pytest.mark.parametrize("limit", [10.0, None])
+def test_tiled_subtile_paths(T, E, k, H, I, seed, limit):
+    whole_layer_parity(tiny(T, E, k, H, I, seed, skew=True), limit)
+
+
 @pytest.mark.parametrize("T,E,k,H,I,seed,hot", [
     (7, 16, 2, 2048, 2048, 41, None),   # K = 2048 for both GEMMs: one 1 KB slice per row
     (2, 16, 4, 4096, 2048, 42, None),   # W1 two slices per row, W2 one
