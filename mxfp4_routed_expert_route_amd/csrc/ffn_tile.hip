@@ -21,14 +21,17 @@ namespace {
 // twice, i.e. the bf16 rate, without the dequantisation instructions of a bf16
 // MFMA path.  The activation tile of each K chunk (kMSub*16 rows x 128 elements,
 // 256 bytes a row) is loaded once per workgroup into LDS (double-buffered, in the
-// layout described at kAPieces) and read by all its wavefronts.  Weights go straight to
-// registers, issued right after the chunk that frees their registers.  The E8M0
-// scales of the wavefronts' weight rows are staged in LDS for all of K while they
-// fit beside the activation buffers (K <= 4096 for both shapes; staging them
-// took the 128-row kernel's loop off four scale loads per chunk, 11% of the
-// skewed layer); beyond that they come with the weights.  Each tile runs only
-// the 16-row subtiles that hold rows and stages only their activation rows (the
-// K loop is instantiated per subtile count).
+// layout described at kAPieces) and read by all its wavefronts.  W1's weights go
+// straight to registers in the operand layout, issued right after the chunk that
+// frees their registers, and the E8M0 scales of the wavefronts' weight rows are
+// staged in LDS for all of K while they fit beside the activation buffers (K <=
+// 4096 for both shapes; staging them took the 128-row kernel's loop off four
+// scale loads per chunk, 11% of the skewed layer); beyond that they come with the
+// weights.  W2 (on 128-row tiles: those with fewer than eight subtiles) reads its
+// weights 8 rows x 128 contiguous bytes per load and moves them into the operand
+// layout through a per-wavefront LDS transit, scales with them (see load_pair).
+// Each tile runs only the 16-row subtiles that hold rows and stages only their
+// activation rows (the K loop and the epilogue are instantiated per subtile count).
 //
 // Two shapes are used:
 //  * 80 x 256 (kMSub 5, four wavefronts, two workgroups per CU) for experts of
