@@ -146,9 +146,9 @@ def ffn_kernel_name(T: int, E: int, k: int, H: int, I: int) -> str:
         return "gemm_stream_kernel<true, 2, true, 4>"
     if T * k // E < 96:
         lds_scales = 2 * 80 * 256 + 2 * 256 * 4 + 4 * (H // 128) * 64 * 4 <= 80 * 1024
-        return f"gemm_tile_kernel<true, 5, 4, 4, {'true' if lds_scales else 'false'}, false>"
+        return f"gemm_tile_kernel<true, 5, 4, 4, false, {'true' if lds_scales else 'false'}, false>"
     tiled = H % 2048 == 0 and 2 * 128 * 256 + 128 * (H // 128 + 1) * 4 + 8 * (H // 128) * 64 * 4 <= 160 * 1024
-    return f"gemm_tile_kernel<true, 8, 4, 8, {'true, true' if tiled else 'false, false'}>"
+    return f"gemm_tile_kernel<true, 8, 4, 8, false, {'true, true' if tiled else 'false, false'}>"
 
 
 def blas_threads() -> int:
