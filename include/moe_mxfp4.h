@@ -50,7 +50,8 @@ typedef enum moe_status {
   MOE_OK = 0,
   MOE_ERR_INVALID_ARGUMENT = 1,   /* negative T, k < 1, k > E, null pointer, ... */
   MOE_ERR_UNSUPPORTED = 2,        /* E > 1024, k > 8, H or I not a multiple of 128 or above
-                                     65536, T*k > INT32_MAX, activations above 3.5 GiB */
+                                     65536, H = I = 65536 (one expert's W1 codes would reach
+                                     4 GiB), T*k > INT32_MAX, activations above 3.5 GiB */
   MOE_ERR_MISALIGNED = 3,         /* a buffer is not aligned as its call requires */
   MOE_ERR_WORKSPACE_TOO_SMALL = 4,
   MOE_ERR_HIP = 5                 /* the HIP runtime rejected a launch */

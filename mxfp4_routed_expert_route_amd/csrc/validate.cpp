@@ -21,6 +21,9 @@ moe_status check_sizes(int64_t T, int32_t E, int32_t k) {
 moe_status check_dims(int32_t H, int32_t I) {
   if (H <= 0 || I <= 0) return MOE_ERR_INVALID_ARGUMENT;
   if (H % 128 != 0 || I % 128 != 0 || H > kMaxDim || I > kMaxDim) return MOE_ERR_UNSUPPORTED;
+  // the FFN kernels address one expert's W1 codes (2I rows of H/2 bytes) through a
+  // buffer resource with a 32-bit size: below 4 GiB (only H = I = 65536 reaches it)
+  if (static_cast<int64_t>(H) * I >= (int64_t{1} << 32)) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 

@@ -92,6 +92,9 @@ def test_error_codes_through_the_abi(lib):
     assert fwd(16, 4100, 2048, 256, 6, nulls, 0) == INVALID          # nulls are checked first
     assert fwd(-1, 4096, 2048, 256, 6, nulls, 0) == INVALID
     assert fwd(16, 4096, 2048, 256, 9, nulls, 0) == UNSUPPORTED      # k > 8
+    big = [4096] * 16
+    assert fwd(1, 65536, 65536, 4, 1, big, 1 << 40) == UNSUPPORTED   # a 4 GiB W1 slab per expert
+    assert fwd(1, 65536, 65536 - 128, 4, 1, big, 0) == WS_SMALL      # just below: size checks pass
     # the timed one-call layer: the same checks, then its three events
     lib.moe_forward_mxfp4_timed.argtypes = lib.moe_forward_mxfp4.argtypes[:-1] + [P, P]
     ws = lib.moe_workspace_bytes(16, 256, 6, 4096, 2048)
