@@ -149,8 +149,7 @@ void gemm_stream_kernel(
   // row wrow(f, m), chosen so that a lane's D values are consecutive output
   // columns -- W2: 4 kFrag columns from cg * 16 kFrag + 4 kFrag g; W1: 4 kGate gate
   // columns and the matching up columns -- and the epilogue stores 8 or 16 bytes
-  // per lane and instruction (the activation rows' 2-byte stores it replaces cost
-  // the burst step ~4% of W1 and ~10% of W2).
+  // per lane and instruction instead of one bf16 per activation row.
   auto wrow = [&](int f, int c16) {   // W1: gate fragments, then the matching up fragments
     return kW1 ? (f >= kGate ? half : 0) + cg * (16 * kGate) + (c16 >> 2) * (4 * kGate) +
                      (f % kGate) * 4 + (c16 & 3)
