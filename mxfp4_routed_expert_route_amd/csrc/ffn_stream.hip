@@ -143,17 +143,10 @@ void gemm_stream_kernel(
                                              : a_lds + a_lds_rows * a_row_bytes + 128 * g;
   const int a_step = r16 < nvalid ? 512 : 0;
 
-  // The weights are the MFMA's A operand and the activations its B operand, so a
-  // lane of D holds rows 4g .. 4g+3 of each fragment (weight rows, i.e. output
-  // columns) for one activation row (lane & 15).  Lane m of fragment f loads weight
-  // row wrow(f, m), chosen so that a lane's D values are consecutive output
-  // columns -- W2: 4 kFrag columns from cg * 16 kFrag + 4 kFrag g; W1: 4 kGate gate
-  // columns and the matching up columns -- and the epilogue stores 8 or 16 bytes
-  // per lane and instruction instead of one bf16 per activation row.
+  // weight row of fragment f for a lane whose MFMA column is c16
   auto wrow = [&](int f, int c16) {   // W1: gate fragments, then the matching up fragments
-    return kW1 ? (f >= kGate ? half : 0) + cg * (16 * kGate) + (c16 >> 2) * (4 * kGate) +
-                     (f % kGate) * 4 + (c16 & 3)
-               : cg * (16 * kFrag) + (c16 >> 2) * (4 * kFrag) + f * 4 + (c16 & 3);
+    return kW1 ? (f >= kGate ? half : 0) + cg * (16 * kGate) + (f % kGate) * 16 + c16
+               : cg * (16 * kFrag) + f * 16 + c16;
   };
   int nrow[kFrag];
 #pragma unroll
@@ -245,7 +238,7 @@ void gemm_stream_kernel(
         const bf16x8 b = dequant8(w[f][s], scl[f]);
 #pragma unroll
         for (int mi = 0; mi < MSUB; ++mi)
-          acc[mi][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, a[mi][s], acc[mi][f], 0, 0, 0);
+          acc[mi][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mi][s], b, acc[mi][f], 0, 0, 0);
       }
     }
   };
@@ -366,7 +359,7 @@ void gemm_stream_kernel(
             const bf16x8 b = dequant8(w[f][s], scl[f]);
 #pragma unroll
             for (int mi = 0; mi < MSUB; ++mi)
-              acc[mi][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, a[mi][4 * j + s], acc[mi][f],
+              acc[mi][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mi][4 * j + s], b, acc[mi][f],
                                                                    0, 0, 0);
           }
         }
@@ -509,37 +502,24 @@ void gemm_stream_kernel(
     }
   }
 
-  // D of fragment f, lane (r16, g), element i: activation row 16 mi + r16, output
-  // column wrow(f, 4g + i); per lane these are consecutive from column wrow(0, 4g)
+  // D layout of a 16x16 MFMA tile: lane holds column (lane & 15), rows 4*(lane>>4) + i.
   const bool do_clamp = clamp != 0;
-  const int col0 = wrow(0, 4 * g);
 #pragma unroll
   for (int mi = 0; mi < MSUB; ++mi) {
-    const int p = rt.p_begin + mi * 16 + r16;
-    if (p >= rt.p_end) continue;
-    uint16_t* orow = out + static_cast<int64_t>(p) * ld_out + col0;
-    if constexpr (kW1) {
-      uint32_t w[2 * kGate];
 #pragma unroll
-      for (int f = 0; f < kGate; ++f)
+    for (int i = 0; i < 4; ++i) {
+      const int p = rt.p_begin + mi * 16 + 4 * g + i;
+      if (p >= rt.p_end) continue;
+      uint16_t* orow = out + static_cast<int64_t>(p) * ld_out;
+      if (kW1) {
 #pragma unroll
-        for (int i = 0; i < 4; i += 2)
-          w[2 * f + i / 2] =
-              pack_bf16x2(swiglu(acc[mi][f][i], acc[mi][f + kGate][i], limit, do_clamp),
-                          swiglu(acc[mi][f][i + 1], acc[mi][f + kGate][i + 1], limit, do_clamp));
-      if constexpr (kGate == 2)
-        *reinterpret_cast<uint4*>(orow) = make_uint4(w[0], w[1], w[2], w[3]);
-      else
-        *reinterpret_cast<uint2*>(orow) = make_uint2(w[0], w[1]);
-    } else {
-      uint32_t w[2 * kFrag];
+        for (int f = 0; f < kGate; ++f)
+          orow[nrow[f]] =
+              f32_to_bf16_bits(swiglu(acc[mi][f][i], acc[mi][f + kGate][i], limit, do_clamp));
+      } else {
 #pragma unroll
-      for (int f = 0; f < kFrag; ++f)
-#pragma unroll
-        for (int i = 0; i < 4; i += 2) w[2 * f + i / 2] = pack_bf16x2(acc[mi][f][i], acc[mi][f][i + 1]);
-      *reinterpret_cast<uint4*>(orow) = make_uint4(w[0], w[1], w[2], w[3]);
-      if constexpr (kFrag == 4)
-        *reinterpret_cast<uint4*>(orow + 8) = make_uint4(w[4], w[5], w[6], w[7]);
+        for (int f = 0; f < kFrag; ++f) orow[nrow[f]] = f32_to_bf16_bits(acc[mi][f][i]);
+      }
     }
   }
 }
