@@ -56,15 +56,21 @@ moe_status forward_layer(const float* logits, const uint16_t* x, int64_t T, int3
                      reinterpret_cast<int32_t*>(wsb + L.ffn_plan_offset),
                      wsb + L.ffn_plan_offset + 256};
   bool plan_written = false;
+  // the tiled FFN reads x in two-part FP8: the routing launch converts it meanwhile
+  const SplitArgs split{x, T, H, reinterpret_cast<uint8_t*>(wsb + L.ffn_xq_offset),
+                        reinterpret_cast<uint8_t*>(wsb + L.ffn_xs_offset)};
+  bool split_done = false;
   hipError_t e = launch_route_and_group(logits, T, E, k, topk_ids, topk_weights, bitmatrix,
                                         counts, offsets, gather, scatter, ws, st, &plan,
-                                        &plan_written);
+                                        &plan_written, ffn_tiled(T, E, k, H, I) ? &split : nullptr,
+                                        &split_done);
   if (e != hipSuccess) return MOE_ERR_HIP;
   // on the decode GEMV path the W2 launch also writes y (same arithmetic as the combine)
   const CombineArgs fold{topk_ids, topk_weights, scatter, y};
   bool combined = false;
   e = launch_ffn(x, T, H, I, E, k, w1, w1_scale, w2, w2_scale, counts, offsets, gather,
-                 swiglu_limit, y_sorted, ws, L, st, events, plan_written, &fold, &combined);
+                 swiglu_limit, y_sorted, ws, L, st, events, plan_written, &fold, &combined,
+                 split_done);
   if (e != hipSuccess) return MOE_ERR_HIP;
   if (combined) return MOE_OK;
   return from_hip(launch_combine(y_sorted, topk_weights, scatter, T, H, k, y, st));

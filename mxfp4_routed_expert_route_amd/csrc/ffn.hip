@@ -42,7 +42,8 @@ hipError_t launch_ffn(const uint16_t* x, int64_t T, int H, int I, int E, int k,
                       const uint8_t* w2s, const int32_t* counts, const int32_t* offsets,
                       const int32_t* gather, float limit, uint16_t* y_sorted, void* ws,
                       const WsLayout& L, hipStream_t stream, hipEvent_t const* events,
-                      bool plan_ready, const CombineArgs* combine, bool* combined) {
+                      bool plan_ready, const CombineArgs* combine, bool* combined,
+                      bool split_ready) {
   if (combined) *combined = false;
   const int64_t n_slots = T * k;
   char* wsb = static_cast<char*>(ws);
@@ -69,7 +70,7 @@ hipError_t launch_ffn(const uint16_t* x, int64_t T, int H, int I, int E, int k,
     if (err != hipSuccess) return err;
   }
   const bool tiled = tile_rows >= 80;
-  if (tiled) {   // x in two-part FP8 for the tiled kernels (ahead of the W1 event)
+  if (tiled && !split_ready) {   // x in two-part FP8 for the tiled kernels (ahead of the W1 event)
     err = launch_act_split(x, T, H, reinterpret_cast<uint8_t*>(wsb + L.ffn_xq_offset),
                            reinterpret_cast<uint8_t*>(wsb + L.ffn_xs_offset), stream);
     if (err != hipSuccess) return err;

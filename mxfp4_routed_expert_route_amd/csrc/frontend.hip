@@ -147,11 +147,14 @@ __global__ __launch_bounds__(1024) void frontend_small_kernel(
 hipError_t launch_route_and_group(const float* logits, int64_t T, int E, int k, int32_t* ids,
                                   float* weights, uint32_t* bm, int32_t* counts, int32_t* offsets,
                                   int32_t* gather, int32_t* scatter, void* ws, hipStream_t stream,
-                                  const PlanOut* plan, bool* plan_written) {
+                                  const PlanOut* plan, bool* plan_written,
+                                  const SplitArgs* split, bool* split_done) {
   if (plan_written) *plan_written = false;
+  if (split_done) *split_done = false;
   if (T > kFrontMaxTokens) {
-    hipError_t err = launch_route(logits, T, E, k, ids, weights, stream, bm);
+    hipError_t err = launch_route(logits, T, E, k, ids, weights, stream, bm, split);
     if (err != hipSuccess) return err;
+    if (split_done) *split_done = split != nullptr;
     return launch_offsets(bm, ids, T, E, k, counts, offsets, gather, scatter, ws, stream, plan,
                           plan_written);
   }

@@ -9,8 +9,20 @@ namespace moe {
 
 // With bm != nullptr, also the bit matrix ([T][ceil(E/32)] words, every word of
 // each row written).
+// x (rows x K bf16) to the tiled FFN's two-part FP8 form (xq) and block scales (xs)
+struct SplitArgs {
+  const uint16_t* x;
+  int64_t rows;
+  int K;
+  uint8_t* xq;
+  uint8_t* xs;
+};
+
+// With split != nullptr the routing launch also converts x (extra workgroups after
+// the routing ones: the conversion streams while routing waits on its latencies).
 hipError_t launch_route(const float* logits, int64_t T, int E, int k, int32_t* ids,
-                        float* weights, hipStream_t stream, uint32_t* bm = nullptr);
+                        float* weights, hipStream_t stream, uint32_t* bm = nullptr,
+                        const SplitArgs* split = nullptr);
 
 hipError_t launch_bitmatrix(const int32_t* ids, int64_t T, int E, int k, uint32_t* bm,
                             hipStream_t stream);
@@ -38,13 +50,14 @@ struct CombineArgs {
 // The grouped FFN; `L` is the workspace layout for these sizes (validate.h).  With
 // `combine` set, the decode GEMV path (one-row tiles) also writes the combined y
 // from its W2 step and sets *combined; other paths leave the combine to the caller.
+// split_ready: x is already in the workspace's two-part FP8 form (routing launch).
 hipError_t launch_ffn(const uint16_t* x, int64_t T, int H, int I, int E, int k,
                       const uint8_t* w1, const uint8_t* w1s, const uint8_t* w2,
                       const uint8_t* w2s, const int32_t* counts, const int32_t* offsets,
                       const int32_t* gather, float limit, uint16_t* y_sorted, void* ws,
                       const WsLayout& L, hipStream_t stream, hipEvent_t const* events = nullptr,
                       bool plan_ready = false, const CombineArgs* combine = nullptr,
-                      bool* combined = nullptr);
+                      bool* combined = nullptr, bool split_ready = false);
 
 // Where the one-launch front-end also writes the FFN's row-tile plan (count, then
 // the tile list; see ffn.hip).
@@ -58,10 +71,13 @@ struct PlanOut {
 // With plan != nullptr the one-launch path (T <= 64) also writes the FFN plan and
 // sets *plan_written; larger T runs the routing kernel (writing the bit matrix
 // too) and the offsets kernels, whose last step writes the plan.
+// With split != nullptr and T above the one-launch front-end's limit the routing
+// launch also converts x (launch_route) and sets *split_done.
 hipError_t launch_route_and_group(const float* logits, int64_t T, int E, int k, int32_t* ids,
                                   float* weights, uint32_t* bm, int32_t* counts, int32_t* offsets,
                                   int32_t* gather, int32_t* scatter, void* ws, hipStream_t stream,
-                                  const PlanOut* plan = nullptr, bool* plan_written = nullptr);
+                                  const PlanOut* plan = nullptr, bool* plan_written = nullptr,
+                                  const SplitArgs* split = nullptr, bool* split_done = nullptr);
 
 // x [rows][K] bf16 -> two-part FP8 rows (xq: [rows][2K] bytes) and their E8M0 block
 // scales (xs: [rows][K/32] bytes), the input form of the tiled FFN kernels.
