@@ -66,8 +66,10 @@ def test_forward_matches_separate_calls_workloads(index):
     (1, 256, 6, 256, 128, 41),       # one token, 16-row tiles
     (40, 8, 1, 128, 128, 42),        # 5 rows per expert: 16-row tiles, several per expert
     (64, 24, 7, 256, 128, 43),       # 18.7 rows per expert: 32-row tiles, front-end plan
-    (64, 16, 8, 256, 256, 44),       # 32 rows per expert: 80-row LDS tiles, front-end plan
-    (65, 16, 8, 256, 256, 45),       # past the one-launch limit: the offsets kernel's plan
+    (64, 16, 8, 256, 256, 44),       # 32 rows per expert: 80-row LDS tiles, front-end plan,
+                                     # x split by its own launch
+    (65, 16, 8, 256, 256, 45),       # past the one-launch limit: the offsets kernel's plan,
+                                     # x split by extra workgroups of the routing launch
     (300, 8, 3, 256, 256, 48),       # 112 rows per expert: 128-row tiles, offsets kernel
     (100, 256, 6, 256, 128, 51),     # 16-row tiles for 2.3 rows per expert, offsets kernel
     (200, 64, 6, 256, 128, 52),      # 18.75 rows per expert: 32-row tiles, offsets kernel
