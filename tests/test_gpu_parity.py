@@ -439,3 +439,25 @@ def test_full_size_workload(index, limit):
     y_ref, ys_ref, pos = oracle_rows.token_outputs(inp, ref, wl.k, S, limit)
     ffn_close(ys[pos], ys_ref)
     ffn_close(y[S], y_ref)
+
+
+def _random_shapes(seed, n):
+    """Shapes drawn from a fixed generator: experts, k, rows per expert (every tile
+    class), widths that are any multiple of 128 up to 1152, skewed routing or not,
+    clamp on or off, separate calls or the one-call layer."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        E = int(rng.choice([4, 8, 16, 32, 64, 256]))
+        k = int(rng.integers(1, min(8, E) + 1))
+        rows = int(rng.choice([2, 6, 12, 20, 30, 50, 70, 100, 150]))
+        T = int(max(1, min(1200, rows * E // k + int(rng.integers(-5, 6)))))
+        H, I = 128 * int(rng.integers(1, 10)), 128 * int(rng.integers(1, 10))
+        out.append((T, E, k, H, I, int(rng.integers(0, 10**6)), bool(rng.random() < 0.4),
+                    [10.0, None][i % 2], i % 3 == 0))
+    return out
+
+
+@pytest.mark.parametrize("T,E,k,H,I,seed,skew,limit,fused", _random_shapes(2024, 24))
+def test_random_shapes(T, E, k, H, I, seed, skew, limit, fused):
+    whole_layer_parity(tiny(T, E, k, H, I, seed, skew=skew), limit, fused)
